@@ -1,0 +1,380 @@
+"""Oracle: MoE layer forward and backward in float64. TEST INFRASTRUCTURE ONLY.
+
+What the layer computes, from the pages:
+  * [A] "nemo_automodel.components.moe.mok_experts", ``GroupedExpertsMoK.forward``:
+    fused shared and routed SwiGLU experts; x [T,H] BF16, router weights
+    [T,k], int64 expert ids [T,k], shared gate/up [I_s,H] and down [H,I_s];
+    routed gate/up [E,I,H] and down [E,H,I] (``_MoKRuntime.forward``); no
+    expert bias (``down_proj_bias`` / ``gate_up_proj_bias`` are None).
+  * [A] ``_MoKRuntime.backward``: gradients for x, the router weights, the
+    three routed and the three shared weight tensors, reusing the forward's
+    schedule; the integer ids get none.
+  * [R] "Mixture-of-Kittens: a deterministic MoE megakernel for NVL72 racks",
+    §"The two API layers and the schedule object": one schedule drives both
+    dispatch and combine, and is reused by backward.
+
+Formula (weights in the nn.Linear [out, in] layout, so y = W a):
+  for each kept assignment (t, j) with expert e = top[t, j] and weight w[t, j]:
+      g = W_g[e] x_t,  u = W_u[e] x_t,  h = silu(g) * u,  y = W_d[e] h
+  out[t] = sum_j w[t, j] * y_(t, j) + S_d (silu(S_g x_t) * (S_u x_t))
+with silu(z) = z * sigmoid(z). Dropped or invalid assignments contribute 0.
+
+Readings taken (listed in the design doc): SwiGLU is silu(gate) * up; the shared
+expert has weight 1 and is always on; router weights are used as given (the
+router is outside the layer, [R] §"Where MoK is the wrong tool"); the weight
+is applied to the expert output (equal to applying it to h by linearity).
+
+All arithmetic is float64. Inputs are float arrays (bf16 already decoded).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import mxfp8
+from .schedule import build_schedule
+
+__all__ = ["sigmoid", "silu", "forward", "forward_per_token", "forward_tokens",
+           "backward", "forward_mxfp8", "backward_mxfp8", "segment_rows"]
+
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu(z):
+    return z * sigmoid(z)
+
+
+def segment_rows(sched: dict, e: int):
+    """Kept rows of expert e: (row ids, flat assignment ids, token ids)."""
+    lo = sched["offsets"][e]
+    rows = np.arange(lo, lo + sched["kept"][e], dtype=np.int64)
+    a = sched["row_src"][rows]
+    return rows, a, a // sched["k"]
+
+
+def _expert_mlp(A, Wg, Wu, Wd):
+    g = A @ Wg.T
+    u = A @ Wu.T
+    h = silu(g) * u
+    return g, u, h, h @ Wd.T
+
+
+def forward(x, top_experts, router_weights, w_gate, w_up, w_down,
+            s_gate=None, s_up=None, s_down=None, sched=None,
+            capacity_multiplier=1.0, expert_pad=32, return_parts=False):
+    """Layer output [T,H] in float64, expert-grouped formulation: each
+    expert's kept rows are gathered, run through its SwiGLU MLP, weighted and
+    added back at their tokens.
+
+    Pins (tests/test_oracle_moe.py): with E=1, k=1, w=1 and no shared expert
+    it equals a dense SwiGLU MLP written with torch CPU ops; it equals the
+    per-token loop ``forward_per_token``; permuting tokens permutes the output
+    (no drops); it is linear in the router weights; w = 0 leaves only the
+    shared expert."""
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    k = top_experts.shape[1]
+    E = w_gate.shape[0]
+    if sched is None:
+        sched = build_schedule(top_experts, E, capacity_multiplier, expert_pad)
+    wflat = np.asarray(router_weights, np.float64).reshape(-1)
+    out = np.zeros((T, H))
+    parts = {}
+    for e in range(E):
+        rows, a, t = segment_rows(sched, e)
+        if rows.size == 0:
+            continue
+        g, u, h, y = _expert_mlp(x[t], w_gate[e], w_up[e], w_down[e])
+        np.add.at(out, t, wflat[a][:, None] * y)
+        if return_parts:
+            parts[e] = dict(rows=rows, a=a, t=t, g=g, u=u, h=h, y=y)
+    if s_gate is not None:
+        g, u, h, y = _expert_mlp(x, s_gate, s_up, s_down)
+        out += y
+        if return_parts:
+            parts["shared"] = dict(g=g, u=u, h=h, y=y)
+    if return_parts:
+        return out, sched, parts
+    return out
+
+
+def forward_per_token(x, top_experts, router_weights, w_gate, w_up, w_down,
+                      s_gate=None, s_up=None, s_down=None, sched=None,
+                      capacity_multiplier=1.0, expert_pad=32):
+    """The same output by a scalar-style loop over tokens and slots, reading
+    the keep/drop decision from the schedule's slot map. Used at tiny sizes
+    as an independent formulation of ``forward``."""
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    k = top_experts.shape[1]
+    E = w_gate.shape[0]
+    if sched is None:
+        sched = build_schedule(top_experts, E, capacity_multiplier, expert_pad)
+    out = np.zeros((T, H))
+    for t in range(T):
+        acc = np.zeros(H)
+        for j in range(k):
+            if sched["slot_row"][t * k + j] < 0:
+                continue
+            e = int(top_experts[t, j])
+            h = silu(w_gate[e] @ x[t]) * (w_up[e] @ x[t])
+            acc += float(router_weights[t, j]) * (w_down[e] @ h)
+        if s_gate is not None:
+            acc += s_down @ (silu(s_gate @ x[t]) * (s_up @ x[t]))
+        out[t] = acc
+    return out
+
+
+def forward_tokens(tokens, x, top_experts, router_weights, w_gate, w_up, w_down,
+                   s_gate=None, s_up=None, s_down=None, slot_row=None):
+    """Output rows for a subset of tokens only, each computed on its own
+    (used for sampled checks at full sizes). ``slot_row`` ([T*k], -1 where an
+    assignment was not kept) comes from the oracle schedule of the whole
+    batch; None means every valid assignment is kept."""
+    k = top_experts.shape[1]
+    E = w_gate.shape[0]
+    outs = []
+    for t in tokens:
+        xt = np.asarray(x[t], np.float64)
+        acc = np.zeros(xt.shape[0])
+        for j in range(k):
+            e = int(top_experts[t, j])
+            kept = (0 <= e < E) if slot_row is None else slot_row[t * k + j] >= 0
+            if not kept:
+                continue
+            Wg, Wu, Wd = (np.asarray(w[e], np.float64) for w in (w_gate, w_up, w_down))
+            h = silu(Wg @ xt) * (Wu @ xt)
+            acc += float(router_weights[t, j]) * (Wd @ h)
+        if s_gate is not None:
+            acc += np.asarray(s_down, np.float64) @ (silu(np.asarray(s_gate, np.float64) @ xt)
+                                                     * (np.asarray(s_up, np.float64) @ xt))
+        outs.append(acc)
+    return np.stack(outs) if outs else np.zeros((0, x.shape[1]))
+
+
+def backward(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
+             s_gate=None, s_up=None, s_down=None, sched=None,
+             capacity_multiplier=1.0, expert_pad=32):
+    """Gradients of sum(grad_out * out) with respect to every float input.
+
+    Returns dict: dx [T,H], d_router_weights [T,k], d_w_gate, d_w_up
+    [E,I,H], d_w_down [E,H,I], d_s_gate, d_s_up [I_s,H], d_s_down [H,I_s]
+    (None without a shared expert). Dropped or invalid assignments get a zero
+    router-weight gradient and add nothing anywhere.
+
+    Per kept row r (token t, expert e, weight w), with y the unweighted
+    expert output:
+      dw     = <grad_out[t], y>
+      dy     = w * grad_out[t];    dh = W_d[e]^T dy
+      dg     = dh * u * s * (1 + g (1 - s)),  s = sigmoid(g);   du = dh * silu(g)
+      dW_d  += dy h^T;   dW_g += dg x_t^T;   dW_u += du x_t^T
+      dx[t] += W_g[e]^T dg + W_u[e]^T du
+    and the same for the shared expert with w = 1.
+
+    Pins (tests/test_oracle_moe.py): central finite differences in float64
+    for every input on tiny shapes, and torch.autograd (CPU, float64) through
+    a torch-written forward.
+    """
+    dO = np.asarray(grad_out, np.float64)
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    k = top_experts.shape[1]
+    E, I, _ = w_gate.shape
+    if sched is None:
+        sched = build_schedule(top_experts, E, capacity_multiplier, expert_pad)
+    wflat = np.asarray(router_weights, np.float64).reshape(-1)
+    dx = np.zeros((T, H))
+    dwr = np.zeros(T * k)
+    dWg = np.zeros((E, I, H))
+    dWu = np.zeros((E, I, H))
+    dWd = np.zeros((E, H, I))
+    for e in range(E):
+        rows, a, t = segment_rows(sched, e)
+        if rows.size == 0:
+            continue
+        A = x[t]
+        g, u, h, y = _expert_mlp(A, w_gate[e], w_up[e], w_down[e])
+        dOt = dO[t]
+        dwr[a] = np.sum(dOt * y, axis=1)
+        dy = wflat[a][:, None] * dOt
+        dh = dy @ w_down[e]
+        s = sigmoid(g)
+        dg = dh * u * s * (1.0 + g * (1.0 - s))
+        du = dh * g * s
+        dWd[e] = dy.T @ h
+        dWg[e] = dg.T @ A
+        dWu[e] = du.T @ A
+        np.add.at(dx, t, dg @ w_gate[e] + du @ w_up[e])
+    res = dict(dx=dx, d_router_weights=dwr.reshape(T, k), d_w_gate=dWg, d_w_up=dWu,
+               d_w_down=dWd, d_s_gate=None, d_s_up=None, d_s_down=None)
+    if s_gate is not None:
+        g, u, h, y = _expert_mlp(x, s_gate, s_up, s_down)
+        dh = dO @ s_down
+        s = sigmoid(g)
+        dg = dh * u * s * (1.0 + g * (1.0 - s))
+        du = dh * g * s
+        res["d_s_down"] = dO.T @ h
+        res["d_s_gate"] = dg.T @ x
+        res["d_s_up"] = du.T @ x
+        dx += dg @ s_gate + du @ s_up
+    return res
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 emulation
+# ---------------------------------------------------------------------------
+
+def forward_mxfp8(x, top_experts, router_weights, w_gate, w_up, w_down,
+                  s_gate=None, s_up=None, s_down=None, sched=None,
+                  capacity_multiplier=1.0, expert_pad=32, return_parts=False,
+                  quantize_h=True):
+    """MXFP8 forward: x, W_g, W_u (blocks along H) and W_d (blocks along I),
+    shared weights included, are replaced by dequantize(quantize(.)); h is
+    computed in float64 from those and itself quantized along I before the
+    down projection. SwiGLU, the weighting and the combine stay in float64.
+
+    Reading: [R] §"Tuning the five hyperparameters before production" keeps
+    activations in BF16 at the interface and quantizes weights beforehand;
+    the quantization of x and h along the contraction dimension inside the
+    layer is the plain reading of "MXFP8 forward" (blocks along K).
+
+    Pin (tests/test_oracle_moe.py): when x and every weight already sit on
+    the MX grid, the only difference to ``forward`` is h's quantization, so
+    replacing the h step by the identity must reproduce ``forward`` exactly.
+    """
+    q = mxfp8.qdq
+    qh = mxfp8.qdq if quantize_h else (lambda v, axis: v)
+    xq = q(np.asarray(x, np.float64), axis=1)
+    Wg = q(np.asarray(w_gate, np.float64), axis=2)
+    Wu = q(np.asarray(w_up, np.float64), axis=2)
+    Wd = q(np.asarray(w_down, np.float64), axis=2)
+    T, H = xq.shape
+    E = Wg.shape[0]
+    if sched is None:
+        sched = build_schedule(top_experts, E, capacity_multiplier, expert_pad)
+    wflat = np.asarray(router_weights, np.float64).reshape(-1)
+    out = np.zeros((T, H))
+    parts = {}
+    for e in range(E):
+        rows, a, t = segment_rows(sched, e)
+        if rows.size == 0:
+            continue
+        A = xq[t]
+        g = A @ Wg[e].T
+        u = A @ Wu[e].T
+        h = qh(silu(g) * u, axis=1)
+        y = h @ Wd[e].T
+        np.add.at(out, t, wflat[a][:, None] * y)
+        if return_parts:
+            parts[e] = dict(rows=rows, a=a, t=t, g=g, u=u, hq=h, y=y)
+    if s_gate is not None:
+        Sg = q(np.asarray(s_gate, np.float64), axis=1)
+        Su = q(np.asarray(s_up, np.float64), axis=1)
+        Sd = q(np.asarray(s_down, np.float64), axis=1)
+        g = xq @ Sg.T
+        u = xq @ Su.T
+        h = qh(silu(g) * u, axis=1)
+        out += h @ Sd.T
+        if return_parts:
+            parts["shared"] = dict(g=g, u=u, hq=h)
+    if return_parts:
+        return out, sched, parts
+    return out
+
+
+def _qdq_rows_in_segment(v, q, block=32):
+    """Quantize [n, C] along rows in 32-row blocks, the rows being one
+    expert's kept rows followed by zero padding up to a multiple of 32."""
+    n = v.shape[0]
+    npad = -(-n // block) * block
+    vp = np.zeros((npad,) + v.shape[1:])
+    vp[:n] = v
+    return q(vp, axis=0)[:n]
+
+
+def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
+                   s_gate=None, s_up=None, s_down=None, sched=None,
+                   capacity_multiplier=1.0, expert_pad=32, qfun=None):
+    """MXFP8 backward: every backward GEMM operand is quantized along that
+    GEMM's contraction dimension, the forward activations being the MXFP8
+    forward's (g, u from quantized x and weights; h quantized along I).
+
+      dh   = Q_H(grad_out rows) @ Q_H(W_d)              (contraction over H)
+      dA   = Q_I(dg) @ Q_I(W_g) + Q_I(du) @ Q_I(W_u)   (contraction over I)
+      dW_d = Q_r(dy)^T @ Q_r(h)                        (contraction over rows)
+      dW_g = Q_r(dg)^T @ Q_r(x rows);  dW_u likewise
+    where Q_r works in 32-row blocks inside each expert's zero-padded segment.
+    The router-weight gradient is <dh_unweighted, h> (equal to <grad_out, y>).
+    Reading: the pages give the MXFP8 backward only by name; quantizing each
+    operand along its own contraction dimension is the plain reading of
+    "MXFP8" (blocks along K) for a GEMM whose K differs from the forward's.
+
+    Pin (tests/test_oracle_moe.py): with ``qfun`` the identity this must equal
+    ``backward`` (checks which operand goes where); the quantizer itself is
+    pinned in tests/test_oracle_mxfp8.py.
+    """
+    q = mxfp8.qdq if qfun is None else qfun
+    dO = np.asarray(grad_out, np.float64)
+    xq = q(np.asarray(x, np.float64), axis=1)
+    xraw = np.asarray(x, np.float64)
+    T, H = xraw.shape
+    k = top_experts.shape[1]
+    E, I, _ = w_gate.shape
+    Wg_f = q(np.asarray(w_gate, np.float64), axis=2)
+    Wu_f = q(np.asarray(w_up, np.float64), axis=2)
+    Wd_b = q(np.asarray(w_down, np.float64), axis=1)       # [E,H,I] blocks along H
+    Wg_b = q(np.asarray(w_gate, np.float64), axis=1)       # [E,I,H] blocks along I
+    Wu_b = q(np.asarray(w_up, np.float64), axis=1)
+    if sched is None:
+        sched = build_schedule(top_experts, E, capacity_multiplier, expert_pad)
+    wflat = np.asarray(router_weights, np.float64).reshape(-1)
+    dx = np.zeros((T, H))
+    dwr = np.zeros(T * k)
+    dWg = np.zeros((E, I, H))
+    dWu = np.zeros((E, I, H))
+    dWd = np.zeros((E, H, I))
+    for e in range(E):
+        rows, a, t = segment_rows(sched, e)
+        if rows.size == 0:
+            continue
+        A = xq[t]
+        g = A @ Wg_f[e].T
+        u = A @ Wu_f[e].T
+        hq = q(silu(g) * u, axis=1)
+        dOq = q(dO[t], axis=1)
+        dh_un = dOq @ Wd_b[e]
+        dwr[a] = np.sum(dh_un * hq, axis=1)
+        w = wflat[a][:, None]
+        dh = w * dh_un
+        s = sigmoid(g)
+        dg = dh * u * s * (1.0 + g * (1.0 - s))
+        du = dh * g * s
+        dx_rows = q(dg, axis=1) @ Wg_b[e] + q(du, axis=1) @ Wu_b[e]
+        np.add.at(dx, t, dx_rows)
+        dy = w * dO[t]
+        dWd[e] = _qdq_rows_in_segment(dy, q).T @ _qdq_rows_in_segment(hq, q)
+        xr = _qdq_rows_in_segment(xraw[t], q)
+        dWg[e] = _qdq_rows_in_segment(dg, q).T @ xr
+        dWu[e] = _qdq_rows_in_segment(du, q).T @ xr
+    res = dict(dx=dx, d_router_weights=dwr.reshape(T, k), d_w_gate=dWg, d_w_up=dWu,
+               d_w_down=dWd, d_s_gate=None, d_s_up=None, d_s_down=None)
+    if s_gate is not None:
+        Sg_f = q(np.asarray(s_gate, np.float64), axis=1)
+        Su_f = q(np.asarray(s_up, np.float64), axis=1)
+        Sd_b = q(np.asarray(s_down, np.float64), axis=0)
+        Sg_b = q(np.asarray(s_gate, np.float64), axis=0)
+        Su_b = q(np.asarray(s_up, np.float64), axis=0)
+        g = xq @ Sg_f.T
+        u = xq @ Su_f.T
+        hq = q(silu(g) * u, axis=1)
+        dh = q(dO, axis=1) @ Sd_b
+        s = sigmoid(g)
+        dg = dh * u * s * (1.0 + g * (1.0 - s))
+        du = dh * g * s
+        dx += q(dg, axis=1) @ Sg_b + q(du, axis=1) @ Su_b
+        res["d_s_down"] = _qdq_rows_in_segment(dO, q).T @ _qdq_rows_in_segment(hq, q)
+        xr = _qdq_rows_in_segment(xraw, q)
+        res["d_s_gate"] = _qdq_rows_in_segment(dg, q).T @ xr
+        res["d_s_up"] = _qdq_rows_in_segment(du, q).T @ xr
+    return res
