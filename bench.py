@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic
+input already resident in HBM: mok_build_schedule + mok_forward (and
+mok_backward for the forward+backward workloads). Default workload: the
+8192-token BF16 forward (T=8192, H=2048, I=768, E=128, k=8, shared I_s=768).
+
+Prints ONE JSON line (rank 0, N=1):
+  value = tokens/s of the whole step; roofline = the dominant kernel (the
+  gate/up grouped GEMM) against the bf16 (or MXFP8) MFMA peak, timed with
+  HIP events on its launch stream over the timed region; cpu_baseline = the
+  float64 NumPy oracle on a bounded token sample on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       [--no-cpu-baseline] [--all]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import CONFIGS, MoEShape, make_inputs  # noqa: E402
+
+METRIC = "MoE layer tokens/s + achieved TFLOP/s vs MFMA peak, BF16 & MXFP8 fwd/bwd"
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}
+HBM_GBS = 8000.0
+DEFAULT = "t8192_bf16_fwd"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(CONFIGS))
+    ap.add_argument("--mult", type=float, default=None, help="override the capacity multiplier")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="0 = automatic")
+    ap.add_argument("--all", action="store_true", help="one line per workload (diagnostics)")
+    return ap.parse_args()
+
+
+def to_device(inp, torch):
+    def bf(a):
+        if a is None:
+            return None
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    d = dict(x=bf(inp["x"]), top=torch.from_numpy(inp["top_experts"]).cuda(),
+             w=torch.from_numpy(inp["router_weights"]).cuda(), g=bf(inp.get("grad_out")))
+    d["weights"] = {"routed_gate": bf(inp["w_gate"]), "routed_up": bf(inp["w_up"]),
+                    "routed_down": bf(inp["w_down"])}
+    if inp.get("s_gate") is not None:
+        d["weights"].update(shared_gate=bf(inp["s_gate"]), shared_up=bf(inp["s_up"]), shared_down=bf(inp["s_down"]))
+    return d
+
+
+def kept_assignments(sched_fields) -> int:
+    return int(sched_fields["kept"].sum().item())
+
+
+def cpu_baseline(c: MoEShape, inp: dict, mult: float, sample_tokens: int) -> dict:
+    """The oracle (float64 NumPy, as it stands) on the first `sample_tokens`
+    tokens of the same batch, with its own schedule for that sample."""
+    from oracle import moe as omoe
+    from workloads import bf16_bits_to_f32
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    n = min(sample_tokens, c.T)
+    f = lambda a: None if a is None else bf16_bits_to_f32(a).astype(np.float64)  # noqa: E731
+    args = [f(inp["x"][:n]), inp["top_experts"][:n], inp["router_weights"][:n], f(inp["w_gate"]),
+            f(inp["w_up"]), f(inp["w_down"]), f(inp["s_gate"]), f(inp["s_up"]), f(inp["s_down"])]
+    t0 = time.perf_counter()
+    if c.passes == "fwd":
+        if c.mode == "mxfp8":
+            omoe.forward_mxfp8(*args, capacity_multiplier=mult)
+        else:
+            omoe.forward(*args, capacity_multiplier=mult)
+    else:
+        g = f(inp["grad_out"][:n])
+        if c.mode == "mxfp8":
+            omoe.forward_mxfp8(*args, capacity_multiplier=mult)
+            omoe.backward_mxfp8(g, *args, capacity_multiplier=mult)
+        else:
+            omoe.forward(*args, capacity_multiplier=mult)
+            omoe.backward(g, *args, capacity_multiplier=mult)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {c.T} tokens of the same seeded batch, float64 NumPy oracle "
+                      f"({'fwd' if c.passes == 'fwd' else 'fwd+bwd'}, {c.mode}), {dt:.2f} s"}
+
+
+def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sample_tokens: int) -> dict:
+    import torch
+    import mixture_experts_layer_build_amd as mok
+
+    inp = make_inputs(c)
+    d = to_device(inp, torch)
+    cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=c.T,
+                        shared_intermediate=c.I_s, capacity_multiplier=mult, expert_pad=c.expert_pad)
+    ws = mok.Workspace(cfg)
+    mode = mok.MOK_MODE_MXFP8 if c.mode == "mxfp8" else mok.MOK_MODE_BF16
+    training = c.passes != "fwd"
+    ctx = torch.empty(mok.context_bytes(cfg, mode), dtype=torch.uint8, device="cuda") if training else None
+    sched = torch.empty(ws.layout.total_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["x"])
+    weights = d["weights"]
+    if mode == mok.MOK_MODE_MXFP8:
+        # weights pre-quantized once, outside the step (the pages' MXFP8 workflow)
+        q = {}
+        for n, t in d["weights"].items():
+            codes, sc = mok.mxfp8_quantize(t.reshape(-1, t.shape[-1]), axis=1)
+            q[n] = codes.view(t.shape)
+            q[n + "_scale"] = sc
+        weights = q
+        bf16_weights = d["weights"]
+    grads = None
+
+    def step():
+        nonlocal grads
+        mok.build_schedule(ws, d["top"], sched)
+        mok.forward(ws, sched, d["x"], d["w"], weights, mode=mode, out=out, context=ctx)
+        if training:
+            grads = mok.backward(ws, sched, ctx, d["g"], d["x"], d["w"],
+                                 bf16_weights if mode == mok.MOK_MODE_MXFP8 else weights, mode=mode, grads=grads)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ws.set_timing(True)
+    ws.read_timing()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    timing = ws.read_timing()
+    ws.set_timing(False)
+
+    fields = mok.schedule_fields(ws, sched)
+    R_kept = kept_assignments(fields)
+    fwd_flops = c.fwd_flops(kept_assignments=R_kept)
+    flops = fwd_flops * (3.0 if training else 1.0)
+    ms = dt / steps * 1e3
+    tok_s = c.T * steps / dt
+    dtype = "mxfp8" if mode == mok.MOK_MODE_MXFP8 else "bf16"
+    peak = PEAK_TFLOPS[dtype]
+    # dominant kernel: the gate/up grouped GEMM, 4*H*(R_kept*I + T*I_s) flops per launch
+    gu_flops = 4.0 * c.H * (R_kept * c.I + (c.T * c.I_s if c.I_s else 0))
+    gu_ms, gu_n = timing.get("gate_up", (float("nan"), 0))
+    gu_avg = gu_ms / max(gu_n, 1)
+    achieved = gu_flops / (gu_avg * 1e-3) / 1e12 if gu_n else None
+    line = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded, random-init weights)",
+        "config": {"workload": c.name, "tokens": c.T, "hidden": c.H, "intermediate": c.I, "experts": c.E,
+                   "topk": c.k, "shared_intermediate": c.I_s, "capacity_multiplier": mult,
+                   "expert_pad": c.expert_pad, "passes": c.passes, "kept_assignments": R_kept,
+                   "parallelism": "single GPU (one GPU's share; no all-to-all)"},
+        "tflops": round(flops / (dt / steps) / 1e12, 2),
+        "frac_of_peak_layer": round(flops / (dt / steps) / 1e12 / peak, 4),
+        "roofline": {"bound": "mfma", "kernel": "gate_up grouped GEMM",
+                     "achieved": None if achieved is None else round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": None if achieved is None else round(achieved / peak, 4),
+                     "avg_launch_ms": round(gu_avg, 5), "algorithmic_flops_per_launch": gu_flops,
+                     "traffic": None},
+        "kernels_ms_per_step": {k: round(v[0] / steps, 5) for k, v in timing.items()},
+    }
+    if want_cpu:
+        # about 2048 tokens' worth of the 8192-token workload's per-token work
+        per_tok = c.fwd_flops() / c.T * (3.0 if c.passes != "fwd" else 1.0)
+        n = sample_tokens or int(min(c.T, max(64, 2048 * 84.9e6 / per_tok)))
+        line["cpu_baseline"] = cpu_baseline(c, inp, mult, n)
+    return line
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the all-to-all between GPUs is left out, "
+                                   "so --gpus N with N > 1 is not supported"}))
+        sys.exit(2)
+    names = [n for n in CONFIGS] if a.all else [a.workload]
+    for n in names:
+        c = CONFIGS[n]
+        mult = c.capacity_multiplier if a.mult is None else a.mult
+        line = run(c, a.steps, a.warmup, mult, not a.no_cpu_baseline and not a.all, a.cpu_sample_tokens)
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,440 @@
+// Host side of the C ABI declared in include/mok.h: configuration checks,
+// schedule/context sizing, workspace allocation, launch sequencing.
+//
+// "Mixture-of-Kittens: a deterministic MoE megakernel for NVL72 racks",
+// section "The two API layers and the schedule object": a workspace is
+// allocated once and reused; the schedule is built once per layer and step
+// and passed to both forward and backward. Every check below happens before
+// anything is enqueued, and no call reads device memory on the host.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "mok_internal.h"
+
+namespace mok {
+
+int64_t capacity(int64_t T, float mult) {
+  // C = min(T, ceil(mult * T)), the float32 multiplier evaluated in float64.
+  const double c = std::ceil((double)mult * (double)T);
+  const int64_t ci = c < 0 ? 0 : (int64_t)c;
+  return std::min<int64_t>(T, ci);
+}
+
+int64_t rows_cap(const mok_config& c, int64_t T) {
+  const int64_t C = capacity(T, c.capacity_multiplier);
+  return std::min<int64_t>(T * c.topk, (int64_t)c.num_experts * C) + (int64_t)c.num_experts * (c.expert_pad - 1);
+}
+
+int64_t n_minibatches(const mok_config& c, int64_t T) {
+  if (c.minibatch_size <= 0 || T <= 0) return 1;
+  return std::max<int64_t>(1, (T + c.minibatch_size - 1) / c.minibatch_size);
+}
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+Layout schedule_layout(const mok_config& c) {
+  Layout L{};
+  const int64_t E = c.num_experts;
+  L.rows_cap_max = rows_cap(c, c.max_tokens);
+  L.n_mb_max = n_minibatches(c, c.max_tokens);
+  size_t off = 0;
+  auto take = [&](size_t ints) {
+    const size_t o = off;
+    off = align_up(off + ints * sizeof(int32_t), 256);
+    return o;
+  };
+  L.header = take(HDR_INTS);
+  L.counts = take(E);
+  L.kept = take(E);
+  L.offsets = take(E + 1);
+  L.mb_offsets = take((L.n_mb_max + 1) * E);
+  L.row_src = take(L.rows_cap_max);
+  L.slot_row = take((size_t)c.max_tokens * c.topk);
+  L.tiles = take((size_t)kNumTileBMs * (E + 2));
+  L.total = off;
+  return L;
+}
+
+uint32_t config_hash(const mok_config& c) {
+  // FNV-1a over the fields that shape a schedule.
+  uint32_t h = 2166136261u;
+  auto mix = [&](const void* p, size_t n) {
+    const unsigned char* b = (const unsigned char*)p;
+    for (size_t i = 0; i < n; ++i) h = (h ^ b[i]) * 16777619u;
+  };
+  mix(&c.num_experts, 4);
+  mix(&c.topk, 4);
+  mix(&c.max_tokens, 8);
+  mix(&c.capacity_multiplier, 4);
+  mix(&c.expert_pad, 4);
+  mix(&c.minibatch_size, 4);
+  return h & 0x7FFFFFFFu;
+}
+
+SchedView sched_view(void* base, const Layout& L) {
+  char* b = (char*)base;
+  SchedView v;
+  v.header = (int32_t*)(b + L.header);
+  v.counts = (int32_t*)(b + L.counts);
+  v.kept = (int32_t*)(b + L.kept);
+  v.offsets = (int32_t*)(b + L.offsets);
+  v.mb_offsets = (int32_t*)(b + L.mb_offsets);
+  v.row_src = (int32_t*)(b + L.row_src);
+  v.slot_row = (int32_t*)(b + L.slot_row);
+  v.tiles = (int32_t*)(b + L.tiles);
+  return v;
+}
+
+LaunchTimer::LaunchTimer(mok_workspace* w, int k, hipStream_t s) : ws(w), kernel(k), stream(s) {
+  if (!ws || !ws->timing) return;
+  auto get = [&]() {
+    hipEvent_t e = nullptr;
+    if (!ws->event_pool.empty()) {
+      e = ws->event_pool.back();
+      ws->event_pool.pop_back();
+    } else if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+    }
+    return e;
+  };
+  a = get();
+  b = get();
+  if (a) (void)hipEventRecord(a, stream);
+}
+
+LaunchTimer::~LaunchTimer() {
+  if (!ws || !ws->timing || !a || !b) return;
+  (void)hipEventRecord(b, stream);
+  ws->launches.push_back(TimedLaunch{kernel, a, b});
+}
+
+// Restores the caller's current device when a call switches to the
+// workspace's device.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+size_t workspace_bytes(const mok_config& c, const Layout& L, size_t* parts) {
+  const int64_t Tm = c.max_tokens, H = c.hidden;
+  const int64_t rowsR = L.rows_cap_max;
+  const int64_t n_chunks_max = std::max<int64_t>(1, 24 * 1024 / c.num_experts);
+  size_t p[8] = {
+      (size_t)n_chunks_max * c.num_experts * 4 + (size_t)n_chunks_max * 4,  // schedule chunk histograms
+      ctx_elems(c, L) * 2,                                                  // h when no context is kept
+      (size_t)(rowsR + Tm) * H * 2,                                         // y rows (bf16)
+      (size_t)Tm * H + (size_t)Tm * (H / 32),                               // x in MXFP8 (+ scales)
+      ctx_elems(c, L) + ctx_elems(c, L) / 32,                               // h in MXFP8 (+ scales)
+      0, 0, 0};
+  size_t total = 0;
+  for (int i = 0; i < 8; ++i) {
+    if (parts) parts[i] = align_up(p[i], 256);
+    total += align_up(p[i], 256);
+  }
+  return total;
+}
+
+}  // namespace mok
+
+using namespace mok;
+
+static mok_status to_status(hipError_t e) {
+  if (e == hipSuccess) return MOK_OK;
+  if (e == hipErrorNotSupported) return MOK_ERR_UNSUPPORTED;
+  return MOK_ERR_HIP;
+}
+
+// ------------------------------------------------------------------------
+// Pure host queries
+// ------------------------------------------------------------------------
+extern "C" const char* mok_status_string(mok_status s) {
+  switch (s) {
+    case MOK_OK: return "MOK_OK";
+    case MOK_ERR_INVALID_ARGUMENT: return "MOK_ERR_INVALID_ARGUMENT";
+    case MOK_ERR_UNSUPPORTED: return "MOK_ERR_UNSUPPORTED";
+    case MOK_ERR_CONFIG_MISMATCH: return "MOK_ERR_CONFIG_MISMATCH";
+    case MOK_ERR_BUFFER_TOO_SMALL: return "MOK_ERR_BUFFER_TOO_SMALL";
+    case MOK_ERR_HIP: return "MOK_ERR_HIP";
+  }
+  return "MOK_ERR_UNKNOWN";
+}
+
+extern "C" mok_status mok_validate_config(const mok_config* c) {
+  if (!c) return MOK_ERR_INVALID_ARGUMENT;
+  if (c->struct_size != sizeof(mok_config)) return MOK_ERR_INVALID_ARGUMENT;
+  if (c->hidden <= 0 || c->intermediate <= 0 || c->num_experts <= 0 || c->topk <= 0 || c->max_tokens <= 0 ||
+      c->shared_intermediate < 0 || c->expert_pad <= 0 || c->minibatch_size < 0 || c->num_mover_wgs < 0)
+    return MOK_ERR_INVALID_ARGUMENT;
+  if (!(c->capacity_multiplier > 0.0f) || !std::isfinite(c->capacity_multiplier)) return MOK_ERR_INVALID_ARGUMENT;
+  if (c->hidden % 128 != 0 || c->intermediate % 64 != 0 || c->shared_intermediate % 64 != 0)
+    return MOK_ERR_UNSUPPORTED;
+  if (c->num_experts > 1024 || c->topk > 64 || c->expert_pad % 32 != 0) return MOK_ERR_UNSUPPORTED;
+  if (c->max_tokens * (int64_t)c->topk >= (int64_t)1 << 31) return MOK_ERR_UNSUPPORTED;
+  const Layout L = schedule_layout(*c);
+  if (L.rows_cap_max + c->max_tokens >= (int64_t)1 << 31) return MOK_ERR_UNSUPPORTED;
+  return MOK_OK;
+}
+
+extern "C" size_t mok_schedule_bytes(const mok_config* c) {
+  if (mok_validate_config(c) != MOK_OK) return 0;
+  return schedule_layout(*c).total;
+}
+
+extern "C" mok_status mok_schedule_layout_query(const mok_config* c, mok_schedule_layout* out) {
+  const mok_status st = mok_validate_config(c);
+  if (st != MOK_OK) return st;
+  if (!out) return MOK_ERR_INVALID_ARGUMENT;
+  const Layout L = schedule_layout(*c);
+  out->total_bytes = L.total;
+  out->header = L.header;
+  out->counts = L.counts;
+  out->kept = L.kept;
+  out->offsets = L.offsets;
+  out->mb_offsets = L.mb_offsets;
+  out->row_src = L.row_src;
+  out->slot_row = L.slot_row;
+  out->tiles = L.tiles;
+  out->rows_cap_max = L.rows_cap_max;
+  out->n_mb_max = L.n_mb_max;
+  return MOK_OK;
+}
+
+extern "C" size_t mok_context_bytes(const mok_config* c, mok_mode mode) {
+  if (mok_validate_config(c) != MOK_OK) return 0;
+  if (mode != MOK_MODE_BF16 && mode != MOK_MODE_MXFP8) return 0;
+  const Layout L = schedule_layout(*c);
+  return 3 * align_up(ctx_elems(*c, L) * 2, 256);
+}
+
+extern "C" size_t mok_workspace_bytes(const mok_config* c) {
+  if (mok_validate_config(c) != MOK_OK) return 0;
+  return workspace_bytes(*c, schedule_layout(*c), nullptr);
+}
+
+// ------------------------------------------------------------------------
+// Workspace
+// ------------------------------------------------------------------------
+extern "C" mok_status mok_workspace_create(const mok_config* c, int device, mok_workspace** out) {
+  if (!out) return MOK_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  const mok_status st = mok_validate_config(c);
+  if (st != MOK_OK) return st;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess) return MOK_ERR_HIP;
+  if (device < 0 || device >= ndev) return MOK_ERR_INVALID_ARGUMENT;
+  DeviceGuard g(device);
+  if (!g.ok) return MOK_ERR_HIP;
+  mok_workspace* ws = new (std::nothrow) mok_workspace();
+  if (!ws) return MOK_ERR_HIP;
+  ws->cfg = *c;
+  ws->device = device;
+  ws->layout = schedule_layout(*c);
+  if (hipDeviceGetAttribute(&ws->num_cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      ws->num_cus <= 0) {
+    delete ws;
+    return MOK_ERR_HIP;
+  }
+  size_t parts[8];
+  ws->scratch_bytes = workspace_bytes(*c, ws->layout, parts);
+  if (hipMalloc((void**)&ws->scratch, ws->scratch_bytes) != hipSuccess) {
+    delete ws;
+    return MOK_ERR_HIP;
+  }
+  char* p = ws->scratch;
+  ws->n_chunks_max = std::max<int64_t>(1, 24 * 1024 / c->num_experts);
+  ws->chunk_hist = (int32_t*)p;
+  ws->chunk_invalid = (int32_t*)(p + (size_t)ws->n_chunks_max * c->num_experts * 4);
+  p += parts[0];
+  ws->hbuf = p;
+  ws->hbuf_bytes = parts[1];
+  p += parts[1];
+  ws->ybuf = p;
+  p += parts[2];
+  ws->xq = (uint8_t*)p;
+  ws->xq_scale = (uint8_t*)p + (size_t)c->max_tokens * c->hidden;
+  p += parts[3];
+  ws->hq = (uint8_t*)p;
+  ws->hq_scale = (uint8_t*)p + ctx_elems(*c, ws->layout);
+  p += parts[4];
+  *out = ws;
+  return MOK_OK;
+}
+
+extern "C" mok_status mok_workspace_destroy(mok_workspace* ws) {
+  if (!ws) return MOK_OK;
+  mok_status st = MOK_OK;
+  {
+    DeviceGuard g(ws->device);
+    if (hipDeviceSynchronize() != hipSuccess) st = MOK_ERR_HIP;
+    for (auto& l : ws->launches) {
+      (void)hipEventDestroy(l.start);
+      (void)hipEventDestroy(l.stop);
+    }
+    for (auto e : ws->event_pool) (void)hipEventDestroy(e);
+    if (ws->scratch && hipFree(ws->scratch) != hipSuccess) st = MOK_ERR_HIP;
+  }
+  delete ws;
+  return st;
+}
+
+// ------------------------------------------------------------------------
+// Hot path
+// ------------------------------------------------------------------------
+extern "C" mok_status mok_build_schedule(mok_workspace* ws, const int64_t* top_experts, int64_t T, void* schedule,
+                                         size_t schedule_bytes, void* stream) {
+  if (!ws || !schedule) return MOK_ERR_INVALID_ARGUMENT;
+  if (T < 0 || T > ws->cfg.max_tokens) return MOK_ERR_INVALID_ARGUMENT;
+  if (T > 0 && !top_experts) return MOK_ERR_INVALID_ARGUMENT;
+  if (schedule_bytes < ws->layout.total) return MOK_ERR_BUFFER_TOO_SMALL;
+  DeviceGuard g(ws->device);
+  if (!g.ok) return MOK_ERR_HIP;
+  return launch_schedule(ws, top_experts, T, schedule, (hipStream_t)stream) == hipSuccess ? MOK_OK : MOK_ERR_HIP;
+}
+
+static mok_status check_weights(const mok_config& c, mok_mode mode, const mok_weights* w, bool need_scales) {
+  if (!w || !w->routed_gate || !w->routed_up || !w->routed_down) return MOK_ERR_INVALID_ARGUMENT;
+  const bool sh = c.shared_intermediate > 0;
+  if (sh != (w->shared_gate != nullptr) || sh != (w->shared_up != nullptr) || sh != (w->shared_down != nullptr))
+    return MOK_ERR_INVALID_ARGUMENT;
+  if (mode == MOK_MODE_MXFP8 && need_scales) {
+    if (!w->routed_gate_scale || !w->routed_up_scale || !w->routed_down_scale) return MOK_ERR_INVALID_ARGUMENT;
+    if (sh && (!w->shared_gate_scale || !w->shared_up_scale || !w->shared_down_scale))
+      return MOK_ERR_INVALID_ARGUMENT;
+  }
+  return MOK_OK;
+}
+
+extern "C" mok_status mok_forward(mok_workspace* ws, mok_mode mode, const void* schedule, size_t schedule_bytes,
+                                  const void* x, const float* router_weights, const mok_weights* weights, void* out,
+                                  void* context, size_t context_bytes, void* stream) {
+  if (!ws || !schedule || !x || !router_weights || !out) return MOK_ERR_INVALID_ARGUMENT;
+  if (mode != MOK_MODE_BF16 && mode != MOK_MODE_MXFP8) return MOK_ERR_INVALID_ARGUMENT;
+  if (schedule_bytes < ws->layout.total) return MOK_ERR_BUFFER_TOO_SMALL;
+  mok_status st = check_weights(ws->cfg, mode, weights, true);
+  if (st != MOK_OK) return st;
+  if (context && context_bytes < mok_context_bytes(&ws->cfg, mode)) return MOK_ERR_BUFFER_TOO_SMALL;
+  DeviceGuard g(ws->device);
+  if (!g.ok) return MOK_ERR_HIP;
+  FwdArgs a{};
+  a.w = weights;
+  a.x = x;
+  a.router_w = router_weights;
+  a.out = out;
+  a.mxfp8 = mode == MOK_MODE_MXFP8;
+  const size_t ce = ctx_elems(ws->cfg, ws->layout);
+  if (context) {
+    char* cb = (char*)context;
+    const size_t part = align_up(ce * 2, 256);
+    a.ctx_g = cb;
+    a.ctx_u = cb + part;
+    a.h = cb + 2 * part;
+  } else {
+    a.h = ws->hbuf;
+  }
+  a.y = ws->ybuf;
+  return to_status(launch_forward(ws, schedule, a, (hipStream_t)stream));
+}
+
+extern "C" mok_status mok_backward(mok_workspace* ws, mok_mode mode, const void* schedule, size_t schedule_bytes,
+                                   const void* context, size_t context_bytes, const void* grad_out, const void* x,
+                                   const float* router_weights, const mok_weights* weights, const mok_grads* grads,
+                                   void* stream) {
+  if (!ws || !schedule || !context || !grad_out || !x || !router_weights || !grads) return MOK_ERR_INVALID_ARGUMENT;
+  if (mode != MOK_MODE_BF16 && mode != MOK_MODE_MXFP8) return MOK_ERR_INVALID_ARGUMENT;
+  if (schedule_bytes < ws->layout.total) return MOK_ERR_BUFFER_TOO_SMALL;
+  if (context_bytes < mok_context_bytes(&ws->cfg, mode)) return MOK_ERR_BUFFER_TOO_SMALL;
+  mok_status st = check_weights(ws->cfg, mode, weights, false);
+  if (st != MOK_OK) return st;
+  const bool sh = ws->cfg.shared_intermediate > 0;
+  if (!grads->dx || !grads->d_router_weights || !grads->d_routed_gate || !grads->d_routed_up ||
+      !grads->d_routed_down)
+    return MOK_ERR_INVALID_ARGUMENT;
+  if (sh != (grads->d_shared_gate != nullptr) || sh != (grads->d_shared_up != nullptr) ||
+      sh != (grads->d_shared_down != nullptr))
+    return MOK_ERR_INVALID_ARGUMENT;
+  DeviceGuard g(ws->device);
+  if (!g.ok) return MOK_ERR_HIP;
+  const size_t ce = ctx_elems(ws->cfg, ws->layout);
+  const size_t part = align_up(ce * 2, 256);
+  BwdArgs a{};
+  a.w = weights;
+  a.x = x;
+  a.grad_out = grad_out;
+  a.router_w = router_weights;
+  a.ctx_g = context;
+  a.ctx_u = (const char*)context + part;
+  a.ctx_h = (const char*)context + 2 * part;
+  a.g = grads;
+  a.mxfp8 = mode == MOK_MODE_MXFP8;
+  return to_status(launch_backward(ws, schedule, a, (hipStream_t)stream));
+}
+
+extern "C" mok_status mok_mxfp8_quantize(const void* src, int src_is_fp32, int64_t rows, int64_t cols,
+                                         int64_t ld_src, int axis, uint8_t* dst, int64_t ld_dst,
+                                         uint8_t* dst_scale, void* stream) {
+  if (rows < 0 || cols < 0 || (axis != 0 && axis != 1) || (src_is_fp32 != 0 && src_is_fp32 != 1))
+    return MOK_ERR_INVALID_ARGUMENT;
+  if (rows == 0 || cols == 0) return MOK_OK;
+  if (!src || !dst || !dst_scale) return MOK_ERR_INVALID_ARGUMENT;
+  if (ld_src < cols || ld_dst < cols) return MOK_ERR_INVALID_ARGUMENT;
+  if (cols % 8 != 0 || ld_dst % 8 != 0 || ld_src % 8 != 0) return MOK_ERR_UNSUPPORTED;
+  if (axis == 1 && cols % 32 != 0) return MOK_ERR_UNSUPPORTED;
+  if (axis == 0 && rows % 32 != 0) return MOK_ERR_UNSUPPORTED;
+  if ((((uintptr_t)src) & 15) || (((uintptr_t)dst) & 7)) return MOK_ERR_UNSUPPORTED;
+  if (axis == 0 && (((uintptr_t)dst_scale) & 7)) return MOK_ERR_UNSUPPORTED;
+  return launch_quantize(src, src_is_fp32, rows, cols, ld_src, axis, dst, ld_dst, dst_scale, (hipStream_t)stream) ==
+                 hipSuccess
+             ? MOK_OK
+             : MOK_ERR_HIP;
+}
+
+// ------------------------------------------------------------------------
+// Diagnostics
+// ------------------------------------------------------------------------
+extern "C" const char* mok_kernel_name(int id) {
+  static const char* names[MOK_K_COUNT] = {
+      "sched_count", "sched_scan",     "sched_scatter", "sched_minibatch", "quant_x",      "gate_up",
+      "down",        "combine",        "bwd_dh",        "bwd_dw_reduce",   "bwd_dx_rows",  "bwd_dx_sum",
+      "bwd_dwd",     "bwd_dwgu",       "bwd_quant"};
+  if (id < 0 || id >= MOK_K_COUNT) return "unknown";
+  return names[id];
+}
+
+extern "C" mok_status mok_workspace_set_timing(mok_workspace* ws, int enable) {
+  if (!ws) return MOK_ERR_INVALID_ARGUMENT;
+  ws->timing = enable != 0;
+  return MOK_OK;
+}
+
+extern "C" mok_status mok_workspace_read_timing(mok_workspace* ws, float* total_ms, int64_t* launches, int n) {
+  if (!ws || n < 0 || (n > 0 && (!total_ms || !launches))) return MOK_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < n; ++i) {
+    total_ms[i] = 0.f;
+    launches[i] = 0;
+  }
+  DeviceGuard g(ws->device);
+  mok_status st = MOK_OK;
+  for (auto& l : ws->launches) {
+    float ms = 0.f;
+    if (hipEventSynchronize(l.stop) != hipSuccess || hipEventElapsedTime(&ms, l.start, l.stop) != hipSuccess)
+      st = MOK_ERR_HIP;
+    if (l.kernel >= 0 && l.kernel < n) {
+      total_ms[l.kernel] += ms;
+      launches[l.kernel] += 1;
+    }
+    ws->event_pool.push_back(l.start);
+    ws->event_pool.push_back(l.stop);
+  }
+  ws->launches.clear();
+  return st;
+}

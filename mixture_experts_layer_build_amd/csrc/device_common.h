@@ -1,0 +1,98 @@
+// Device-side helpers: bf16 conversion, MXFP8 (E4M3 + E8M0) encoding,
+// MFMA vector types. Included by the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace mok {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+
+__host__ __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__host__ __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+__host__ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return u2f((uint32_t)b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs finite; NaN kept quiet).
+__host__ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = f2u(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__host__ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// floor(log2 |v|) of a non-zero fp32 magnitude given by its bits (sign clear),
+// exact, subnormals included.
+__host__ __device__ __forceinline__ int floor_log2_bits(uint32_t mag) {
+  int ef = (int)(mag >> 23);
+  if (ef > 0) return ef - 127;
+  return (31 - __builtin_clz(mag)) - 149;  // mantissa only: value = m * 2^-149
+}
+
+// MXFP8 block exponent X from the block's largest magnitude (fp32 bits, sign
+// clear): clamp(floor(log2 amax) - 8, -127, 127); -127 for amax == 0.
+__host__ __device__ __forceinline__ int mx_block_exponent(uint32_t amax_bits) {
+  if (amax_bits == 0) return -127;
+  int x = floor_log2_bits(amax_bits) - 8;
+  return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// E4M3 ("FN": bias 7, no infinity, 0x7F NaN, max 448) code of v / 2^X,
+// rounded to nearest even on the E4M3 grid, magnitudes above 448
+// saturating to 0x7E, sign kept. Integer arithmetic on the fp32 bits, so
+// the result is exact for every finite input (no flush of subnormals).
+__host__ __device__ __forceinline__ uint32_t e4m3_encode_scaled(float v, int X) {
+  uint32_t u = f2u(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t mag = u & 0x7FFFFFFFu;
+  if (mag == 0) return sign;
+  int ef = (int)(mag >> 23);
+  uint32_t S;   // integer significand
+  int e2;       // |v| = S * 2^e2
+  if (ef > 0) {
+    S = (mag & 0x7FFFFFu) | 0x800000u;
+    e2 = ef - 150;
+  } else {
+    S = mag;
+    e2 = -149;
+  }
+  int L = floor_log2_bits(mag) - X;              // floor(log2 |v / 2^X|)
+  int qe = (L < -6 ? -6 : L) - 3;                // exponent of one grid step at that binade
+  int sh = qe - (e2 - X);                        // right shift that maps S onto grid steps
+  uint32_t n;
+  if (sh <= 0) {
+    n = S << (-sh);                              // exact (only tiny shifts occur: |v/2^X| < 2^9)
+  } else if (sh > 25) {
+    n = 0;
+  } else {
+    n = S >> sh;
+    uint32_t rem = S & ((1u << sh) - 1u);
+    uint32_t half = 1u << (sh - 1);
+    if (rem > half || (rem == half && (n & 1u))) n += 1u;
+  }
+  uint32_t code;
+  if (L < -6) {
+    code = n;                                    // subnormal steps of 2^-9; n == 8 is 0x08 = 2^-6
+  } else {
+    code = (uint32_t)((L + 7) << 3) + n - 8u;    // n == 16 carries into the next binade
+  }
+  if (code > 0x7Eu) code = 0x7Eu;
+  return code | sign;
+}
+
+// Wave-wide helpers (wave64).
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+}  // namespace mok

@@ -1,0 +1,159 @@
+// Internal definitions shared by the library's translation units.
+// Not part of the ABI (include/mok.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "mok.h"
+
+namespace mok {
+
+// ---------------------------------------------------------------------------
+// Schedule buffer
+// ---------------------------------------------------------------------------
+enum HeaderField : int {
+  HDR_T = 0,
+  HDR_K = 1,
+  HDR_E = 2,
+  HDR_C = 3,
+  HDR_P = 4,
+  HDR_ROWS_CAP = 5,
+  HDR_NMB = 6,
+  HDR_MB = 7,
+  HDR_DROPPED = 8,
+  HDR_INVALID = 9,
+  HDR_ROWS_TOTAL = 10,
+  HDR_HASH = 11,
+  HDR_INTS = 16
+};
+
+// Tile heights whose per-expert tile prefix sums the schedule carries.
+constexpr int kNumTileBMs = 4;
+constexpr int kTileBM[kNumTileBMs] = {32, 64, 128, 256};
+__host__ __device__ constexpr int tile_bm_index(int bm) { return bm == 32 ? 0 : bm == 64 ? 1 : bm == 128 ? 2 : 3; }
+
+struct Layout {
+  size_t header, counts, kept, offsets, mb_offsets, row_src, slot_row, tiles, total;
+  int64_t rows_cap_max, n_mb_max;
+};
+
+int64_t capacity(int64_t T, float mult);
+int64_t rows_cap(const mok_config& c, int64_t T);
+int64_t n_minibatches(const mok_config& c, int64_t T);
+Layout schedule_layout(const mok_config& c);
+uint32_t config_hash(const mok_config& c);
+
+// Device view of a schedule buffer (all int32).
+struct SchedView {
+  int32_t* header;
+  int32_t* counts;
+  int32_t* kept;
+  int32_t* offsets;     // [E+1]
+  int32_t* mb_offsets;  // [(n_mb_max+1)*E]
+  int32_t* row_src;     // [rows_cap_max]
+  int32_t* slot_row;    // [T_max*k]
+  int32_t* tiles;       // [4][E+2]
+};
+SchedView sched_view(void* base, const Layout& L);
+
+// ---------------------------------------------------------------------------
+// Workspace
+// ---------------------------------------------------------------------------
+struct TimedLaunch {
+  int kernel;
+  hipEvent_t start, stop;
+};
+
+}  // namespace mok
+
+struct mok_workspace {
+  mok_config cfg;
+  int device;
+  int num_cus;
+  mok::Layout layout;
+  // scratch
+  char* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  int32_t* chunk_hist = nullptr;   // [n_chunks_max * E]
+  int32_t* chunk_invalid = nullptr;  // [n_chunks_max]
+  int64_t n_chunks_max = 0;
+  void* hbuf = nullptr;            // h (bf16) or MXFP8 h codes + scales when no context is kept
+  size_t hbuf_bytes = 0;
+  void* ybuf = nullptr;            // bf16 [(rows_cap_max + T_max) * H]
+  uint8_t* xq = nullptr;           // E4M3 [T_max * H]
+  uint8_t* xq_scale = nullptr;     // [T_max * H/32]
+  uint8_t* hq = nullptr;           // E4M3 h (routed rows then shared rows)
+  uint8_t* hq_scale = nullptr;     // its E8M0 scales, one per 32 along I
+  // backward scratch
+  void* dgu = nullptr;             // bf16 dG, dU for routed + shared rows
+  float* dw_part = nullptr;        // fp32 partial router-weight gradients
+  // timing
+  bool timing = false;
+  std::vector<mok::TimedLaunch> launches;
+  std::vector<hipEvent_t> event_pool;
+};
+
+namespace mok {
+
+// Event bracket around one launch when timing is enabled.
+struct LaunchTimer {
+  mok_workspace* ws;
+  int kernel;
+  hipStream_t stream;
+  hipEvent_t a = nullptr, b = nullptr;
+  LaunchTimer(mok_workspace* w, int k, hipStream_t s);
+  ~LaunchTimer();
+};
+
+// ---------------------------------------------------------------------------
+// Launchers (each returns hipSuccess or the launch error)
+// ---------------------------------------------------------------------------
+hipError_t launch_schedule(mok_workspace* ws, const int64_t* top, int64_t T, void* sched, hipStream_t s);
+
+hipError_t launch_quantize(const void* src, int src_is_fp32, int64_t rows, int64_t cols, int64_t ld_src, int axis,
+                           uint8_t* dst, int64_t ld_dst, uint8_t* dst_scale, hipStream_t s);
+
+struct FwdArgs {
+  const mok_weights* w;
+  const void* x;              // bf16 [T,H]
+  const float* router_w;      // [T,k]
+  void* out;                  // bf16 [T,H]
+  void* ctx_g;                // bf16 routed [rows_cap_max, I] then shared [T_max, I_s]; null = not kept
+  void* ctx_u;
+  void* h;                    // bf16 h (routed rows then shared rows)
+  void* y;                    // bf16 [(rows_cap_max + T_max), H]
+  int mxfp8;
+};
+hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a, hipStream_t s);
+hipError_t launch_forward_bf16(mok_workspace* ws, const void* sched, const FwdArgs& a, hipStream_t s);
+hipError_t launch_forward_mxfp8(mok_workspace* ws, const void* sched, const FwdArgs& a, hipStream_t s);
+
+struct BwdArgs {
+  const mok_weights* w;
+  const void* x;
+  const void* grad_out;
+  const float* router_w;
+  const void* ctx_g;
+  const void* ctx_u;
+  const void* ctx_h;
+  const mok_grads* g;
+  int mxfp8;
+};
+hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& a, hipStream_t s);
+
+// Context layout: G, U, h each [rows_cap_max*I + T_max*I_s] bf16.
+inline size_t ctx_elems(const mok_config& c, const Layout& L) {
+  return (size_t)L.rows_cap_max * c.intermediate + (size_t)c.max_tokens * c.shared_intermediate;
+}
+
+}  // namespace mok
+
+#define MOK_HIP_TRY(expr)                   \
+  do {                                      \
+    hipError_t e_ = (expr);                 \
+    if (e_ != hipSuccess) return e_;        \
+  } while (0)

@@ -1,0 +1,179 @@
+"""GPU parity of mok_forward (BF16) against the float64 oracle:
+max|err| <= 2e-2 * max|ref| per output (fp32 accumulation, bf16 output).
+
+Small cases are compared element by element over every token; they span
+several 128-row tiles per expert with ragged tails, partial N tiles, invalid
+ids, capacity drops and a shared expert whose width differs from the routed
+one. The seeded workloads are run at full size with sampled tokens computed
+one by one by the oracle (with the oracle's own schedule deciding which
+assignments are kept)."""
+import numpy as np
+import pytest
+
+from mokutil import TOL_BF16, Bf16Array, assert_close_inf, f64, to_dev
+
+from oracle import moe as omoe
+from oracle.schedule import build_schedule as oracle_schedule
+from workloads import CONFIGS, MoEShape, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import mixture_experts_layer_build_amd as mok  # noqa: E402
+
+
+def gpu_forward(c: MoEShape, inp: dict, mult: float, with_context=False, minibatch=0):
+    d = to_dev(inp)
+    cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=c.T,
+                        shared_intermediate=c.I_s, capacity_multiplier=mult, expert_pad=c.expert_pad,
+                        minibatch_size=minibatch)
+    ws = mok.Workspace(cfg)
+    sched = mok.build_schedule(ws, d["top_experts"])
+    ctx = torch.empty(mok.context_bytes(cfg), dtype=torch.uint8, device="cuda") if with_context else None
+    out = mok.forward(ws, sched, d["x"], d["router_weights"], d["weights"], context=ctx)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), (ws, sched, ctx, d)
+
+
+def oracle_full(inp, mult):
+    return omoe.forward(f64(inp["x"]), inp["top_experts"], inp["router_weights"], f64(inp["w_gate"]),
+                        f64(inp["w_up"]), f64(inp["w_down"]), f64(inp["s_gate"]), f64(inp["s_up"]),
+                        f64(inp["s_down"]), capacity_multiplier=mult)
+
+
+SMALL = [
+    # name, T, H, I, E, k, I_s, mult, invalid ids
+    ("ragged", 300, 256, 192, 5, 3, 128, 1.0, False),
+    ("drops", 300, 256, 192, 5, 3, 128, 0.3, True),
+    ("wide_n", 200, 384, 320, 3, 2, 0, 1.0, False),
+    ("many_experts", 513, 128, 64, 40, 4, 64, 1.0, True),
+    ("one_expert", 260, 256, 128, 1, 1, 0, 1.0, False),
+    ("deep_k", 130, 1024, 256, 4, 2, 512, 0.6, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[s[0] for s in SMALL])
+def test_forward_bf16_small(case):
+    name, T, H, I, E, k, Is, mult, invalid = case
+    c = MoEShape(name, T=T, H=H, I=I, E=E, k=k, I_s=Is, seed=77, w_std=0.05)
+    inp = make_inputs(c)
+    if invalid:
+        top = inp["top_experts"].copy()
+        top[::7, 0] = -1
+        top[3::11, -1] = E + 3
+        inp["top_experts"] = top
+    print(f"forward small {name}", flush=True)
+    got, _ = gpu_forward(c, inp, mult)
+    ref = oracle_full(inp, mult)
+    assert_close_inf(got, ref, TOL_BF16, name)
+
+
+def test_forward_bf16_tiny_workload():
+    c = CONFIGS["tiny_bf16_fwd"]
+    inp = make_inputs(c)
+    got, _ = gpu_forward(c, inp, c.capacity_multiplier)
+    ref = oracle_full(inp, c.capacity_multiplier)
+    err, scale = assert_close_inf(got, ref, TOL_BF16, "tiny")
+    print(f"tiny: max err {err:.3g} of max {scale:.3g}")
+
+
+def sampled_check(c: MoEShape, mult: float, n_tokens=40, seed=0):
+    inp = make_inputs(c)
+    got, _ = gpu_forward(c, inp, mult)
+    sched = oracle_schedule(inp["top_experts"], c.E, mult, c.expert_pad)
+    rng = np.random.default_rng(seed)
+    toks = np.unique(np.concatenate([[0, c.T - 1], rng.integers(0, c.T, size=n_tokens)]))
+    ref = omoe.forward_tokens(toks, Bf16Array(inp["x"]), inp["top_experts"], inp["router_weights"],
+                              Bf16Array(inp["w_gate"]), Bf16Array(inp["w_up"]), Bf16Array(inp["w_down"]),
+                              f64(inp["s_gate"]), f64(inp["s_up"]), f64(inp["s_down"]),
+                              slot_row=sched["slot_row"])
+    err, scale = assert_close_inf(got[toks], ref, TOL_BF16, c.name)
+    print(f"{c.name} mult={mult}: sampled {toks.size} tokens, max err {err:.3g} of max {scale:.3g}, "
+          f"dropped {sched['dropped']}")
+    assert np.all(np.isfinite(got))
+
+
+def test_forward_bf16_8192_tokens_sampled():
+    c = CONFIGS["t8192_bf16_fwd"]
+    sampled_check(c, 1.0)
+
+
+@pytest.mark.parametrize("mult", [1.0, 0.5])
+def test_forward_bf16_skewed_sampled(mult):
+    c = CONFIGS["skew_bf16_fwd"]
+    sampled_check(c, mult)
+
+
+def test_forward_bf16_context_holds_gate_and_up():
+    c = MoEShape("ctx", T=200, H=256, I=128, E=4, k=2, I_s=64, seed=5, w_std=0.05)
+    inp = make_inputs(c)
+    got, (ws, sched, ctx, d) = gpu_forward(c, inp, 1.0, with_context=True)
+    ref, osched, parts = omoe.forward(f64(inp["x"]), inp["top_experts"], inp["router_weights"],
+                                      f64(inp["w_gate"]), f64(inp["w_up"]), f64(inp["w_down"]),
+                                      f64(inp["s_gate"]), f64(inp["s_up"]), f64(inp["s_down"]),
+                                      return_parts=True)
+    assert_close_inf(got, ref, TOL_BF16, "out")
+    L = ws.layout
+    n = L.rows_cap_max * c.I + c.T * c.I_s
+    part = (n * 2 + 255) // 256 * 256
+    ctxb = ctx.cpu()
+    def view(i):
+        return ctxb[i * part: i * part + n * 2].view(torch.bfloat16).float().numpy().astype(np.float64)
+    G, U = view(0), view(1)
+    for e in range(c.E):
+        p = parts.get(e)
+        if p is None:
+            continue
+        rows = p["rows"]
+        g = G[: L.rows_cap_max * c.I].reshape(L.rows_cap_max, c.I)[rows]
+        u = U[: L.rows_cap_max * c.I].reshape(L.rows_cap_max, c.I)[rows]
+        assert_close_inf(g, p["g"], TOL_BF16, f"G expert {e}")
+        assert_close_inf(u, p["u"], TOL_BF16, f"U expert {e}")
+    gs = G[L.rows_cap_max * c.I:].reshape(c.T, c.I_s)
+    assert_close_inf(gs, parts["shared"]["g"], TOL_BF16, "G shared")
+
+
+def test_forward_bf16_deterministic_and_graph_replay():
+    c = MoEShape("det", T=700, H=256, I=192, E=6, k=3, I_s=64, seed=11, w_std=0.05)
+    inp = make_inputs(c)
+    d = to_dev(inp)
+    cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=c.T,
+                        shared_intermediate=c.I_s)
+    ws = mok.Workspace(cfg)
+    sched = mok.build_schedule(ws, d["top_experts"])
+    a = mok.forward(ws, sched, d["x"], d["router_weights"], d["weights"]).clone()
+    b = mok.forward(ws, sched, d["x"], d["router_weights"], d["weights"]).clone()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    out = torch.zeros_like(a)
+    sbuf = torch.zeros_like(sched)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            mok.build_schedule(ws, d["top_experts"], sbuf)
+            mok.forward(ws, sbuf, d["x"], d["router_weights"], d["weights"], out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), a.view(torch.int16))
+
+
+def test_forward_rejects_bad_arguments():
+    c = MoEShape("bad", T=64, H=128, I=64, E=2, k=1, I_s=0, seed=1)
+    inp = make_inputs(c)
+    d = to_dev(inp)
+    cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=c.T)
+    ws = mok.Workspace(cfg)
+    sched = mok.build_schedule(ws, d["top_experts"])
+    with pytest.raises(mok.MokError):
+        mok.forward(ws, sched[:16], d["x"], d["router_weights"], d["weights"])
+    w = dict(d["weights"])
+    w["shared_gate"] = w["routed_gate"][0]  # shared pointer without a shared expert
+    with pytest.raises(mok.MokError):
+        mok.forward(ws, sched, d["x"], d["router_weights"], w)
+    with pytest.raises(mok.MokError):
+        mok.build_schedule(ws, torch.zeros((c.T + 1, 1), dtype=torch.int64, device="cuda"))
