@@ -90,6 +90,14 @@ __host__ __device__ __forceinline__ uint32_t e4m3_encode_scaled(float v, int X) 
   return code | sign;
 }
 
+typedef unsigned int u32x4 __attribute__((vector_size(16)));
+
+// Raw buffer resource over [base, base + bytes): loads at offsets at or past
+// `bytes` return zeros. Word 3 selects 32-bit data format (gfx9 family).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Wave-wide helpers (wave64).
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 

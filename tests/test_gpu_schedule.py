@@ -118,9 +118,15 @@ def test_build_schedule_is_deterministic_and_graph_capturable():
     cfg = mok.MoKConfig(hidden=128, intermediate=64, num_experts=32, topk=8, max_tokens=4096,
                         capacity_multiplier=0.25)
     ws = mok.Workspace(cfg)
+
+    def fields(buf):
+        # the defined fields only (alignment gaps between fields are never written)
+        return {n: v.clone() for n, v in mok.schedule_fields(ws, buf).items()}
+
     a = mok.build_schedule(ws, top).clone()
-    b = mok.build_schedule(ws, top).clone()
-    assert torch.equal(a, b)
+    fa = fields(a)
+    fb = fields(mok.build_schedule(ws, top))
+    assert all(torch.equal(fa[n], fb[n]) for n in fa)
     # capture: any host synchronisation inside the call would make capture fail
     buf = torch.zeros_like(a)
     s = torch.cuda.Stream()
@@ -135,4 +141,5 @@ def test_build_schedule_is_deterministic_and_graph_capturable():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(buf, a)
+        fg = fields(buf)
+        assert all(torch.equal(fa[n], fg[n]) for n in fa)
