@@ -301,6 +301,12 @@ extern "C" mok_status mok_build_schedule(mok_workspace* ws, const int64_t* top_e
   return launch_schedule(ws, top_experts, T, schedule, (hipStream_t)stream) == hipSuccess ? MOK_OK : MOK_ERR_HIP;
 }
 
+// MXFP8 GEMMs load one dword of E8M0 scales (4 blocks of 32) per row and
+// two K steps, so every contraction length must be a multiple of 128.
+static bool mxfp8_shapes_ok(const mok_config& c) {
+  return c.hidden % 128 == 0 && c.intermediate % 128 == 0 && c.shared_intermediate % 128 == 0;
+}
+
 static mok_status check_weights(const mok_config& c, mok_mode mode, const mok_weights* w, bool need_scales) {
   if (!w || !w->routed_gate || !w->routed_up || !w->routed_down) return MOK_ERR_INVALID_ARGUMENT;
   const bool sh = c.shared_intermediate > 0;
@@ -322,6 +328,7 @@ extern "C" mok_status mok_forward(mok_workspace* ws, mok_mode mode, const void* 
   if (schedule_bytes < ws->layout.total) return MOK_ERR_BUFFER_TOO_SMALL;
   mok_status st = check_weights(ws->cfg, mode, weights, true);
   if (st != MOK_OK) return st;
+  if (mode == MOK_MODE_MXFP8 && !mxfp8_shapes_ok(ws->cfg)) return MOK_ERR_UNSUPPORTED;
   if (context && context_bytes < mok_context_bytes(&ws->cfg, mode)) return MOK_ERR_BUFFER_TOO_SMALL;
   DeviceGuard g(ws->device);
   if (!g.ok) return MOK_ERR_HIP;

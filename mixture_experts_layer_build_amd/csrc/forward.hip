@@ -1,0 +1,164 @@
+// Forward of the grouped SwiGLU expert MLP and the router-weighted combine,
+// in BF16 and in MXFP8.
+//
+// "nemo_automodel.components.moe.mok_experts", GroupedExpertsMoK.forward and
+// _MoKRuntime.forward: fused shared and routed SwiGLU experts; routed
+// gate/up [E, I, H], down [E, H, I]; shared gate/up [I_s, H], down [H, I_s];
+// no expert bias. "Mixture-of-Kittens: a deterministic MoE megakernel for
+// NVL72 racks", section "The two API layers and the schedule object": the
+// schedule drives both dispatch (here a gather of token rows into the
+// expert-contiguous order) and combine (a gather-sum back to token order);
+// section "Tuning the five hyperparameters before production": in MXFP8 mode
+// the activations enter in BF16 and are quantized here, the weights arrive
+// pre-quantized.
+//
+// Launch sequence (all stream-ordered, no host synchronisation; every grid
+// is sized from the configuration, the real counts are read on the device):
+//   [MXFP8: quantize x along H into E4M3 + E8M0]
+//   gate_up : grouped GEMM, epilogue h = silu(g) * u (bf16, or MXFP8 along I)
+//   down    : grouped GEMM, epilogue y = w_r * acc (bf16)
+//   combine : out[t] = bf16(sum over j in slot order of y[slot_row[t, j]]
+//             + y_shared[t]), fp32 accumulation, no atomics.
+#include "device_common.h"
+#include "gemm_nt.h"
+#include "mok_internal.h"
+
+namespace mok {
+namespace {
+
+// out[t] = bf16(sum_j y[slot_row[t*k + j]] (kept slots, slot order) + y_shared[t]).
+__global__ void __launch_bounds__(256) combine_bf16(const int32_t* __restrict__ hdr, const int32_t* __restrict__ slot_row,
+                                                    const uint16_t* __restrict__ y, const uint16_t* __restrict__ y_shared,
+                                                    uint16_t* __restrict__ out, int H, int k) {
+  const int T = hdr[HDR_T];
+  const int nchunk = H / 8;
+  for (int t = blockIdx.x; t < T; t += gridDim.x) {
+    const int32_t* sl = slot_row + (int64_t)t * k;
+    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const int row = sl[j];
+        if (row < 0) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)row * H + c * 8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += u2f(w[q] << 16);
+          acc[2 * q + 1] += u2f(w[q] & 0xFFFF0000u);
+        }
+      }
+      if (y_shared) {
+        const uint4 v = *reinterpret_cast<const uint4*>(y_shared + (int64_t)t * H + c * 8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += u2f(w[q] << 16);
+          acc[2 * q + 1] += u2f(w[q] & 0xFFFF0000u);
+        }
+      }
+      uint4 o;
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
+      *reinterpret_cast<uint4*>(out + (int64_t)t * H + c * 8) = o;
+    }
+  }
+}
+
+}  // namespace
+
+static void fill_schedule(nt::Params& p, const mok_workspace* ws, const SchedView& v) {
+  const mok_config& c = ws->cfg;
+  p.hdr = v.header;
+  p.offsets = v.offsets;
+  p.kept = v.kept;
+  p.tiles = v.tiles + tile_bm_index(nt::BM) * (c.num_experts + 2);
+  p.row_src = v.row_src;
+  p.E = c.num_experts;
+  p.k = c.topk;
+  p.H = c.hidden;
+  p.I = c.intermediate;
+  p.Is = c.shared_intermediate;
+  p.rows_cap_max = ws->layout.rows_cap_max;
+}
+
+hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a, hipStream_t s) {
+  const mok_config& c = ws->cfg;
+  const SchedView v = sched_view(const_cast<void*>(sched), ws->layout);
+  const int grid = ws->num_cus * nt::kBlocksPerCu;
+  const size_t ce = ctx_elems(c, ws->layout);
+  nt::Params p{};
+  fill_schedule(p, ws, v);
+  p.router_w = a.router_w;
+  p.ctx_g = (uint16_t*)a.ctx_g;
+  p.ctx_u = (uint16_t*)a.ctx_u;
+  // h: bf16 in BF16 mode; E4M3 codes then E8M0 scales in MXFP8 mode (in the
+  // context's h region when a context is kept, else in the workspace).
+  uint8_t* hq = nullptr;
+  uint8_t* hq_scale = nullptr;
+  if (a.mxfp8) {
+    hq = a.ctx_g ? (uint8_t*)a.h : ws->hq;
+    hq_scale = a.ctx_g ? (uint8_t*)a.h + ce : ws->hq_scale;
+    LaunchTimer tm(ws, MOK_K_QUANT_X, s);
+    MOK_HIP_TRY(launch_quantize_rows_dev(a.x, v.header, c.max_tokens, c.hidden, ws->xq, ws->xq_scale, s));
+  }
+  // gate/up
+  if (a.mxfp8) {
+    p.a_tok = ws->xq;
+    p.a_tok_scale = ws->xq_scale;
+    p.out = hq;
+    p.out_scale = hq_scale;
+    p.b0s = a.w->routed_gate_scale;
+    p.b1s = a.w->routed_up_scale;
+    p.sb0s = a.w->shared_gate_scale;
+    p.sb1s = a.w->shared_up_scale;
+  } else {
+    p.a_tok = a.x;
+    p.out = a.h;
+  }
+  p.b0 = a.w->routed_gate;
+  p.b1 = a.w->routed_up;
+  p.sb0 = a.w->shared_gate;
+  p.sb1 = a.w->shared_up;
+  {
+    LaunchTimer tm(ws, MOK_K_GATE_UP, s);
+    if (a.mxfp8)
+      nt::grouped_gemm_nt<nt::GATE_UP, true><<<grid, nt::NTHR, 0, s>>>(p);
+    else
+      nt::grouped_gemm_nt<nt::GATE_UP, false><<<grid, nt::NTHR, 0, s>>>(p);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  // down
+  nt::Params d{};
+  fill_schedule(d, ws, v);
+  d.router_w = a.router_w;
+  d.a_row = a.mxfp8 ? (const void*)hq : a.h;
+  d.a_row_scale = hq_scale;
+  d.b0 = a.w->routed_down;
+  d.sb0 = a.w->shared_down;
+  d.b0s = a.w->routed_down_scale;
+  d.sb0s = a.w->shared_down_scale;
+  d.out = a.y;
+  {
+    LaunchTimer tm(ws, MOK_K_DOWN, s);
+    if (a.mxfp8)
+      nt::grouped_gemm_nt<nt::DOWN, true><<<grid, nt::NTHR, 0, s>>>(d);
+    else
+      nt::grouped_gemm_nt<nt::DOWN, false><<<grid, nt::NTHR, 0, s>>>(d);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  {
+    LaunchTimer tm(ws, MOK_K_COMBINE, s);
+    const int cgrid = (int)std::min<int64_t>(c.max_tokens, (int64_t)ws->num_cus * 8);
+    const uint16_t* y = (const uint16_t*)a.y;
+    const uint16_t* ys = c.shared_intermediate > 0 ? y + ws->layout.rows_cap_max * c.hidden : nullptr;
+    combine_bf16<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, ys, (uint16_t*)a.out, c.hidden, c.topk);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  return hipSuccess;
+}
+
+}  // namespace mok

@@ -124,13 +124,16 @@ struct FwdArgs {
   void* out;                  // bf16 [T,H]
   void* ctx_g;                // bf16 routed [rows_cap_max, I] then shared [T_max, I_s]; null = not kept
   void* ctx_u;
-  void* h;                    // bf16 h (routed rows then shared rows)
+  void* h;                    // h (routed rows then shared rows): bf16, or MXFP8 codes + scales
   void* y;                    // bf16 [(rows_cap_max + T_max), H]
   int mxfp8;
 };
 hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a, hipStream_t s);
-hipError_t launch_forward_bf16(mok_workspace* ws, const void* sched, const FwdArgs& a, hipStream_t s);
-hipError_t launch_forward_mxfp8(mok_workspace* ws, const void* sched, const FwdArgs& a, hipStream_t s);
+
+// Axis-1 MXFP8 quantization of a bf16 [T, cols] tensor whose row count T is
+// read on the device from a schedule header; the grid covers max_rows.
+hipError_t launch_quantize_rows_dev(const void* src, const int32_t* hdr, int64_t max_rows, int64_t cols, uint8_t* dst,
+                                    uint8_t* dst_scale, hipStream_t s);
 
 struct BwdArgs {
   const mok_weights* w;

@@ -54,6 +54,46 @@ __global__ void __launch_bounds__(256) quant_axis1_bf16(const uint16_t* __restri
   if (part == 0) scale[row * nblk_row + blk] = (uint8_t)(X + 127);
 }
 
+// axis = 1, bf16 source with the row count read on the device (the
+// schedule header's token count), over a grid sized for max_rows.
+__global__ void __launch_bounds__(256) quant_rows_dev_bf16(const uint16_t* __restrict__ src, const int32_t* __restrict__ hdr,
+                                                           int64_t cols, uint8_t* __restrict__ dst,
+                                                           uint8_t* __restrict__ scale) {
+  const int64_t rows = hdr[HDR_T];
+  const int64_t nblk_row = cols >> 5;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = g >> 2;
+  const int part = (int)(g & 3);
+  const bool live = b < rows * nblk_row;
+  int64_t row = 0, blk = 0;
+  uint4 raw = make_uint4(0, 0, 0, 0);
+  if (live) {
+    row = b / nblk_row;
+    blk = b - row * nblk_row;
+    raw = *reinterpret_cast<const uint4*>(src + row * cols + blk * 32 + part * 8);
+  }
+  uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t lo = (w[i] << 16) & 0x7FFFFFFFu, hi = w[i] & 0x7FFF0000u;
+    amax = max(amax, max(lo, hi));
+  }
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+  if (!live) return;
+  const int X = mx_block_exponent(amax);
+  uint32_t c[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t e0 = e4m3_encode_scaled(u2f(w[i] << 16), X);
+    uint32_t e1 = e4m3_encode_scaled(u2f(w[i] & 0xFFFF0000u), X);
+    c[i >> 1] |= (e0 | (e1 << 8)) << ((i & 1) * 16);
+  }
+  *reinterpret_cast<uint2*>(dst + row * cols + blk * 32 + part * 8) = make_uint2(c[0], c[1]);
+  if (part == 0) scale[row * nblk_row + blk] = (uint8_t)(X + 127);
+}
+
 // axis = 1, fp32 source: 8 lanes per block, 4 elements per lane.
 __global__ void __launch_bounds__(256) quant_axis1_f32(const float* __restrict__ src, int64_t rows, int64_t cols,
                                                        int64_t ld_src, uint8_t* __restrict__ dst, int64_t ld_dst,
@@ -143,6 +183,15 @@ __global__ void __launch_bounds__(256) quant_axis0(const T* __restrict__ src, in
 }
 
 }  // namespace
+
+hipError_t launch_quantize_rows_dev(const void* src, const int32_t* hdr, int64_t max_rows, int64_t cols, uint8_t* dst,
+                                    uint8_t* dst_scale, hipStream_t s) {
+  const int64_t lanes = max_rows * (cols >> 5) * 4;
+  const int64_t grid = (lanes + 255) / 256;
+  if (grid == 0) return hipSuccess;
+  quant_rows_dev_bf16<<<dim3((unsigned)grid), dim3(256), 0, s>>>((const uint16_t*)src, hdr, cols, dst, dst_scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const void* src, int src_is_fp32, int64_t rows, int64_t cols, int64_t ld_src, int axis,
                            uint8_t* dst, int64_t ld_dst, uint8_t* dst_scale, hipStream_t s) {

@@ -2,6 +2,5 @@
 #include "mok_internal.h"
 
 namespace mok {
-hipError_t launch_forward_mxfp8(mok_workspace*, const void*, const FwdArgs&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_backward(mok_workspace*, const void*, const BwdArgs&, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace mok

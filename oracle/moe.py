@@ -34,7 +34,7 @@ from . import mxfp8
 from .schedule import build_schedule
 
 __all__ = ["sigmoid", "silu", "forward", "forward_per_token", "forward_tokens",
-           "backward", "forward_mxfp8", "backward_mxfp8", "segment_rows"]
+           "backward", "forward_mxfp8", "forward_tokens_mxfp8", "backward_mxfp8", "segment_rows"]
 
 
 def sigmoid(z):
@@ -281,6 +281,51 @@ def forward_mxfp8(x, top_experts, router_weights, w_gate, w_up, w_down,
     if return_parts:
         return out, sched, parts
     return out
+
+
+def forward_tokens_mxfp8(tokens, x, top_experts, router_weights, w_gate, w_up, w_down,
+                         s_gate=None, s_up=None, s_down=None, slot_row=None):
+    """``forward_mxfp8`` for a subset of tokens, each computed on its own
+    (for sampled checks at full sizes): x_t quantized along H; the gate/up
+    weights of each expert it uses along H, the down weights along I; h
+    computed in float64 and quantized along I; weighted sum in float64.
+    ``slot_row`` as in ``forward_tokens``. Weight arguments may be any
+    indexable of float rows per expert (decoded lazily).
+
+    Pin (tests/test_oracle_moe.py): over all tokens of random small cases it
+    equals ``forward_mxfp8`` (with drops and invalid ids)."""
+    q = mxfp8.qdq
+    k = top_experts.shape[1]
+    E = w_gate.shape[0]
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache[e] = (q(np.asarray(w_gate[e], np.float64), axis=1), q(np.asarray(w_up[e], np.float64), axis=1),
+                        q(np.asarray(w_down[e], np.float64), axis=1))
+        return cache[e]
+
+    if s_gate is not None:
+        Sg = q(np.asarray(s_gate, np.float64), axis=1)
+        Su = q(np.asarray(s_up, np.float64), axis=1)
+        Sd = q(np.asarray(s_down, np.float64), axis=1)
+    outs = []
+    for t in tokens:
+        xt = q(np.asarray(x[t], np.float64)[None, :], axis=1)[0]
+        acc = np.zeros(xt.shape[0])
+        for j in range(k):
+            e = int(top_experts[t, j])
+            kept = (0 <= e < E) if slot_row is None else slot_row[t * k + j] >= 0
+            if not kept:
+                continue
+            Wg, Wu, Wd = expert(e)
+            h = q((silu(Wg @ xt) * (Wu @ xt))[None, :], axis=1)[0]
+            acc += float(router_weights[t, j]) * (Wd @ h)
+        if s_gate is not None:
+            h = q((silu(Sg @ xt) * (Su @ xt))[None, :], axis=1)[0]
+            acc += Sd @ h
+        outs.append(acc)
+    return np.stack(outs) if outs else np.zeros((0, x.shape[1]))
 
 
 def _qdq_rows_in_segment(v, q, block=32):

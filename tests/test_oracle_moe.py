@@ -171,3 +171,20 @@ def test_mxfp8_backward_structure_with_identity_quantizer():
     b = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
     for n in b:
         np.testing.assert_allclose(a[n], b[n], rtol=1e-11, atol=1e-11, err_msg=n)
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("mult", [1.0, 0.4])
+def test_forward_tokens_mxfp8_equals_forward_mxfp8(seed, mult):
+    rng = np.random.default_rng(100 + seed)
+    T, H, I, E, k, Is = 10, 64, 32, 3, 2, 32
+    x = rng.standard_normal((T, H))
+    top = rng.integers(-1, E + 1, size=(T, k)).astype(np.int64)
+    w = rng.uniform(0.1, 1.0, size=(T, k))
+    Wg, Wu = rng.standard_normal((E, I, H)) * 0.3, rng.standard_normal((E, I, H)) * 0.3
+    Wd = rng.standard_normal((E, H, I)) * 0.3
+    Sg, Su, Sd = rng.standard_normal((Is, H)) * 0.3, rng.standard_normal((Is, H)) * 0.3, rng.standard_normal((H, Is)) * 0.3
+    s = build_schedule(top, E, mult, 32)
+    a = moe.forward_mxfp8(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+    b = moe.forward_tokens_mxfp8(range(T), x, top, w, Wg, Wu, Wd, Sg, Su, Sd, slot_row=s["slot_row"])
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
