@@ -271,12 +271,13 @@ typedef enum mok_kernel_id {
   MOK_K_GATE_UP,
   MOK_K_DOWN,
   MOK_K_COMBINE,
+  MOK_K_BWD_TRANSPOSE,
+  MOK_K_BWD_GATHER,
   MOK_K_BWD_DH,
   MOK_K_BWD_DW_REDUCE,
   MOK_K_BWD_DX_ROWS,
   MOK_K_BWD_DX_SUM,
-  MOK_K_BWD_DWD,
-  MOK_K_BWD_DWGU,
+  MOK_K_BWD_DW,
   MOK_K_BWD_QUANT,
   MOK_K_COUNT
 } mok_kernel_id;

@@ -29,7 +29,7 @@ EXPORTS = (
 
 HDR_FIELDS = ("T", "k", "E", "C", "P", "rows_cap", "n_mb", "minibatch", "dropped", "invalid",
               "rows_total", "hash")
-KERNEL_COUNT = 15
+KERNEL_COUNT = 16
 TILE_BMS = (32, 64, 128, 256)
 
 

@@ -125,19 +125,37 @@ struct DeviceGuard {
   }
 };
 
+// Scratch parts, in allocation order.
+enum ScratchPart : int {
+  SP_SCHED = 0,  // schedule chunk histograms
+  SP_H,          // h when no context is kept (bf16 or MXFP8 codes)
+  SP_Y,          // y rows (bf16), reused for the backward's dA rows
+  SP_XQ,         // x in MXFP8 (+ scales)
+  SP_HQ,         // h in MXFP8 (+ scales) when no context is kept
+  SP_WT,         // transposed weights for the backward (routed + shared)
+  SP_DGUH,       // dG, dU, w*h (3 x context-sized)
+  SP_DWP,        // partial router-weight gradients
+  SP_ROWS,       // x and grad_out rows in schedule order
+  SP_COUNT
+};
+
 size_t workspace_bytes(const mok_config& c, const Layout& L, size_t* parts) {
-  const int64_t Tm = c.max_tokens, H = c.hidden;
+  const int64_t Tm = c.max_tokens, H = c.hidden, E = c.num_experts, I = c.intermediate, Is = c.shared_intermediate;
   const int64_t rowsR = L.rows_cap_max;
   const int64_t n_chunks_max = std::max<int64_t>(1, 24 * 1024 / c.num_experts);
-  size_t p[8] = {
-      (size_t)n_chunks_max * c.num_experts * 4 + (size_t)n_chunks_max * 4,  // schedule chunk histograms
-      ctx_elems(c, L) * 2,                                                  // h when no context is kept
-      (size_t)(rowsR + Tm) * H * 2,                                         // y rows (bf16)
-      (size_t)Tm * H + (size_t)Tm * (H / 32),                               // x in MXFP8 (+ scales)
-      ctx_elems(c, L) + ctx_elems(c, L) / 32,                               // h in MXFP8 (+ scales)
-      0, 0, 0};
+  const size_t ce = ctx_elems(c, L);
+  size_t p[SP_COUNT] = {
+      (size_t)n_chunks_max * E * 4 + (size_t)n_chunks_max * 4,
+      ce * 2,
+      (size_t)(rowsR + Tm) * H * 2,
+      (size_t)Tm * H + (size_t)Tm * (H / 32),
+      ce + ce / 32,
+      3 * align_up((size_t)E * I * H * 2, 256) + 3 * align_up((size_t)Is * H * 2, 256),
+      3 * align_up(ce * 2, 256),
+      (size_t)(rowsR + Tm) * dw_parts(c) * 4,
+      2 * align_up((size_t)rowsR * H * 2, 256)};
   size_t total = 0;
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < SP_COUNT; ++i) {
     if (parts) parts[i] = align_up(p[i], 256);
     total += align_up(p[i], 256);
   }
@@ -182,6 +200,9 @@ extern "C" mok_status mok_validate_config(const mok_config* c) {
   if (c->max_tokens * (int64_t)c->topk >= (int64_t)1 << 31) return MOK_ERR_UNSUPPORTED;
   const Layout L = schedule_layout(*c);
   if (L.rows_cap_max + c->max_tokens >= (int64_t)1 << 31) return MOK_ERR_UNSUPPORTED;
+  // token-indexed operands are read through one buffer range each, offsets
+  // below 2 GiB (the kernels' out-of-range marker sits at 2 GiB)
+  if (c->max_tokens * (int64_t)c->hidden * 2 >= (int64_t)1 << 31) return MOK_ERR_UNSUPPORTED;
   return MOK_OK;
 }
 
@@ -244,7 +265,7 @@ extern "C" mok_status mok_workspace_create(const mok_config* c, int device, mok_
     delete ws;
     return MOK_ERR_HIP;
   }
-  size_t parts[8];
+  size_t parts[SP_COUNT];
   ws->scratch_bytes = workspace_bytes(*c, ws->layout, parts);
   if (hipMalloc((void**)&ws->scratch, ws->scratch_bytes) != hipSuccess) {
     delete ws;
@@ -254,18 +275,42 @@ extern "C" mok_status mok_workspace_create(const mok_config* c, int device, mok_
   ws->n_chunks_max = std::max<int64_t>(1, 24 * 1024 / c->num_experts);
   ws->chunk_hist = (int32_t*)p;
   ws->chunk_invalid = (int32_t*)(p + (size_t)ws->n_chunks_max * c->num_experts * 4);
-  p += parts[0];
+  p += parts[SP_SCHED];
   ws->hbuf = p;
-  ws->hbuf_bytes = parts[1];
-  p += parts[1];
+  ws->hbuf_bytes = parts[SP_H];
+  p += parts[SP_H];
   ws->ybuf = p;
-  p += parts[2];
+  p += parts[SP_Y];
   ws->xq = (uint8_t*)p;
   ws->xq_scale = (uint8_t*)p + (size_t)c->max_tokens * c->hidden;
-  p += parts[3];
+  p += parts[SP_XQ];
+  const size_t ce = ctx_elems(*c, ws->layout);
   ws->hq = (uint8_t*)p;
-  ws->hq_scale = (uint8_t*)p + ctx_elems(*c, ws->layout);
-  p += parts[4];
+  ws->hq_scale = (uint8_t*)p + ce;
+  p += parts[SP_HQ];
+  {
+    const size_t wr = align_up((size_t)c->num_experts * c->intermediate * c->hidden * 2, 256);
+    const size_t wsh = align_up((size_t)c->shared_intermediate * c->hidden * 2, 256);
+    BwdScratch& b = ws->bwd;
+    b.wdT = (uint16_t*)p;
+    b.wgT = (uint16_t*)(p + wr);
+    b.wuT = (uint16_t*)(p + 2 * wr);
+    b.sdT = (uint16_t*)(p + 3 * wr);
+    b.sgT = (uint16_t*)(p + 3 * wr + wsh);
+    b.suT = (uint16_t*)(p + 3 * wr + 2 * wsh);
+    p += parts[SP_WT];
+    const size_t cb = align_up(ce * 2, 256);
+    b.dg = (uint16_t*)p;
+    b.du = (uint16_t*)(p + cb);
+    b.hw = (uint16_t*)(p + 2 * cb);
+    p += parts[SP_DGUH];
+    b.dw_part = (float*)p;
+    p += parts[SP_DWP];
+    const size_t rb = align_up((size_t)ws->layout.rows_cap_max * c->hidden * 2, 256);
+    b.x_rows = (uint16_t*)p;
+    b.dout_rows = (uint16_t*)(p + rb);
+    p += parts[SP_ROWS];
+  }
   *out = ws;
   return MOK_OK;
 }
@@ -410,9 +455,9 @@ extern "C" mok_status mok_mxfp8_quantize(const void* src, int src_is_fp32, int64
 // ------------------------------------------------------------------------
 extern "C" const char* mok_kernel_name(int id) {
   static const char* names[MOK_K_COUNT] = {
-      "sched_count", "sched_scan",     "sched_scatter", "sched_minibatch", "quant_x",      "gate_up",
-      "down",        "combine",        "bwd_dh",        "bwd_dw_reduce",   "bwd_dx_rows",  "bwd_dx_sum",
-      "bwd_dwd",     "bwd_dwgu",       "bwd_quant"};
+      "sched_count", "sched_scan", "sched_scatter", "sched_minibatch", "quant_x",      "gate_up",
+      "down",        "combine",    "bwd_transpose", "bwd_gather",      "bwd_dh",       "bwd_dw_reduce",
+      "bwd_dx_rows", "bwd_dx_sum", "bwd_dw",        "bwd_quant"};
   if (id < 0 || id >= MOK_K_COUNT) return "unknown";
   return names[id];
 }

@@ -1,0 +1,281 @@
+// BF16 backward of the grouped SwiGLU expert MLP.
+//
+// "nemo_automodel.components.moe.mok_experts", _MoKRuntime.backward: one
+// gradient per float input of the forward (x, router weights, the three
+// routed and the three shared weight tensors), reusing the forward's
+// schedule and saved context; the integer expert ids get none.
+// "Mixture-of-Kittens: a deterministic MoE megakernel for NVL72 racks",
+// section "The two API layers and the schedule object": backward takes the
+// same schedule object as forward.
+//
+// Per kept row r (token t, expert e, router weight w), with G, U, h saved by
+// the forward and y = W_d h the unweighted expert output:
+//   dh_hat = W_d^T dOut[t]                 d_router_weight = <dh_hat, h> = <dOut[t], y>
+//   dh = w * dh_hat                        dG = dh * U * s * (1 + G (1 - s)), s = sigmoid(G)
+//   dU = dh * silu(G)                      dA_r = W_g^T dG + W_u^T dU
+//   dx[t] = sum over t's kept rows of dA_r (+ the shared expert's row)
+//   dW_d[e] += dOut[t] (w h)^T,  dW_g[e] += dG x_t^T,  dW_u[e] += dU x_t^T
+// and the same for the shared expert with w = 1 (no router-weight gradient).
+//
+// Launch sequence (stream-ordered, no host synchronisation):
+//   transpose : W_d^T [E, I, H], W_g^T and W_u^T [E, H, I] (and shared)
+//   gather    : x and grad_out rows copied into schedule order
+//   bwd_dh    : NT grouped GEMM grad_out-rows x W_d^T; epilogue writes dG,
+//               dU, w*h and per-tile partial sums of d_router_weight
+//   dw reduce : d_router_weights[t, j] = fixed-order sum of the partials
+//   bwd_dx    : NT grouped GEMM [dG | dU] x [W_g^T | W_u^T] -> dA rows
+//   dx        : fixed-order gather-sum of dA rows back to token order
+//   bwd_dw    : TN grouped GEMM, the three weight gradients per expert
+#include "device_common.h"
+#include "gemm_nt.h"
+#include "gemm_tn.h"
+#include "mok_internal.h"
+
+namespace mok {
+namespace {
+
+// out[b][c][r] = in[b][r][c] for bf16 [nb][R][C]; R, C multiples of 64.
+__global__ void __launch_bounds__(256) transpose_bf16(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                      int R, int C) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int tiles_c = C / 64;
+  const int tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
+  const int64_t b = blockIdx.y;
+  const uint16_t* src = in + b * (int64_t)R * C;
+  uint16_t* dst = out + b * (int64_t)R * C;
+  const int t = threadIdx.x;
+  // load 64 rows x 64 columns: 8 threads per row, 8 elements each, 2 passes
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int r = pass * 32 + (t >> 3), c = (t & 7) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)(tr * 64 + r) * C + tc * 64 + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tile[r][c + 2 * q] = (uint16_t)(w[q] & 0xFFFFu);
+      tile[r][c + 2 * q + 1] = (uint16_t)(w[q] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int c = pass * 32 + (t >> 3), r = (t & 7) * 8;  // output row c, columns r .. r+7
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = (uint32_t)tile[r + 2 * q][c] | ((uint32_t)tile[r + 2 * q + 1][c] << 16);
+    *reinterpret_cast<uint4*>(dst + (int64_t)(tc * 64 + c) * R + tr * 64 + r) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// x_rows[r] = x[token(r)], dout_rows[r] = grad_out[token(r)] for the kept
+// rows of the schedule (padding rows are never read).
+__global__ void __launch_bounds__(256) gather_rows(const int32_t* __restrict__ hdr, const int32_t* __restrict__ row_src,
+                                                   const uint16_t* __restrict__ x, const uint16_t* __restrict__ dout,
+                                                   uint16_t* __restrict__ x_rows, uint16_t* __restrict__ dout_rows,
+                                                   int H, int k) {
+  const int rows = hdr[HDR_ROWS_TOTAL];
+  const int nch = H / 8;
+  for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+    const int a = row_src[r];
+    if (a < 0) continue;
+    const int64_t tok = a / k;
+    for (int c = threadIdx.x; c < nch; c += blockDim.x) {
+      *reinterpret_cast<uint4*>(x_rows + (int64_t)r * H + c * 8) = *reinterpret_cast<const uint4*>(x + tok * H + c * 8);
+      *reinterpret_cast<uint4*>(dout_rows + (int64_t)r * H + c * 8) =
+          *reinterpret_cast<const uint4*>(dout + tok * H + c * 8);
+    }
+  }
+}
+
+// d_router_weights[a] = sum over parts (fixed order) of dw_part[slot_row[a]],
+// 0 for dropped or invalid assignments.
+__global__ void __launch_bounds__(256) reduce_dw(const int32_t* __restrict__ hdr, const int32_t* __restrict__ slot_row,
+                                                 const float* __restrict__ dw_part, int parts, int n_parts_used, int k,
+                                                 float* __restrict__ dwr) {
+  const int64_t n = (int64_t)hdr[HDR_T] * k;
+  for (int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; a < n; a += (int64_t)gridDim.x * blockDim.x) {
+    const int row = slot_row[a];
+    float s = 0.f;
+    if (row >= 0)
+      for (int q = 0; q < n_parts_used; ++q) s += dw_part[(int64_t)row * parts + q];
+    dwr[a] = s;
+  }
+}
+
+// dx[t] = bf16(sum_j dA[slot_row[t, j]] + dA_shared[t]), fp32, slot order.
+__global__ void __launch_bounds__(256) gather_sum_rows(const int32_t* __restrict__ hdr, const int32_t* __restrict__ slot_row,
+                                                       const uint16_t* __restrict__ y, const uint16_t* __restrict__ y_shared,
+                                                       uint16_t* __restrict__ out, int H, int k) {
+  const int T = hdr[HDR_T];
+  const int nchunk = H / 8;
+  for (int t = blockIdx.x; t < T; t += gridDim.x) {
+    const int32_t* sl = slot_row + (int64_t)t * k;
+    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const int row = sl[j];
+        if (row < 0) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)row * H + c * 8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += u2f(w[q] << 16);
+          acc[2 * q + 1] += u2f(w[q] & 0xFFFF0000u);
+        }
+      }
+      if (y_shared) {
+        const uint4 v = *reinterpret_cast<const uint4*>(y_shared + (int64_t)t * H + c * 8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += u2f(w[q] << 16);
+          acc[2 * q + 1] += u2f(w[q] & 0xFFFF0000u);
+        }
+      }
+      uint4 o;
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
+      *reinterpret_cast<uint4*>(out + (int64_t)t * H + c * 8) = o;
+    }
+  }
+}
+
+hipError_t transpose(const void* in, void* out, int nb, int R, int C, hipStream_t s) {
+  if (nb == 0) return hipSuccess;
+  dim3 grid((unsigned)((R / 64) * (C / 64)), (unsigned)nb);
+  transpose_bf16<<<grid, 256, 0, s>>>((const uint16_t*)in, (uint16_t*)out, R, C);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int dw_parts(const mok_config& c) {
+  const int Imax = c.intermediate > c.shared_intermediate ? c.intermediate : c.shared_intermediate;
+  return 2 * ((Imax + nt::BN - 1) / nt::BN);
+}
+
+hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& a, hipStream_t s) {
+  if (a.mxfp8) return hipErrorNotSupported;
+  const mok_config& c = ws->cfg;
+  const int E = c.num_experts, H = c.hidden, I = c.intermediate, Is = c.shared_intermediate, k = c.topk;
+  const SchedView v = sched_view(const_cast<void*>(sched), ws->layout);
+  const int64_t rcm = ws->layout.rows_cap_max;
+  const mok_weights* w = a.w;
+  const mok_grads* g = a.g;
+  BwdScratch& b = ws->bwd;
+  {
+    LaunchTimer tm(ws, MOK_K_BWD_TRANSPOSE, s);
+    MOK_HIP_TRY(transpose(w->routed_down, b.wdT, E, H, I, s));  // [E,H,I] -> [E,I,H]
+    MOK_HIP_TRY(transpose(w->routed_gate, b.wgT, E, I, H, s));  // [E,I,H] -> [E,H,I]
+    MOK_HIP_TRY(transpose(w->routed_up, b.wuT, E, I, H, s));
+    if (Is > 0) {
+      MOK_HIP_TRY(transpose(w->shared_down, b.sdT, 1, H, Is, s));
+      MOK_HIP_TRY(transpose(w->shared_gate, b.sgT, 1, Is, H, s));
+      MOK_HIP_TRY(transpose(w->shared_up, b.suT, 1, Is, H, s));
+    }
+  }
+  const int rows_grid = (int)std::min<int64_t>(rcm, (int64_t)ws->num_cus * 8);
+  {
+    LaunchTimer tm(ws, MOK_K_BWD_GATHER, s);
+    gather_rows<<<rows_grid, 256, 0, s>>>(v.header, v.row_src, (const uint16_t*)a.x, (const uint16_t*)a.grad_out,
+                                          b.x_rows, b.dout_rows, H, k);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  const int grid = ws->num_cus * nt::kBlocksPerCu;
+  auto sched_params = [&](nt::Params& p) {
+    p.hdr = v.header;
+    p.offsets = v.offsets;
+    p.kept = v.kept;
+    p.tiles = v.tiles + tile_bm_index(nt::BM) * (E + 2);
+    p.row_src = v.row_src;
+    p.E = E;
+    p.k = k;
+    p.H = H;
+    p.I = I;
+    p.Is = Is;
+    p.rows_cap_max = rcm;
+  };
+  {
+    nt::Params p{};
+    sched_params(p);
+    p.router_w = a.router_w;
+    p.a_tok = a.grad_out;
+    p.b0 = b.wdT;
+    p.sb0 = b.sdT;
+    p.g_in = (const uint16_t*)a.ctx_g;
+    p.u_in = (const uint16_t*)a.ctx_u;
+    p.h_in = (const uint16_t*)a.ctx_h;
+    p.dg_out = b.dg;
+    p.du_out = b.du;
+    p.hw_out = b.hw;
+    p.dw_part = b.dw_part;
+    p.dw_parts = dw_parts(c);
+    LaunchTimer tm(ws, MOK_K_BWD_DH, s);
+    nt::grouped_gemm_nt<nt::BWD_DH, false><<<grid, nt::NTHR, 0, s>>>(p);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  {
+    LaunchTimer tm(ws, MOK_K_BWD_DW_REDUCE, s);
+    const int n_used = 2 * ((I + nt::BN - 1) / nt::BN);
+    const int64_t n = c.max_tokens * k;
+    const int rgrid = (int)std::min<int64_t>((n + 255) / 256, (int64_t)ws->num_cus * 16);
+    reduce_dw<<<rgrid, 256, 0, s>>>(v.header, v.slot_row, b.dw_part, dw_parts(c), n_used, k, g->d_router_weights);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  {
+    nt::Params p{};
+    sched_params(p);
+    p.a_row = b.dg;
+    p.a_row2 = b.du;
+    p.b0 = b.wgT;
+    p.b1 = b.wuT;
+    p.sb0 = b.sgT;
+    p.sb1 = b.suT;
+    p.out = ws->ybuf;
+    LaunchTimer tm(ws, MOK_K_BWD_DX_ROWS, s);
+    nt::grouped_gemm_nt<nt::BWD_DX, false><<<grid, nt::NTHR, 0, s>>>(p);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  {
+    LaunchTimer tm(ws, MOK_K_BWD_DX_SUM, s);
+    const int cgrid = (int)std::min<int64_t>(c.max_tokens, (int64_t)ws->num_cus * 8);
+    const uint16_t* y = (const uint16_t*)ws->ybuf;
+    gather_sum_rows<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, Is > 0 ? y + rcm * H : nullptr,
+                                          (uint16_t*)g->dx, H, k);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  {
+    tn::Params p{};
+    p.offsets = v.offsets;
+    p.kept = v.kept;
+    p.hdr = v.header;
+    p.E = E;
+    p.H = H;
+    p.I = I;
+    p.Is = Is;
+    p.rows_cap_max = rcm;
+    p.dout_rows = b.dout_rows;
+    p.x_rows = b.x_rows;
+    p.dout = (const uint16_t*)a.grad_out;
+    p.x = (const uint16_t*)a.x;
+    p.hw = b.hw;
+    p.dg = b.dg;
+    p.du = b.du;
+    p.d_wd = (uint16_t*)g->d_routed_down;
+    p.d_wg = (uint16_t*)g->d_routed_gate;
+    p.d_wu = (uint16_t*)g->d_routed_up;
+    p.d_sd = (uint16_t*)g->d_shared_down;
+    p.d_sg = (uint16_t*)g->d_shared_gate;
+    p.d_su = (uint16_t*)g->d_shared_up;
+    LaunchTimer tm(ws, MOK_K_BWD_DW, s);
+    tn::grouped_gemm_tn<<<ws->num_cus * tn::kBlocksPerCu, tn::NTHR, 0, s>>>(p);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  return hipSuccess;
+}
+
+}  // namespace mok

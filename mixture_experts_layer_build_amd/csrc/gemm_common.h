@@ -21,6 +21,8 @@
 namespace mok {
 
 typedef int i32x4v __attribute__((ext_vector_type(4)));
+typedef short i16x4v __attribute__((vector_size(8)));   // ds_read_b64_tr_b16 result
+typedef short i16x8v __attribute__((vector_size(16)));
 
 // Physical chunk = logical chunk ^ swz(row). 16-byte reads of 16
 // consecutive rows at one logical chunk hit 16 distinct 16-byte bank groups
@@ -48,11 +50,17 @@ __device__ __forceinline__ i32x4v rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
+// The resource as SGPR operands (wave-uniform by construction).
+__device__ __forceinline__ i32x4v sgpr(i32x4v r) {
+  return i32x4v{__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
+                __builtin_amdgcn_readfirstlane(r.z), __builtin_amdgcn_readfirstlane(r.w)};
+}
+
 // 16 bytes per lane from buffer offset voff + soff into LDS at m0 + 16 * lane.
 __device__ __forceinline__ void lds_dma16(i32x4v rs, uint32_t voff, uint32_t soff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(soff)),
+               : "v"(voff), "s"(sgpr(rs)), "s"(__builtin_amdgcn_readfirstlane(soff)),
                  "s"(__builtin_amdgcn_readfirstlane(m0))
                : "memory", "m0");
 }
@@ -63,7 +71,7 @@ __device__ __forceinline__ void lds_dma16(i32x4v rs, uint32_t voff, uint32_t sof
 __device__ __forceinline__ void lds_dma4(i32x4v rs, uint32_t voff, uint32_t soff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
                :
-               : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(soff)),
+               : "v"(voff), "s"(sgpr(rs)), "s"(__builtin_amdgcn_readfirstlane(soff)),
                  "s"(__builtin_amdgcn_readfirstlane(m0))
                : "memory", "m0");
 }

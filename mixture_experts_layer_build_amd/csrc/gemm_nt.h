@@ -204,11 +204,11 @@ grouped_gemm_nt(Params p) {
       float w = 0.f;
       if (r < t.m_end) {
         if (shared) {
-          src = r;
+          src = (MODE == GATE_UP || MODE == BWD_DH) ? r : tid;
           w = 1.f;
         } else {
           const int a = p.row_src[r];
-          src = (MODE == GATE_UP || MODE == BWD_DH) ? a / p.k : r;
+          src = (MODE == GATE_UP || MODE == BWD_DH) ? a / p.k : tid;  // token, or tile-local row
           if (MODE == DOWN || MODE == BWD_DH) w = p.router_w[a];
         }
       }
@@ -228,10 +228,12 @@ grouped_gemm_nt(Params p) {
       a_base = (const uint8_t*)p.a_tok;
       a_bytes = (uint32_t)((int64_t)T * K * ES);
     } else {
-      const int64_t sh_off = shared ? p.rows_cap_max * p.I * ES : 0;
-      a_base = (const uint8_t*)p.a_row + sh_off;
-      if (MODE == BWD_DX) a_base2 = (const uint8_t*)p.a_row2 + sh_off;
-      a_bytes = (uint32_t)(shared ? (int64_t)T * a_k * ES : p.rows_cap_max * a_k * ES);
+      // based at the tile's first row (rows are tile-local below), so the
+      // buffer ranges stay small whatever the total row count
+      const int64_t off0 = (shared ? p.rows_cap_max * p.I * ES : 0) + (int64_t)t.m0 * a_k * ES;
+      a_base = (const uint8_t*)p.a_row + off0;
+      if (MODE == BWD_DX) a_base2 = (const uint8_t*)p.a_row2 + off0;
+      a_bytes = (uint32_t)((int64_t)(t.m_end - t.m0) * a_k * ES);
     }
     const i32x4v rs_a = rsrc(a_base, a_bytes);
     const i32x4v rs_a2 = rsrc(MODE == BWD_DX ? a_base2 : a_base, a_bytes);
@@ -283,9 +285,10 @@ grouped_gemm_nt(Params p) {
     uint32_t sa_off = kOff, sb_off = kOff;
     if (FP8) {
       const int kb = K / 32;
-      const uint8_t* sa_base = a_by_token ? p.a_tok_scale
-                                          : p.a_row_scale + (shared ? p.rows_cap_max * (p.I / 32) : 0);
-      rs_sa = rsrc(sa_base, a_by_token ? (uint32_t)T * kb : (uint32_t)((shared ? T : p.rows_cap_max) * kb));
+      const uint8_t* sa_base =
+          a_by_token ? p.a_tok_scale
+                     : p.a_row_scale + (shared ? p.rows_cap_max * (p.I / 32) : 0) + (int64_t)t.m0 * kb;
+      rs_sa = rsrc(sa_base, a_by_token ? (uint32_t)T * kb : (uint32_t)((t.m_end - t.m0) * kb));
       rs_sb = rsrc(bs_base, (uint32_t)Nd * kb);
       if (wave < 2) {
         const int src = L.row_src[64 * wave + lane];

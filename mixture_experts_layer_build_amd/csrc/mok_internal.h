@@ -68,6 +68,22 @@ struct TimedLaunch {
   hipEvent_t start, stop;
 };
 
+// Device scratch of the backward, sized for the configuration.
+struct BwdScratch {
+  uint16_t* wdT = nullptr;  // [E, I, H] transposed routed down weights
+  uint16_t* wgT = nullptr;  // [E, H, I]
+  uint16_t* wuT = nullptr;
+  uint16_t* sdT = nullptr;  // [I_s, H]
+  uint16_t* sgT = nullptr;  // [H, I_s]
+  uint16_t* suT = nullptr;
+  uint16_t* dg = nullptr;   // dG, dU, w*h: routed [rows_cap_max, I] then shared [T_max, I_s]
+  uint16_t* du = nullptr;
+  uint16_t* hw = nullptr;
+  float* dw_part = nullptr;      // [rows_cap_max + T_max, dw_parts(cfg)]
+  uint16_t* x_rows = nullptr;    // [rows_cap_max, H]
+  uint16_t* dout_rows = nullptr;
+};
+
 }  // namespace mok
 
 struct mok_workspace {
@@ -89,8 +105,7 @@ struct mok_workspace {
   uint8_t* hq = nullptr;           // E4M3 h (routed rows then shared rows)
   uint8_t* hq_scale = nullptr;     // its E8M0 scales, one per 32 along I
   // backward scratch
-  void* dgu = nullptr;             // bf16 dG, dU for routed + shared rows
-  float* dw_part = nullptr;        // fp32 partial router-weight gradients
+  mok::BwdScratch bwd;
   // timing
   bool timing = false;
   std::vector<mok::TimedLaunch> launches;
@@ -147,6 +162,9 @@ struct BwdArgs {
   int mxfp8;
 };
 hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& a, hipStream_t s);
+
+// Columns of the per-row partial router-weight gradients.
+int dw_parts(const mok_config& c);
 
 // Context layout: G, U, h each [rows_cap_max*I + T_max*I_s] bf16.
 inline size_t ctx_elems(const mok_config& c, const Layout& L) {

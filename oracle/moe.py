@@ -34,7 +34,8 @@ from . import mxfp8
 from .schedule import build_schedule
 
 __all__ = ["sigmoid", "silu", "forward", "forward_per_token", "forward_tokens",
-           "backward", "forward_mxfp8", "forward_tokens_mxfp8", "backward_mxfp8", "segment_rows"]
+           "backward", "backward_slices", "forward_mxfp8", "forward_tokens_mxfp8", "backward_mxfp8",
+           "segment_rows"]
 
 
 def sigmoid(z):
@@ -218,6 +219,102 @@ def backward(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
         res["d_s_gate"] = dg.T @ x
         res["d_s_up"] = du.T @ x
         dx += dg @ s_gate + du @ s_up
+    return res
+
+
+def backward_slices(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
+                    s_gate=None, s_up=None, s_down=None, slot_row=None, tokens=(), expert_cols=(),
+                    shared_cols=()):
+    """Slices of ``backward`` computed on their own (for sampled checks at
+    full sizes), from the same per-row formulas:
+      dx[t] and d_router_weights[t, :] for t in ``tokens``;
+      for (e, i) in ``expert_cols``: dW_g[e][i, :], dW_u[e][i, :] and
+      dW_d[e][:, i] (sums over the kept rows of expert e in any order);
+      for i in ``shared_cols``: the same slices of the shared expert's
+      gradients (rows = every token).
+    ``slot_row`` ([T*k], -1 where an assignment was not kept) comes from
+    the oracle schedule of the whole batch. Weight and activation arguments
+    may be indexable objects decoding rows lazily (``w[e]`` -> float
+    matrix, ``x[t]`` -> float row).
+
+    Pin (tests/test_oracle_moe.py): every slice equals ``backward`` on
+    random small cases with drops and invalid ids."""
+    T = top_experts.shape[0]
+    k = top_experts.shape[1]
+    E = w_gate.shape[0]
+    f = lambda a: np.asarray(a, np.float64)  # noqa: E731
+
+    def kept(t, j):
+        e = int(top_experts[t, j])
+        return (0 <= e < E) if slot_row is None else slot_row[t * k + j] >= 0
+
+    def row_terms(xt, dOt, w, Wg, Wu, Wd):
+        g = Wg @ xt
+        u = Wu @ xt
+        s = sigmoid(g)
+        h = g * s * u
+        dh_hat = Wd.T @ dOt
+        dh = w * dh_hat
+        dg = dh * u * s * (1.0 + g * (1.0 - s))
+        du = dh * g * s
+        return h, dh_hat, dg, du
+
+    res = dict(dx={}, d_router_weights={}, d_w_gate_rows={}, d_w_up_rows={}, d_w_down_cols={},
+               d_s_gate_rows={}, d_s_up_rows={}, d_s_down_cols={})
+    for t in tokens:
+        xt, dOt = f(x[t]), f(grad_out[t])
+        dx = np.zeros(xt.shape[0])
+        dwr = np.zeros(k)
+        for j in range(k):
+            if not kept(t, j):
+                continue
+            e = int(top_experts[t, j])
+            Wg, Wu, Wd = f(w_gate[e]), f(w_up[e]), f(w_down[e])
+            h, dh_hat, dg, du = row_terms(xt, dOt, float(router_weights[t, j]), Wg, Wu, Wd)
+            dwr[j] = dh_hat @ h
+            dx += Wg.T @ dg + Wu.T @ du
+        if s_gate is not None:
+            h, dh_hat, dg, du = row_terms(xt, dOt, 1.0, f(s_gate), f(s_up), f(s_down))
+            dx += f(s_gate).T @ dg + f(s_up).T @ du
+        res["dx"][t] = dx
+        res["d_router_weights"][t] = dwr
+    for (e, i) in expert_cols:
+        Wg, Wu, Wd = f(w_gate[e]), f(w_up[e]), f(w_down[e])
+        H = Wg.shape[1]
+        dWg = np.zeros(H)
+        dWu = np.zeros(H)
+        dWd = np.zeros(Wd.shape[0])
+        for t in range(T):
+            for j in range(k):
+                if int(top_experts[t, j]) != e or not kept(t, j):
+                    continue
+                xt, dOt, w = f(x[t]), f(grad_out[t]), float(router_weights[t, j])
+                g, u = Wg[i] @ xt, Wu[i] @ xt
+                s = sigmoid(g)
+                dh = w * (Wd[:, i] @ dOt)
+                dWg += dh * u * s * (1.0 + g * (1.0 - s)) * xt
+                dWu += dh * g * s * xt
+                dWd += w * (g * s * u) * dOt
+        res["d_w_gate_rows"][(e, i)] = dWg
+        res["d_w_up_rows"][(e, i)] = dWu
+        res["d_w_down_cols"][(e, i)] = dWd
+    if s_gate is not None:
+        for i in shared_cols:
+            Sg, Su, Sd = f(s_gate), f(s_up), f(s_down)
+            dWg = np.zeros(Sg.shape[1])
+            dWu = np.zeros(Sg.shape[1])
+            dWd = np.zeros(Sd.shape[0])
+            for t in range(T):
+                xt, dOt = f(x[t]), f(grad_out[t])
+                g, u = Sg[i] @ xt, Su[i] @ xt
+                s = sigmoid(g)
+                dh = Sd[:, i] @ dOt
+                dWg += dh * u * s * (1.0 + g * (1.0 - s)) * xt
+                dWu += dh * g * s * xt
+                dWd += (g * s * u) * dOt
+            res["d_s_gate_rows"][i] = dWg
+            res["d_s_up_rows"][i] = dWu
+            res["d_s_down_cols"][i] = dWd
     return res
 
 

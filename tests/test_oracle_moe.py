@@ -188,3 +188,26 @@ def test_forward_tokens_mxfp8_equals_forward_mxfp8(seed, mult):
     a = moe.forward_mxfp8(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
     b = moe.forward_tokens_mxfp8(range(T), x, top, w, Wg, Wu, Wd, Sg, Su, Sd, slot_row=s["slot_row"])
     np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("mult", [1.0, 0.4])
+def test_backward_slices_equal_backward(seed, mult):
+    x, top, w, Wg, Wu, Wd, (Sg, Su, Sd) = rand_case(200 + seed, T=11, H=7, I=5, E=3, k=2, I_s=4, id_lo=-1, id_hi=4)
+    dO = np.random.default_rng(300 + seed).standard_normal(x.shape)
+    s = build_schedule(top, 3, mult, 32)
+    full = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+    cols = [(e, i) for e in range(3) for i in range(5)]
+    sl = moe.backward_slices(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, slot_row=s["slot_row"],
+                             tokens=range(11), expert_cols=cols, shared_cols=range(4))
+    for t in range(11):
+        np.testing.assert_allclose(sl["dx"][t], full["dx"][t], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(sl["d_router_weights"][t], full["d_router_weights"][t], rtol=1e-12, atol=1e-12)
+    for (e, i) in cols:
+        np.testing.assert_allclose(sl["d_w_gate_rows"][(e, i)], full["d_w_gate"][e][i], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(sl["d_w_up_rows"][(e, i)], full["d_w_up"][e][i], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(sl["d_w_down_cols"][(e, i)], full["d_w_down"][e][:, i], rtol=1e-12, atol=1e-12)
+    for i in range(4):
+        np.testing.assert_allclose(sl["d_s_gate_rows"][i], full["d_s_gate"][i], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(sl["d_s_up_rows"][i], full["d_s_up"][i], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(sl["d_s_down_cols"][i], full["d_s_down"][:, i], rtol=1e-12, atol=1e-12)
