@@ -155,7 +155,7 @@ hipError_t transpose(const void* in, void* out, int nb, int R, int C, hipStream_
 
 int dw_parts(const mok_config& c) {
   const int Imax = c.intermediate > c.shared_intermediate ? c.intermediate : c.shared_intermediate;
-  return 2 * ((Imax + nt::BN - 1) / nt::BN);
+  return nt::kDwPartsPerNTile * ((Imax + nt::BN - 1) / nt::BN);
 }
 
 hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& a, hipStream_t s) {
@@ -185,7 +185,7 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
                                           b.x_rows, b.dout_rows, H, k);
     MOK_HIP_TRY(hipGetLastError());
   }
-  const int grid = ws->num_cus * nt::kBlocksPerCu;
+  const int grid = ws->num_cus;  // one 512-thread workgroup per compute unit
   auto sched_params = [&](nt::Params& p) {
     p.hdr = v.header;
     p.offsets = v.offsets;
@@ -220,7 +220,7 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
   }
   {
     LaunchTimer tm(ws, MOK_K_BWD_DW_REDUCE, s);
-    const int n_used = 2 * ((I + nt::BN - 1) / nt::BN);
+    const int n_used = nt::kDwPartsPerNTile * ((I + nt::BN - 1) / nt::BN);
     const int64_t n = c.max_tokens * k;
     const int rgrid = (int)std::min<int64_t>((n + 255) / 256, (int64_t)ws->num_cus * 16);
     reduce_dw<<<rgrid, 256, 0, s>>>(v.header, v.slot_row, b.dw_part, dw_parts(c), n_used, k, g->d_router_weights);

@@ -88,7 +88,7 @@ static void fill_schedule(nt::Params& p, const mok_workspace* ws, const SchedVie
 hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a, hipStream_t s) {
   const mok_config& c = ws->cfg;
   const SchedView v = sched_view(const_cast<void*>(sched), ws->layout);
-  const int grid = ws->num_cus * nt::kBlocksPerCu;
+  const int grid = ws->num_cus;  // one 512-thread workgroup per compute unit
   const size_t ce = ctx_elems(c, ws->layout);
   nt::Params p{};
   fill_schedule(p, ws, v);

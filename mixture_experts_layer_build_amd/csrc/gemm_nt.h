@@ -5,18 +5,20 @@
 // GEMMs whose contraction runs along a row (grad rows times the transposed
 // down weights, and [dG | dU] rows times the transposed gate/up weights).
 //
-// Tiling: 256 threads (4 wave64), output tile 128 rows x 256 B-rows, one K
-// step = 64 bytes of every A and B row (32 bf16 or 64 E4M3 elements).
-// Operands stream global -> LDS with 16-byte LDS-DMA loads into a 3-stage
-// ring of XOR-swizzled rows; in MXFP8 mode the E8M0 block scales follow
-// with 4-byte LDS-DMA loads (one dword per row = the scales of two K steps,
-// so the contraction length must be a multiple of 128). Each wave owns a
-// 64 x 128 block: 2 x 4 MFMA tiles of 32 x 32 (v_mfma_f32_32x32x16_bf16, or
+// Tiling: one workgroup of 512 threads (8 wave64, two per SIMD) per compute
+// unit, output tile 256 rows x 256 B-rows, one K step = one 128-byte cache
+// line of every A and B row (64 bf16 or 128 E4M3 elements). Operands stream
+// global -> LDS with 16-byte LDS-DMA loads (a wave instruction fetches 8
+// whole lines) into two 64 KiB stages of XOR-swizzled rows; in MXFP8 mode
+// the step's E8M0 block scales (one dword per row) follow with 4-byte
+// LDS-DMA loads. Wave (wm = wave / 4, wn = wave % 4) owns 128 rows x 64
+// B-rows: 4 x 2 MFMA tiles of 32 x 32 (v_mfma_f32_32x32x16_bf16, or
 // v_mfma_scale_f32_32x32x64_f8f6f4 with per-lane E8M0 scales), 128 fp32
-// accumulators per lane. Two workgroups share a compute unit (about 79 KiB
-// of LDS and at most 256 registers per lane each). Workgroup b runs on XCD
-// b % 8; tile ids are split into 8 contiguous ranges so the tiles of one
-// expert (which share its weights) run on one XCD and hit its L2.
+// accumulators per lane. A wave whose 128 rows are all past the segment's
+// end (the ragged last tile of an expert) skips its MFMAs, so its SIMD runs
+// the partner wave at full rate. Workgroup b runs on XCD b % 8; tile ids are
+// split into 8 contiguous ranges so the tiles of one expert (which share
+// its weights) run on one XCD and hit its L2.
 //
 // The MFMA takes the B (weight) fragment as its first operand, so
 // accumulator element r of lane (lr = lane % 32, lh = lane / 32) in an MFMA
@@ -31,14 +33,14 @@
 namespace mok {
 namespace nt {
 
-constexpr int BM = 128, BN = 256, NTHR = 256, NSTAGE = 3;
-constexpr int ROWB = 64;                        // bytes of one row per K step
-constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
-constexpr int SA_BYTES = BM * 4, SB_BYTES = BN * 4;  // E8M0 scale dwords of a K step (MXFP8)
-constexpr int kBlocksPerCu = 2;
+constexpr int BM = 256, BN = 256, NTHR = 512, NSTAGE = 2;
+constexpr int ROWB = 128;                                     // bytes of one row per K step
+constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;       // 32 KiB + 32 KiB
+constexpr int SA_BYTES = BM * 4, SB_BYTES = BN * 4;           // E8M0 scale dwords of a K step (MXFP8)
 constexpr int kNumXcd = 8;
 constexpr int kMaxLdsE = 256;  // schedules with more experts search the tile table in global memory
-constexpr uint32_t kOff = 0x80000000u;         // offset past every resource: loads return 0
+constexpr int kDwPartsPerNTile = 4;  // partial router-weight gradients per N tile (one per wave column)
+constexpr uint32_t kOff = 0x80000000u;  // offset past every resource: loads return 0
 
 enum Mode : int {
   GATE_UP = 0,  // A = tokens of x, B = gate | up rows, epilogue h = silu(g) * u
@@ -52,7 +54,7 @@ struct Params {
   const int32_t* hdr;
   const int32_t* offsets;
   const int32_t* kept;
-  const int32_t* tiles;    // prefix sums of 128-row tiles per expert; [E] routed total, [E+1] with shared
+  const int32_t* tiles;    // prefix sums of 256-row tiles per expert; [E] routed total, [E+1] with shared
   const int32_t* row_src;
   int E, k, H, I, Is;
   int64_t rows_cap_max;
@@ -93,7 +95,7 @@ struct alignas(16) Lds {
   uint8_t stage[NSTAGE][A_BYTES + B_BYTES];
   uint8_t scale[NSTAGE][SA_BYTES + SB_BYTES];  // used in MXFP8 mode
   int32_t tiles[kMaxLdsE + 2];
-  int32_t row_src[BM];  // per tile row: source row (token, or schedule row), -1 = none
+  int32_t row_src[BM];  // per tile row: source row (token, or tile-local row), -1 = none
   float row_w[BM];      // per tile row: router weight (1 for the shared expert)
 };
 
@@ -118,17 +120,14 @@ __device__ __forceinline__ int n_of(const Params& p, bool shared) {
 }
 
 template <int MODE, bool FP8>
-__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(kBlocksPerCu, kBlocksPerCu)))
+__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 grouped_gemm_nt(Params p) {
   __shared__ Lds L;
   constexpr int ES = FP8 ? 1 : 2;           // element size in bytes
   constexpr int KS = ROWB / ES;             // K elements per step
-  // vector-memory operations per lane per K step: 6 operand loads, plus in
-  // MXFP8 mode one B-scale load and (waves 0-1) one A-scale load
-  constexpr int NVM_LO = FP8 ? 7 : 6;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int lr = lane & 31, lh = lane >> 5;
   const int E = p.E;
 
@@ -196,6 +195,9 @@ grouped_gemm_nt(Params p) {
     const int K = k_of<MODE>(p, shared);
     const int Nd = n_of<MODE>(p, shared);  // valid output columns
     const int Iv = shared ? p.Is : p.I;
+    const int rows_here = t.m_end - t.m0;
+    // this wave's 128 rows hold valid rows (uniform across the wave)
+    const bool wave_live = wm * 128 < rows_here;
 
     // ---- row metadata, one thread per tile row ----
     if (tid < BM) {
@@ -218,7 +220,6 @@ grouped_gemm_nt(Params p) {
     __syncthreads();
 
     // ---- operand resources and per-lane DMA offsets ----
-    // A: token rows (GATE_UP, BWD_DH) or schedule rows (DOWN, BWD_DX).
     const bool a_by_token = MODE == GATE_UP || MODE == BWD_DH;
     const int a_k = MODE == BWD_DX ? Iv : K;  // row length of the A array(s)
     const uint8_t* a_base;
@@ -228,75 +229,72 @@ grouped_gemm_nt(Params p) {
       a_base = (const uint8_t*)p.a_tok;
       a_bytes = (uint32_t)((int64_t)T * K * ES);
     } else {
-      // based at the tile's first row (rows are tile-local below), so the
-      // buffer ranges stay small whatever the total row count
+      // based at the tile's first row (rows are tile-local), so the buffer
+      // ranges stay small whatever the total row count
       const int64_t off0 = (shared ? p.rows_cap_max * p.I * ES : 0) + (int64_t)t.m0 * a_k * ES;
       a_base = (const uint8_t*)p.a_row + off0;
       if (MODE == BWD_DX) a_base2 = (const uint8_t*)p.a_row2 + off0;
-      a_bytes = (uint32_t)((int64_t)(t.m_end - t.m0) * a_k * ES);
+      a_bytes = (uint32_t)((int64_t)rows_here * a_k * ES);
     }
     const i32x4v rs_a = rsrc(a_base, a_bytes);
     const i32x4v rs_a2 = rsrc(MODE == BWD_DX ? a_base2 : a_base, a_bytes);
-    // B: GATE_UP waves 0-1 load gate rows, waves 2-3 the matching up rows.
+    // B: GATE_UP waves 0-3 load the 128 gate rows, waves 4-7 the matching up rows.
     const uint8_t *b_base, *b_base2 = nullptr;
-    const uint8_t* bs_base = nullptr;
     uint32_t b_bytes;
+    const int b_k = MODE == BWD_DX ? Iv : K;
     {
-      const int b_k = MODE == BWD_DX ? Iv : K;
       const int64_t estride = (int64_t)Nd * b_k * ES;
-      const void* r0 = (MODE == GATE_UP && wave >= 2) ? p.b1 : p.b0;
-      const void* s0 = (MODE == GATE_UP && wave >= 2) ? p.sb1 : p.sb0;
+      const void* r0 = (MODE == GATE_UP && wave >= 4) ? p.b1 : p.b0;
+      const void* s0 = (MODE == GATE_UP && wave >= 4) ? p.sb1 : p.sb0;
       b_base = shared ? (const uint8_t*)s0 : (const uint8_t*)r0 + (int64_t)t.e * estride;
       if (MODE == BWD_DX) b_base2 = shared ? (const uint8_t*)p.sb1 : (const uint8_t*)p.b1 + (int64_t)t.e * estride;
       b_bytes = (uint32_t)estride;
-      if (FP8) {
-        const uint8_t* rs0 = (MODE == GATE_UP && wave >= 2) ? p.b1s : p.b0s;
-        const uint8_t* ss0 = (MODE == GATE_UP && wave >= 2) ? p.sb1s : p.sb0s;
-        bs_base = shared ? ss0 : rs0 + (int64_t)t.e * Nd * (b_k / 32);
-      }
     }
     const i32x4v rs_b = rsrc(b_base, b_bytes);
     const i32x4v rs_b2 = rsrc(MODE == BWD_DX ? b_base2 : b_base, b_bytes);
 
-    // This wave's LDS-DMA rows (one 16-byte instruction = 16 rows of 64
-    // bytes): A rows 32*wave + 16*i + lane/4 (i < 2), B rows
-    // 64*wave + 16*i + lane/4 (i < 4); lane % 4 is the physical chunk.
-    const int dr = lane >> 2, dp = lane & 3;
+    // This wave's LDS-DMA rows (one 16-byte instruction = 8 rows of 128
+    // bytes): A and B rows 32*wave + 8*i + lane/8 (i < 4); lane % 8 is the
+    // physical 16-byte chunk, which holds logical chunk (lane % 8) ^ swz.
+    const int dr = lane >> 3, dp = lane & 7;
     const uint32_t a_row_bytes = (uint32_t)a_k * ES;
-    uint32_t a_off[2];
+    uint32_t a_off[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = 32 * wave + 16 * i + dr;
+    for (int i = 0; i < 4; ++i) {
+      const int row = 32 * wave + 8 * i + dr;
       const int src = L.row_src[row];
-      a_off[i] = src >= 0 ? (uint32_t)src * a_row_bytes + 16u * (uint32_t)(dp ^ swz64(row)) : kOff;
+      a_off[i] = src >= 0 ? (uint32_t)src * a_row_bytes + 16u * (uint32_t)(dp ^ swz(row)) : kOff;
     }
-    const uint32_t b_row_bytes = (uint32_t)(MODE == BWD_DX ? Iv : K) * ES;
+    const uint32_t b_row_bytes = (uint32_t)b_k * ES;
     uint32_t b_off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int lb = 64 * wave + 16 * i + dr;
+      const int lb = 32 * wave + 8 * i + dr;
       const int n = MODE == GATE_UP ? t.nt * 128 + (lb & 127) : t.nt * BN + lb;
-      b_off[i] = n < Nd ? (uint32_t)n * b_row_bytes + 16u * (uint32_t)(dp ^ swz64(lb)) : kOff;
+      b_off[i] = n < Nd ? (uint32_t)n * b_row_bytes + 16u * (uint32_t)(dp ^ swz(lb)) : kOff;
     }
-    // MXFP8 scales: one dword per row holds the E8M0 scales of 4 blocks of
-    // 32 (two K steps). Waves 0-1 load A rows 64*wave + lane, every wave
-    // loads B rows 64*wave + lane.
-    i32x4v rs_sa = rs_a, rs_sb = rs_b;
-    uint32_t sa_off = kOff, sb_off = kOff;
+    // MXFP8 scales: one dword per row holds the E8M0 scales of the step's 4
+    // blocks of 32. Waves 0-3 load A rows 64*wave + lane, waves 4-7 load B
+    // rows 64*(wave-4) + lane (GATE_UP: waves 4-5 gate rows, 6-7 up rows).
+    i32x4v rs_s = rs_a;
+    uint32_t s_off = kOff;
     if (FP8) {
       const int kb = K / 32;
-      const uint8_t* sa_base =
-          a_by_token ? p.a_tok_scale
-                     : p.a_row_scale + (shared ? p.rows_cap_max * (p.I / 32) : 0) + (int64_t)t.m0 * kb;
-      rs_sa = rsrc(sa_base, a_by_token ? (uint32_t)T * kb : (uint32_t)((t.m_end - t.m0) * kb));
-      rs_sb = rsrc(bs_base, (uint32_t)Nd * kb);
-      if (wave < 2) {
+      if (wave < 4) {
+        const uint8_t* sa_base =
+            a_by_token ? p.a_tok_scale
+                       : p.a_row_scale + (shared ? p.rows_cap_max * (p.I / 32) : 0) + (int64_t)t.m0 * kb;
+        rs_s = rsrc(sa_base, a_by_token ? (uint32_t)T * kb : (uint32_t)(rows_here * kb));
         const int src = L.row_src[64 * wave + lane];
-        if (src >= 0) sa_off = (uint32_t)src * kb;
+        if (src >= 0) s_off = (uint32_t)src * kb;
+      } else {
+        const int lb = 64 * (wave - 4) + lane;
+        const bool up = MODE == GATE_UP && wave >= 6;
+        const uint8_t* bsb = shared ? (up ? p.sb1s : p.sb0s) : (up ? p.b1s : p.b0s) + (int64_t)t.e * Nd * kb;
+        rs_s = rsrc(bsb, (uint32_t)Nd * kb);
+        const int n = MODE == GATE_UP ? t.nt * 128 + (lb & 127) : t.nt * BN + lb;
+        s_off = n < Nd ? (uint32_t)n * kb : kOff;
       }
-      const int lb = 64 * wave + lane;
-      const int n = MODE == GATE_UP ? t.nt * 128 + (lb & 127) : t.nt * BN + lb;
-      sb_off = n < Nd ? (uint32_t)n * kb : kOff;
     }
 
     const uint32_t lds0 = lds_addr(&L.stage[0][0]);
@@ -307,229 +305,218 @@ grouped_gemm_nt(Params p) {
       const uint32_t kb = (uint32_t)(second ? k0 - Iv : k0) * ES;
       const uint32_t sbase = lds0 + (uint32_t)stage * (A_BYTES + B_BYTES);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        lds_dma16(second ? rs_a2 : rs_a, a_off[i], kb, sbase + (uint32_t)(32 * wave + 16 * i) * ROWB);
+      for (int i = 0; i < 4; ++i)
+        lds_dma16(second ? rs_a2 : rs_a, a_off[i], kb, sbase + (uint32_t)(32 * wave + 8 * i) * ROWB);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        lds_dma16(second ? rs_b2 : rs_b, b_off[i], kb, sbase + A_BYTES + (uint32_t)(64 * wave + 16 * i) * ROWB);
+        lds_dma16(second ? rs_b2 : rs_b, b_off[i], kb, sbase + A_BYTES + (uint32_t)(32 * wave + 8 * i) * ROWB);
       if (FP8) {
         const uint32_t sb = ldss0 + (uint32_t)stage * (SA_BYTES + SB_BYTES);
-        const uint32_t kbs = 4u * (uint32_t)(kstep >> 1);
-        if (wave < 2) lds_dma4(rs_sa, sa_off, kbs, sb + (uint32_t)(64 * wave) * 4u);
-        lds_dma4(rs_sb, sb_off, kbs, sb + SA_BYTES + (uint32_t)(64 * wave) * 4u);
+        lds_dma4(rs_s, s_off, (uint32_t)(k0 / 32), sb + (uint32_t)(64 * wave) * 4u);
       }
     };
 
-    f32x16 acc[2][4];
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int sw = swz64(lr);  // rows read by this lane are lr mod 32
-    auto b_row = [&](int j) {
-      return MODE == GATE_UP ? ((j < 2) ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32) : wn * 128 + j * 32;
-    };
-    auto compute = [&](int stage, int kstep) {
+    const int sw = swz(lr);  // rows read by this lane are lr mod 32
+    auto b_row = [&](int j) { return MODE == GATE_UP ? j * 128 + wn * 32 : wn * 64 + j * 32; };
+    auto compute = [&](int stage) {
       const uint8_t* As = &L.stage[stage][0];
       const uint8_t* Bs = As + A_BYTES;
       if constexpr (!FP8) {
-        bf16x8 fa[2][2], fb[2][4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int pc = ((2 * ks + lh) ^ sw) * 16;
+          bf16x8 fa[4], fb[2];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + i * 32 + lr) * ROWB + pc);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(Bs + (b_row(j) + lr) * ROWB + pc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        }
+      } else {
+        // MFMA sub-step ks covers K bytes [64 ks, 64 ks + 64): lane bytes
+        // 0-15 are chunk 4 ks + lh (block 2 ks), bytes 16-31 chunk
+        // 4 ks + 2 + lh (block 2 ks + 1); the lane's scale operand is block
+        // 2 ks + lh of its row (that byte of the row's scale dword).
+        const uint8_t* Ss = &L.scale[stage][0];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int pc = ((2 * ks + lh) ^ sw) * 16;
+          const int p0 = ((4 * ks + lh) ^ sw) * 16, p1 = ((4 * ks + 2 + lh) ^ sw) * 16;
+          i32x8 fa[4], fb[2];
+          int sa[4], sbv[2];
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-            fa[ks][i] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + i * 32 + lr) * ROWB + pc);
+          for (int i = 0; i < 4; ++i) {
+            const int row = wm * 128 + i * 32 + lr;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(As + row * ROWB + p0);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(As + row * ROWB + p1);
+            fa[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            sa[i] = Ss[row * 4 + 2 * ks + lh];
+          }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) fb[ks][j] = *reinterpret_cast<const bf16x8*>(Bs + (b_row(j) + lr) * ROWB + pc);
+          for (int j = 0; j < 2; ++j) {
+            const int row = b_row(j) + lr;
+            const i32x4 lo = *reinterpret_cast<const i32x4*>(Bs + row * ROWB + p0);
+            const i32x4 hi = *reinterpret_cast<const i32x4*>(Bs + row * ROWB + p1);
+            fb[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            sbv[j] = Ss[SA_BYTES + row * 4 + 2 * ks + lh];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, sbv[j],
+                                                                           0, sa[i]);
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][j], fa[ks][i], acc[i][j], 0, 0, 0);
-      } else {
-        // Lane bytes 0-15 are K [16*lh, 16*lh + 16) (block 0 of the step),
-        // bytes 16-31 are K [32 + 16*lh, ...) (block 1); the lane's scale
-        // operand is block lh of its row (byte 2*(kstep & 1) + lh of the
-        // row's scale dword).
-        const uint8_t* Ss = &L.scale[stage][0];
-        i32x8 fa[2], fb[4];
-        int sa[2], sb[4];
-        const int p0 = (lh ^ sw) * 16, p1 = ((2 + lh) ^ sw) * 16;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int row = wm * 64 + i * 32 + lr;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(As + row * ROWB + p0);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(As + row * ROWB + p1);
-          fa[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          sa[i] = Ss[row * 4 + 2 * (kstep & 1) + lh];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = b_row(j) + lr;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(Bs + row * ROWB + p0);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(Bs + row * ROWB + p1);
-          fb[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          sb[j] = Ss[SA_BYTES + row * 4 + 2 * (kstep & 1) + lh];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, sb[j], 0,
-                                                                         sa[i]);
       }
     };
 
-    // ---- main loop: 3-stage ring, steps kt+1 and kt+2 in flight ----
+    // ---- main loop: two stages, step kt+1 in flight while kt is consumed ----
     const int nk = K / KS;
     wait_vmcnt<0>();  // stores of the previous tile's epilogue are older than these loads
     issue(0, 0);
-    if (nk > 1) issue(1, 1);
     for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 >= nk)
-        wait_vmcnt<0>();
-      else if (FP8 && wave < 2)
-        wait_vmcnt<NVM_LO + 1>();
-      else
-        wait_vmcnt<NVM_LO>();
+      wait_vmcnt<0>();
       __syncthreads();  // every wave's loads of step kt landed; step kt-1's stage is free
-      if (kt + 2 < nk) issue((kt + 2) % NSTAGE, kt + 2);
-      compute(kt % NSTAGE, kt);
+      if (kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
+      if (wave_live) compute(kt & 1);
     }
 
     // ---- epilogue ----
     __syncthreads();  // the stages are free: stage output tiles per wave
-    const int rows_here = t.m_end - t.m0;
     if constexpr (MODE == GATE_UP) {
+      // wave columns: h columns nt*128 + wn*32 .. +32 (gate tile j = 0 and up
+      // tile j = 1 hold the same columns)
       const int64_t sh = shared ? p.rows_cap_max * p.I : 0;  // element offset of the shared rows
+      const int col0 = t.nt * 128 + wn * 32;
       if constexpr (!FP8) {
-        constexpr int SW = 64 + 8;  // staged row stride (bf16): 144 bytes
-        uint16_t* reg = reinterpret_cast<uint16_t*>(&L.stage[0][0]) + wave * 64 * SW;
+        constexpr int SW = 32 + 8;  // staged row stride (bf16): 80 bytes
+        uint16_t* reg = reinterpret_cast<uint16_t*>(&L.stage[0][0]) + wave * 128 * SW;
         uint16_t* outs[3] = {(uint16_t*)p.out + sh, p.ctx_g ? p.ctx_g + sh : nullptr, p.ctx_u ? p.ctx_u + sh : nullptr};
         const int nout = p.ctx_g ? 3 : 1;
         for (int b = 0; b < nout; ++b) {
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int jg = 0; jg < 2; ++jg)
+            for (int q = 0; q < 4; ++q) {
+              float v[4];
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                float v[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                  const float g = acc[i][jg][4 * q + c], u = acc[i][jg + 2][4 * q + c];
-                  v[c] = b == 0 ? silu_f(g) * u : (b == 1 ? g : u);
-                }
-                *reinterpret_cast<uint2*>(reg + (i * 32 + lr) * SW + jg * 32 + 8 * q + 4 * lh) =
-                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+              for (int c = 0; c < 4; ++c) {
+                const float g = acc[i][0][4 * q + c], u = acc[i][1][4 * q + c];
+                v[c] = b == 0 ? silu_f(g) * u : (b == 1 ? g : u);
               }
+              *reinterpret_cast<uint2*>(reg + (i * 32 + lr) * SW + 8 * q + 4 * lh) =
+                  make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          const int col = t.nt * 128 + wn * 64 + (lane & 7) * 8;
+          const int col = col0 + (lane & 3) * 8;
 #pragma unroll
-          for (int it = 0; it < 8; ++it) {  // 64 rows x 8 chunks of 16 bytes, 8 rows per instruction
-            const int r = it * 8 + (lane >> 3);
-            const int ml = wm * 64 + r;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(reg + r * SW + (lane & 7) * 8);
+          for (int it = 0; it < 8; ++it) {  // 128 rows x 4 chunks of 16 bytes, 16 rows per instruction
+            const int r = it * 16 + (lane >> 2);
+            const int ml = wm * 128 + r;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(reg + r * SW + (lane & 3) * 8);
             if (ml < rows_here && col < Nd) *reinterpret_cast<u32x4*>(outs[b] + (int64_t)(t.m0 + ml) * Nd + col) = v;
           }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
       } else {
         // h = silu(g) * u in fp32, quantized along I in blocks of 32: the
-        // block (one MFMA tile's columns) is split between lanes lh = 0 and
-        // 1 of the same row, so the block maximum takes one cross-lane max.
-        constexpr int SW = 64 + 16;  // staged row stride (bytes)
-        uint8_t* reg = &L.stage[0][0] + wave * 64 * SW;
+        // block is this wave's 32 columns, split between lanes lh = 0 and 1
+        // of the same row, so the block maximum takes one cross-lane max.
+        constexpr int SW = 32 + 16;  // staged row stride (bytes)
+        uint8_t* reg = &L.stage[0][0] + wave * 128 * SW;
         uint8_t* hq = (uint8_t*)p.out + sh;
         uint8_t* hs = p.out_scale + (shared ? p.rows_cap_max * (p.I / 32) : 0);
         const int nb = Nd / 32;
+        const int blk = col0 / 32;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i) {
+          float hv[16];
+          uint32_t amax = 0;
 #pragma unroll
-          for (int jg = 0; jg < 2; ++jg) {
-            float hv[16];
-            uint32_t amax = 0;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              hv[r] = silu_f(acc[i][jg][r]) * acc[i][jg + 2][r];
-              amax = max(amax, f2u(hv[r]) & 0x7FFFFFFFu);
-            }
-            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
-            const int X = mx_block_exponent(amax);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              uint32_t w = 0;
-#pragma unroll
-              for (int c = 0; c < 4; ++c) w |= e4m3_encode_scaled(hv[4 * q + c], X) << (8 * c);
-              *reinterpret_cast<uint32_t*>(reg + (i * 32 + lr) * SW + jg * 32 + 8 * q + 4 * lh) = w;
-            }
-            const int ml = wm * 64 + i * 32 + lr;
-            const int blk = (t.nt * 128 + wn * 64 + jg * 32) / 32;
-            if (lh == 0 && ml < rows_here && blk < nb) hs[(int64_t)(t.m0 + ml) * nb + blk] = (uint8_t)(X + 127);
+          for (int r = 0; r < 16; ++r) {
+            hv[r] = silu_f(acc[i][0][r]) * acc[i][1][r];
+            amax = max(amax, f2u(hv[r]) & 0x7FFFFFFFu);
           }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const int col = t.nt * 128 + wn * 64 + (lane & 3) * 16;
+          amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+          const int X = mx_block_exponent(amax);
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {  // 64 rows x 4 chunks of 16 bytes, 16 rows per instruction
-          const int r = it * 16 + (lane >> 2);
-          const int ml = wm * 64 + r;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(reg + r * SW + (lane & 3) * 16);
+          for (int q = 0; q < 4; ++q) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) w |= e4m3_encode_scaled(hv[4 * q + c], X) << (8 * c);
+            *reinterpret_cast<uint32_t*>(reg + (i * 32 + lr) * SW + 8 * q + 4 * lh) = w;
+          }
+          const int ml = wm * 128 + i * 32 + lr;
+          if (lh == 0 && ml < rows_here && blk < nb) hs[(int64_t)(t.m0 + ml) * nb + blk] = (uint8_t)(X + 127);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int col = col0 + (lane & 1) * 16;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {  // 128 rows x 2 chunks of 16 bytes, 32 rows per instruction
+          const int r = it * 32 + (lane >> 1);
+          const int ml = wm * 128 + r;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(reg + r * SW + (lane & 1) * 16);
           if (ml < rows_here && col < Nd) *reinterpret_cast<u32x4*>(hq + (int64_t)(t.m0 + ml) * Nd + col) = v;
         }
         if (p.ctx_g) {  // G and U for the backward, bf16 (direct stores)
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const int ml = wm * 64 + i * 32 + lr;
+          for (int i = 0; i < 4; ++i) {
+            const int ml = wm * 128 + i * 32 + lr;
             if (ml >= rows_here) continue;
 #pragma unroll
-            for (int jg = 0; jg < 2; ++jg)
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const int n = t.nt * 128 + wn * 64 + jg * 32 + 8 * q + 4 * lh;
-                if (n >= Nd) continue;
-                const int64_t o = sh + (int64_t)(t.m0 + ml) * Nd + n;
-                *reinterpret_cast<uint2*>(p.ctx_g + o) = make_uint2(pack_bf16x2(acc[i][jg][4 * q], acc[i][jg][4 * q + 1]),
-                                                                    pack_bf16x2(acc[i][jg][4 * q + 2], acc[i][jg][4 * q + 3]));
-                *reinterpret_cast<uint2*>(p.ctx_u + o) =
-                    make_uint2(pack_bf16x2(acc[i][jg + 2][4 * q], acc[i][jg + 2][4 * q + 1]),
-                               pack_bf16x2(acc[i][jg + 2][4 * q + 2], acc[i][jg + 2][4 * q + 3]));
-              }
+            for (int q = 0; q < 4; ++q) {
+              const int n = col0 + 8 * q + 4 * lh;
+              if (n >= Nd) continue;
+              const int64_t o = sh + (int64_t)(t.m0 + ml) * Nd + n;
+              *reinterpret_cast<uint2*>(p.ctx_g + o) = make_uint2(pack_bf16x2(acc[i][0][4 * q], acc[i][0][4 * q + 1]),
+                                                                  pack_bf16x2(acc[i][0][4 * q + 2], acc[i][0][4 * q + 3]));
+              *reinterpret_cast<uint2*>(p.ctx_u + o) = make_uint2(pack_bf16x2(acc[i][1][4 * q], acc[i][1][4 * q + 1]),
+                                                                  pack_bf16x2(acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]));
+            }
           }
         }
       }
     } else if constexpr (MODE == DOWN || MODE == BWD_DX) {
-      constexpr int SW = 128 + 8;  // 272 bytes
+      // wave tile: 128 rows x 64 columns, staged 64 rows at a time
+      constexpr int SW = 64 + 8;  // 144 bytes
       uint16_t* reg = reinterpret_cast<uint16_t*>(&L.stage[0][0]) + wave * 64 * SW;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const float w = MODE == DOWN ? L.row_w[wm * 64 + i * 32 + lr] : 1.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<uint2*>(reg + (i * 32 + lr) * SW + j * 32 + 8 * q + 4 * lh) =
-                make_uint2(pack_bf16x2(w * acc[i][j][4 * q], w * acc[i][j][4 * q + 1]),
-                           pack_bf16x2(w * acc[i][j][4 * q + 2], w * acc[i][j][4 * q + 3]));
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       uint16_t* ob = (uint16_t*)p.out + (shared ? p.rows_cap_max * p.H : 0);
-      const int col = t.nt * BN + wn * 128 + (lane & 15) * 8;
+      const int col = t.nt * BN + wn * 64 + (lane & 7) * 8;
 #pragma unroll
-      for (int it = 0; it < 16; ++it) {  // 64 rows x 16 chunks of 16 bytes, 4 rows per instruction
-        const int r = it * 4 + (lane >> 4);
-        const int ml = wm * 64 + r;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(reg + r * SW + (lane & 15) * 8);
-        if (ml < rows_here && col < Nd) *reinterpret_cast<u32x4*>(ob + (int64_t)(t.m0 + ml) * p.H + col) = v;
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * half + ii;
+          const float w = MODE == DOWN ? L.row_w[wm * 128 + i * 32 + lr] : 1.0f;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<uint2*>(reg + (ii * 32 + lr) * SW + j * 32 + 8 * q + 4 * lh) =
+                  make_uint2(pack_bf16x2(w * acc[i][j][4 * q], w * acc[i][j][4 * q + 1]),
+                             pack_bf16x2(w * acc[i][j][4 * q + 2], w * acc[i][j][4 * q + 3]));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {  // 64 rows x 8 chunks of 16 bytes, 8 rows per instruction
+          const int r = it * 8 + (lane >> 3);
+          const int ml = wm * 128 + half * 64 + r;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(reg + r * SW + (lane & 7) * 8);
+          if (ml < rows_here && col < Nd) *reinterpret_cast<u32x4*>(ob + (int64_t)(t.m0 + ml) * p.H + col) = v;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
     } else {  // BWD_DH
       // dh_hat[row, col] = acc (fp32). With the saved G, U, h of the row:
@@ -538,17 +525,17 @@ grouped_gemm_nt(Params p) {
       //   hw = w * h (the down-weight gradient's right operand).
       const int64_t sh = shared ? p.rows_cap_max * p.I : 0;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ml = wm * 64 + i * 32 + lr;
+      for (int i = 0; i < 4; ++i) {
+        const int ml = wm * 128 + i * 32 + lr;
         const bool live = ml < rows_here;
         const float w = L.row_w[ml];
         const int64_t rowo = sh + (int64_t)(t.m0 + ml) * Nd;
         float part = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int n = t.nt * BN + wn * 128 + j * 32 + 8 * q + 4 * lh;
+            const int n = t.nt * BN + wn * 64 + j * 32 + 8 * q + 4 * lh;
             if (!live || n >= Nd) continue;
             const uint2 gv = *reinterpret_cast<const uint2*>(p.g_in + rowo + n);
             const uint2 uv = *reinterpret_cast<const uint2*>(p.u_in + rowo + n);
@@ -573,11 +560,11 @@ grouped_gemm_nt(Params p) {
             *reinterpret_cast<uint2*>(p.hw_out + rowo + n) =
                 make_uint2(pack_bf16x2(hwv[0], hwv[1]), pack_bf16x2(hwv[2], hwv[3]));
           }
-        // the row's 128 columns of this wave: lanes lh = 0 and 1 hold halves
+        // the row's 64 columns of this wave: lanes lh = 0 and 1 hold halves
         part += __shfl_xor(part, 32);
         if (live && lh == 0) {
           const int64_t prow = shared ? p.rows_cap_max + t.m0 + ml : t.m0 + ml;
-          p.dw_part[prow * p.dw_parts + t.nt * 2 + wn] = part;
+          p.dw_part[prow * p.dw_parts + t.nt * kDwPartsPerNTile + wn] = part;
         }
       }
     }
