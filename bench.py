@@ -34,6 +34,27 @@ METRIC = "MoE layer tokens/s + achieved TFLOP/s vs MFMA peak, BF16 & MXFP8 fwd/b
 PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}
 HBM_GBS = 8000.0
 DEFAULT = "t8192_bf16_fwd"
+CSRC = os.path.join(ROOT, "mixture_experts_layer_build_amd", "csrc")
+# Sources that define the gate/up grouped-GEMM kernel and its launch.
+GATE_UP_SOURCES = ("gemm_nt.h", "gemm_common.h", "device_common.h", "mok_internal.h", "forward.hip")
+# HBM bytes per gate/up launch from two rocprofv3 counter passes over this
+# script (FETCH_SIZE, then WRITE_SIZE, mean over the dispatches), each scaled
+# by the factor the same counter gives for a plain copy kernel of known size
+# (--copy-calibration): read factor 2.000, write factor 1.000. Keyed by
+# (workload, sha256 of GATE_UP_SOURCES): once the kernel changes, the figure
+# no longer applies and traffic is reported as null.
+MEASURED_TRAFFIC = {
+    ("t8192_bf16_fwd", "755d62bb8a3f213f"): 997710 * 1024 * 2.000 + 119296 * 1024 * 1.000,
+}
+
+
+def gate_up_source_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for n in GATE_UP_SOURCES:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -44,8 +65,11 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(CONFIGS))
     ap.add_argument("--mult", type=float, default=None, help="override the capacity multiplier")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="0 = automatic")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="oracle chunk size; 0 = automatic")
     ap.add_argument("--all", action="store_true", help="one line per workload (diagnostics)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, run one plain device-to-device copy of MIB MiB (a "
+                         "known-size reference for the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -67,9 +91,10 @@ def kept_assignments(sched_fields) -> int:
     return int(sched_fields["kept"].sum().item())
 
 
-def cpu_baseline(c: MoEShape, inp: dict, mult: float, sample_tokens: int) -> dict:
-    """The oracle (float64 NumPy, as it stands) on the first `sample_tokens`
-    tokens of the same batch, with its own schedule for that sample."""
+def cpu_baseline(c: MoEShape, inp: dict, mult: float, chunk_tokens: int, min_seconds: float = 12.0) -> dict:
+    """The oracle (float64 NumPy, as it stands) on consecutive chunks of
+    `chunk_tokens` tokens of the same batch (each chunk with its own
+    schedule), taken in order until at least `min_seconds` of CPU work."""
     from oracle import moe as omoe
     from workloads import bf16_bits_to_f32
     try:
@@ -77,28 +102,50 @@ def cpu_baseline(c: MoEShape, inp: dict, mult: float, sample_tokens: int) -> dic
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    n = min(sample_tokens, c.T)
+    n = max(1, min(chunk_tokens, c.T))
     f = lambda a: None if a is None else bf16_bits_to_f32(a).astype(np.float64)  # noqa: E731
-    args = [f(inp["x"][:n]), inp["top_experts"][:n], inp["router_weights"][:n], f(inp["w_gate"]),
-            f(inp["w_up"]), f(inp["w_down"]), f(inp["s_gate"]), f(inp["s_up"]), f(inp["s_down"])]
+    w = [f(inp["w_gate"]), f(inp["w_up"]), f(inp["w_down"]), f(inp["s_gate"]), f(inp["s_up"]), f(inp["s_down"])]
+    done = 0
+    chunks = 0
     t0 = time.perf_counter()
-    if c.passes == "fwd":
-        if c.mode == "mxfp8":
-            omoe.forward_mxfp8(*args, capacity_multiplier=mult)
+    while True:
+        lo = (chunks * n) % c.T
+        hi = min(lo + n, c.T)
+        args = [f(inp["x"][lo:hi]), inp["top_experts"][lo:hi], inp["router_weights"][lo:hi], *w]
+        if c.passes == "fwd":
+            if c.mode == "mxfp8":
+                omoe.forward_mxfp8(*args, capacity_multiplier=mult)
+            else:
+                omoe.forward(*args, capacity_multiplier=mult)
         else:
-            omoe.forward(*args, capacity_multiplier=mult)
-    else:
-        g = f(inp["grad_out"][:n])
-        if c.mode == "mxfp8":
-            omoe.forward_mxfp8(*args, capacity_multiplier=mult)
-            omoe.backward_mxfp8(g, *args, capacity_multiplier=mult)
-        else:
-            omoe.forward(*args, capacity_multiplier=mult)
-            omoe.backward(g, *args, capacity_multiplier=mult)
+            g = f(inp["grad_out"][lo:hi])
+            if c.mode == "mxfp8":
+                omoe.forward_mxfp8(*args, capacity_multiplier=mult)
+                omoe.backward_mxfp8(g, *args, capacity_multiplier=mult)
+            else:
+                omoe.forward(*args, capacity_multiplier=mult)
+                omoe.backward(g, *args, capacity_multiplier=mult)
+        done += hi - lo
+        chunks += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} of {c.T} tokens of the same seeded batch, float64 NumPy oracle "
-                      f"({'fwd' if c.passes == 'fwd' else 'fwd+bwd'}, {c.mode}), {dt:.2f} s"}
+    return {"value": round(done / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{chunks} consecutive chunks of {n} tokens ({done} tokens) of the same seeded "
+                      f"{c.T}-token batch, each chunk scheduled on its own, float64 NumPy oracle "
+                      f"({'fwd' if c.passes == 'fwd' else 'fwd+bwd'}, {c.mode}), {dt:.1f} s"}
+
+
+def copy_calibration(mib: int) -> None:
+    """One plain elementwise copy kernel (torch.neg on float32) that reads
+    exactly mib MiB and writes exactly mib MiB, launched as a kernel (not a
+    DMA-engine copy), so that a profiler sees its byte counters."""
+    import torch
+    src = torch.ones((mib << 20) // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
 
 
 def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sample_tokens: int) -> dict:
@@ -176,13 +223,13 @@ def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sampl
                      "achieved": None if achieved is None else round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": None if achieved is None else round(achieved / peak, 4),
                      "avg_launch_ms": round(gu_avg, 5), "algorithmic_flops_per_launch": gu_flops,
-                     "traffic": None},
+                     "traffic": MEASURED_TRAFFIC.get((c.name, gate_up_source_sha()))},
         "kernels_ms_per_step": {k: round(v[0] / steps, 5) for k, v in timing.items()},
     }
     if want_cpu:
-        # about 2048 tokens' worth of the 8192-token workload's per-token work
+        # chunks of about 1024 tokens' worth of the 8192-token workload's per-token work
         per_tok = c.fwd_flops() / c.T * (3.0 if c.passes != "fwd" else 1.0)
-        n = sample_tokens or int(min(c.T, max(64, 2048 * 84.9e6 / per_tok)))
+        n = sample_tokens or int(min(c.T, max(64, 1024 * 84.9e6 / per_tok)))
         line["cpu_baseline"] = cpu_baseline(c, inp, mult, n)
     return line
 
@@ -199,6 +246,8 @@ def main():
         mult = c.capacity_multiplier if a.mult is None else a.mult
         line = run(c, a.steps, a.warmup, mult, not a.no_cpu_baseline and not a.all, a.cpu_sample_tokens)
         print(json.dumps(line), flush=True)
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
 
 
 if __name__ == "__main__":
