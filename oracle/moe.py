@@ -33,6 +33,18 @@ import numpy as np
 from . import mxfp8
 from .schedule import build_schedule
 
+
+def bf16_round(v):
+    """Values rounded as a float32 result stored in bfloat16: to float32
+    (nearest even), then to the 8-bit-significand grid (nearest even).
+    Used where the layer saves an activation in bf16 and a later MXFP8
+    quantizer decides codes from it (see ``backward_mxfp8``).
+
+    Pin (tests/test_oracle_moe.py): equals torch's float32 -> bfloat16 cast."""
+    u = np.asarray(v, np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
 __all__ = ["sigmoid", "silu", "forward", "forward_per_token", "forward_tokens",
            "backward", "backward_slices", "forward_mxfp8", "forward_tokens_mxfp8", "backward_mxfp8",
            "segment_rows"]
@@ -437,7 +449,7 @@ def _qdq_rows_in_segment(v, q, block=32):
 
 def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
                    s_gate=None, s_up=None, s_down=None, sched=None,
-                   capacity_multiplier=1.0, expert_pad=32, qfun=None):
+                   capacity_multiplier=1.0, expert_pad=32, qfun=None, saved=bf16_round):
     """MXFP8 backward: every backward GEMM operand is quantized along that
     GEMM's contraction dimension, the forward activations being the MXFP8
     forward's (g, u from quantized x and weights; h quantized along I).
@@ -451,12 +463,19 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
     Reading: the pages give the MXFP8 backward only by name; quantizing each
     operand along its own contraction dimension is the plain reading of
     "MXFP8" (blocks along K) for a GEMM whose K differs from the forward's.
+    The backward differentiates through the context the forward saved
+    ([A] ``_MoKAutogradFunction``: backward consumes the saved context), and
+    the context holds g and u in bf16; since dg and du feed MXFP8 quantizers
+    (a rounding decision), they are formed from g and u as saved:
+    ``saved`` (default ``bf16_round``) is applied to g and u before the
+    SwiGLU derivative. ``saved=None`` keeps them exact.
 
     Pin (tests/test_oracle_moe.py): with ``qfun`` the identity this must equal
     ``backward`` (checks which operand goes where); the quantizer itself is
     pinned in tests/test_oracle_mxfp8.py.
     """
     q = mxfp8.qdq if qfun is None else qfun
+    sv = (lambda a: a) if saved is None else saved
     dO = np.asarray(grad_out, np.float64)
     xq = q(np.asarray(x, np.float64), axis=1)
     xraw = np.asarray(x, np.float64)
@@ -484,6 +503,7 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
         g = A @ Wg_f[e].T
         u = A @ Wu_f[e].T
         hq = q(silu(g) * u, axis=1)
+        g, u = sv(g), sv(u)
         dOq = q(dO[t], axis=1)
         dh_un = dOq @ Wd_b[e]
         dwr[a] = np.sum(dh_un * hq, axis=1)
@@ -510,6 +530,7 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
         g = xq @ Sg_f.T
         u = xq @ Su_f.T
         hq = q(silu(g) * u, axis=1)
+        g, u = sv(g), sv(u)
         dh = q(dO, axis=1) @ Sd_b
         s = sigmoid(g)
         dg = dh * u * s * (1.0 + g * (1.0 - s))
@@ -519,4 +540,124 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
         xr = _qdq_rows_in_segment(xraw, q)
         res["d_s_gate"] = _qdq_rows_in_segment(dg, q).T @ xr
         res["d_s_up"] = _qdq_rows_in_segment(du, q).T @ xr
+    return res
+
+
+def backward_slices_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
+                          s_gate=None, s_up=None, s_down=None, slot_row=None, tokens=(), expert_cols=(),
+                          shared_cols=(), saved=bf16_round):
+    """Slices of ``backward_mxfp8`` computed on their own (for sampled checks
+    at full sizes), with the same quantization of every operand:
+      dx[t] and d_router_weights[t, :] for t in ``tokens``;
+      for (e, i) in ``expert_cols``: dW_g[e][i, :], dW_u[e][i, :] and
+      dW_d[e][:, i]; for i in ``shared_cols`` the shared expert's slices.
+    ``slot_row`` ([T*k], -1 where an assignment was not kept) is the oracle
+    schedule's; an expert's rows are its kept assignments in ascending flat
+    index, which is the row order the 32-row blocks of Q_r follow. Weight
+    and activation arguments may decode rows lazily (``w[e]``, ``x[t]``).
+
+    ``saved`` as in ``backward_mxfp8``.
+
+    Pin (tests/test_oracle_moe.py): every slice equals ``backward_mxfp8`` on
+    random small cases with drops and invalid ids."""
+    q = mxfp8.qdq
+    sv = (lambda a: a) if saved is None else saved
+    T = top_experts.shape[0]
+    k = top_experts.shape[1]
+    E = w_gate.shape[0]
+    f = lambda a: np.asarray(a, np.float64)  # noqa: E731
+    cache = {}
+
+    def expert(e):
+        # forward operands along H (gate/up) and I (down); backward operands
+        # along each backward GEMM's contraction: down along H, gate/up along I
+        if e not in cache:
+            Wg, Wu, Wd = f(w_gate[e]), f(w_up[e]), f(w_down[e])
+            cache[e] = dict(Wg_f=q(Wg, axis=1), Wu_f=q(Wu, axis=1), Wd_b=q(Wd, axis=0),
+                            Wg_b=q(Wg, axis=0), Wu_b=q(Wu, axis=0))
+        return cache[e]
+
+    if s_gate is not None:
+        Sg, Su, Sd = f(s_gate), f(s_up), f(s_down)
+        shared = dict(Wg_f=q(Sg, axis=1), Wu_f=q(Su, axis=1), Wd_b=q(Sd, axis=0), Wg_b=q(Sg, axis=0),
+                      Wu_b=q(Su, axis=0))
+
+    def kept(t, j):
+        e = int(top_experts[t, j])
+        return (0 <= e < E) if slot_row is None else slot_row[t * k + j] >= 0
+
+    def qrow(v):
+        return q(np.asarray(v, np.float64)[None, :], axis=1)[0]
+
+    res = dict(dx={}, d_router_weights={}, d_w_gate_rows={}, d_w_up_rows={}, d_w_down_cols={},
+               d_s_gate_rows={}, d_s_up_rows={}, d_s_down_cols={})
+    for t in tokens:
+        xq = qrow(x[t])
+        dOq = qrow(grad_out[t])
+        dx = np.zeros(xq.shape[0])
+        dwr = np.zeros(k)
+        terms = [(j, float(router_weights[t, j]), expert(int(top_experts[t, j]))) for j in range(k) if kept(t, j)]
+        if s_gate is not None:
+            terms.append((None, 1.0, shared))
+        for j, w, m in terms:
+            g = m["Wg_f"] @ xq
+            u = m["Wu_f"] @ xq
+            hq = qrow(silu(g) * u)
+            g, u = sv(g), sv(u)
+            dh_un = dOq @ m["Wd_b"]
+            if j is not None:
+                dwr[j] = dh_un @ hq
+            dh = w * dh_un
+            s = sigmoid(g)
+            dg = dh * u * s * (1.0 + g * (1.0 - s))
+            du = dh * g * s
+            dx += qrow(dg) @ m["Wg_b"] + qrow(du) @ m["Wu_b"]
+        res["dx"][t] = dx
+        res["d_router_weights"][t] = dwr
+
+    def column_slices(m, X, dO, w, i):
+        """dW_g[i, :], dW_u[i, :], dW_d[:, i] over one segment's rows."""
+        xq = q(X, axis=1)
+        b0 = (i // 32) * 32
+        g = xq @ m["Wg_f"][b0:b0 + 32].T
+        u = xq @ m["Wu_f"][b0:b0 + 32].T
+        hq_i = q(silu(g) * u, axis=1)[:, i - b0]
+        dOq = q(dO, axis=1)
+        dh = w * (dOq @ m["Wd_b"][:, i])
+        gi, ui = sv(g[:, i - b0]), sv(u[:, i - b0])
+        s = sigmoid(gi)
+        dg = dh * ui * s * (1.0 + gi * (1.0 - s))
+        du = dh * gi * s
+        xr = _qdq_rows_in_segment(X, q)
+        dWg = _qdq_rows_in_segment(dg[:, None], q)[:, 0] @ xr
+        dWu = _qdq_rows_in_segment(du[:, None], q)[:, 0] @ xr
+        dy = _qdq_rows_in_segment(w[:, None] * dO, q)
+        dWd = dy.T @ _qdq_rows_in_segment(hq_i[:, None], q)[:, 0]
+        return dWg, dWu, dWd
+
+    for (e, i) in expert_cols:
+        rows = [(t, j) for t in range(T) for j in range(k) if int(top_experts[t, j]) == e and kept(t, j)]
+        m = expert(e)
+        H = m["Wg_f"].shape[1]
+        if not rows:
+            res["d_w_gate_rows"][(e, i)] = np.zeros(H)
+            res["d_w_up_rows"][(e, i)] = np.zeros(H)
+            res["d_w_down_cols"][(e, i)] = np.zeros(m["Wd_b"].shape[0])
+            continue
+        X = np.stack([f(x[t]) for t, _ in rows])
+        dO = np.stack([f(grad_out[t]) for t, _ in rows])
+        w = np.array([float(router_weights[t, j]) for t, j in rows])
+        dWg, dWu, dWd = column_slices(m, X, dO, w, i)
+        res["d_w_gate_rows"][(e, i)] = dWg
+        res["d_w_up_rows"][(e, i)] = dWu
+        res["d_w_down_cols"][(e, i)] = dWd
+    if s_gate is not None and len(shared_cols):
+        X = np.stack([f(x[t]) for t in range(T)])
+        dO = np.stack([f(grad_out[t]) for t in range(T)])
+        w = np.ones(T)
+        for i in shared_cols:
+            dWg, dWu, dWd = column_slices(shared, X, dO, w, i)
+            res["d_s_gate_rows"][i] = dWg
+            res["d_s_up_rows"][i] = dWu
+            res["d_s_down_cols"][i] = dWd
     return res

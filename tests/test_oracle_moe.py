@@ -167,7 +167,7 @@ def test_mxfp8_backward_structure_with_identity_quantizer():
     s = build_schedule(top, 3, 1.0, 32)
     dO = np.random.default_rng(14).standard_normal(x.shape)
     ident = lambda v, axis=-1: np.asarray(v, np.float64)
-    a = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, qfun=ident)
+    a = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, qfun=ident, saved=None)
     b = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
     for n in b:
         np.testing.assert_allclose(a[n], b[n], rtol=1e-11, atol=1e-11, err_msg=n)
@@ -211,3 +211,63 @@ def test_backward_slices_equal_backward(seed, mult):
         np.testing.assert_allclose(sl["d_s_gate_rows"][i], full["d_s_gate"][i], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(sl["d_s_up_rows"][i], full["d_s_up"][i], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(sl["d_s_down_cols"][i], full["d_s_down"][:, i], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(2))
+@pytest.mark.parametrize("mult", [1.0, 0.4])
+def test_backward_slices_mxfp8_equal_backward_mxfp8(seed, mult):
+    # 70 tokens x top-2 over 3 experts: segments of more than one 32-row block;
+    # I = 64 puts sampled columns in both 32-column blocks of h
+    rng = np.random.default_rng(400 + seed)
+    T, H, I, E, k, Is = 70, 64, 64, 3, 2, 32
+    x = rng.standard_normal((T, H))
+    top = rng.integers(-1, E + 1, size=(T, k)).astype(np.int64)
+    w = rng.uniform(0.1, 1.0, size=(T, k))
+    Wg, Wu = rng.standard_normal((E, I, H)) * 0.3, rng.standard_normal((E, I, H)) * 0.3
+    Wd = rng.standard_normal((E, H, I)) * 0.3
+    Sg, Su, Sd = rng.standard_normal((Is, H)) * 0.3, rng.standard_normal((Is, H)) * 0.3, rng.standard_normal((H, Is)) * 0.3
+    dO = rng.standard_normal((T, H))
+    s = build_schedule(top, E, mult, 32)
+    full = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+    cols = [(e, i) for e in range(E) for i in (0, 31, 32, 63)]
+    sl = moe.backward_slices_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, slot_row=s["slot_row"],
+                                   tokens=range(T), expert_cols=cols, shared_cols=(0, 17, 31))
+    tol = dict(rtol=1e-10, atol=1e-10)
+    for t in range(T):
+        np.testing.assert_allclose(sl["dx"][t], full["dx"][t], **tol)
+        np.testing.assert_allclose(sl["d_router_weights"][t], full["d_router_weights"][t], **tol)
+    for (e, i) in cols:
+        np.testing.assert_allclose(sl["d_w_gate_rows"][(e, i)], full["d_w_gate"][e][i], **tol)
+        np.testing.assert_allclose(sl["d_w_up_rows"][(e, i)], full["d_w_up"][e][i], **tol)
+        np.testing.assert_allclose(sl["d_w_down_cols"][(e, i)], full["d_w_down"][e][:, i], **tol)
+    for i in (0, 17, 31):
+        np.testing.assert_allclose(sl["d_s_gate_rows"][i], full["d_s_gate"][i], **tol)
+        np.testing.assert_allclose(sl["d_s_up_rows"][i], full["d_s_up"][i], **tol)
+        np.testing.assert_allclose(sl["d_s_down_cols"][i], full["d_s_down"][:, i], **tol)
+
+
+def test_bf16_round_matches_torch_cast():
+    rng = np.random.default_rng(21)
+    v = np.concatenate([rng.standard_normal(100000) * 10.0 ** rng.integers(-30, 30, size=100000),
+                        [0.0, -0.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 65504.0, 1e-40]])
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    got = moe.bf16_round(v)
+    np.testing.assert_array_equal(got, ref)
+    assert np.signbit(got[v.size - 5])
+
+
+def test_mxfp8_backward_saved_context_rounding_only_touches_swiglu_derivative():
+    # with an identity quantizer, rounding the saved g, u changes the result by
+    # the bf16 rounding only (relative 2^-8), and saved=None gives backward()
+    x, top, w, Wg, Wu, Wd, (Sg, Su, Sd) = rand_case(19, T=10, H=64, I=32, E=3, k=2, I_s=32)
+    s = build_schedule(top, 3, 1.0, 32)
+    dO = np.random.default_rng(15).standard_normal(x.shape)
+    ident = lambda v, axis=-1: np.asarray(v, np.float64)
+    a = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, qfun=ident)
+    b = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+    for n in b:
+        scale = np.max(np.abs(b[n]))
+        assert np.max(np.abs(a[n] - b[n])) <= 2.0 ** -6 * scale, n
+    # d_router_weights and dW_down do not use the derivative: unchanged
+    np.testing.assert_allclose(a["d_router_weights"], b["d_router_weights"], rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(a["d_w_down"], b["d_w_down"], rtol=1e-11, atol=1e-11)
