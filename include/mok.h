@@ -232,7 +232,11 @@ mok_status mok_forward(mok_workspace* ws, mok_mode mode, const void* schedule, s
  * x bf16 [T, H]; router_weights fp32 [T, k]; `weights` are the BF16 weights
  * in both modes (scale pointers ignored): in MXFP8 mode they are quantized on
  * the device along each backward GEMM's own contraction dimension, as are
- * the activation-side operands.
+ * the activation-side operands (grad_out rows along H; dG, dU along I; the
+ * weight gradients' operands in 32-row blocks of each expert's rows), and
+ * the context must come from an MXFP8 forward of the same schedule.
+ * MXFP8 mode returns MOK_ERR_UNSUPPORTED unless H, I and I_s are multiples
+ * of 128. Uses only the workspace's scratch (no allocation).
  */
 mok_status mok_backward(mok_workspace* ws, mok_mode mode, const void* schedule, size_t schedule_bytes,
                         const void* context, size_t context_bytes, const void* grad_out, const void* x,

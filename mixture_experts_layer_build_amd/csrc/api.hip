@@ -139,6 +139,42 @@ enum ScratchPart : int {
   SP_COUNT
 };
 
+// MXFP8 GEMMs load one dword of E8M0 scales (4 blocks of 32) per row and
+// two K steps, so every contraction length must be a multiple of 128.
+bool mxfp8_shapes_ok(const mok_config& c) {
+  return c.hidden % 128 == 0 && c.intermediate % 128 == 0 && c.shared_intermediate % 128 == 0;
+}
+
+// The MXFP8 backward's buffers, placed inside the BF16 backward's regions.
+// kr_cap bounds the routed K of the weight-gradient operands (each segment
+// rounded up to 128 rows: at most rows_cap + 127 E), ks_cap the shared K.
+struct Fp8BwdPlan {
+  size_t w_c, w_s, sw_c, sw_s;     // routed / shared weight codes and scales (each of 3)
+  int64_t kr_cap, ks_cap;
+  size_t xc, xs, ic, is;           // H-column and I-column operand codes / scales (each array)
+  size_t wt, dguh, rows;           // bytes needed in the WT, DGUH and ROWS regions
+};
+
+Fp8BwdPlan fp8_bwd_plan(const mok_config& c, const Layout& L) {
+  const int64_t Tm = c.max_tokens, H = c.hidden, E = c.num_experts, I = c.intermediate, Is = c.shared_intermediate;
+  const size_t ce = ctx_elems(c, L);
+  Fp8BwdPlan f{};
+  f.w_c = align_up((size_t)E * I * H, 256);
+  f.w_s = align_up((size_t)E * I * H / 32, 256);
+  f.sw_c = align_up((size_t)Is * H, 256);
+  f.sw_s = align_up((size_t)Is * H / 32, 256);
+  f.kr_cap = (int64_t)align_up((size_t)(L.rows_cap_max + 128 * E), 128);
+  f.ks_cap = Is > 0 ? (int64_t)align_up((size_t)Tm, 128) : 0;
+  f.xc = align_up((size_t)H * (f.kr_cap + f.ks_cap), 256);
+  f.xs = align_up((size_t)H * (f.kr_cap + f.ks_cap) / 32, 256);
+  f.ic = align_up((size_t)I * f.kr_cap + (size_t)Is * f.ks_cap, 256);
+  f.is = align_up(((size_t)I * f.kr_cap + (size_t)Is * f.ks_cap) / 32, 256);
+  f.wt = 3 * (f.w_c + f.w_s) + 3 * (f.sw_c + f.sw_s);
+  f.dguh = 2 * align_up(ce * 4, 256) + align_up(ce, 256) + align_up(ce / 32, 256);
+  f.rows = 2 * (f.xc + f.xs) + 3 * (f.ic + f.is);
+  return f;
+}
+
 size_t workspace_bytes(const mok_config& c, const Layout& L, size_t* parts) {
   const int64_t Tm = c.max_tokens, H = c.hidden, E = c.num_experts, I = c.intermediate, Is = c.shared_intermediate;
   const int64_t rowsR = L.rows_cap_max;
@@ -154,6 +190,12 @@ size_t workspace_bytes(const mok_config& c, const Layout& L, size_t* parts) {
       3 * align_up(ce * 2, 256),
       (size_t)(rowsR + Tm) * dw_parts(c) * 4,
       2 * align_up((size_t)rowsR * H * 2, 256)};
+  if (mxfp8_shapes_ok(c)) {
+    const Fp8BwdPlan f = fp8_bwd_plan(c, L);
+    p[SP_WT] = std::max(p[SP_WT], f.wt);
+    p[SP_DGUH] = std::max(p[SP_DGUH], f.dguh);
+    p[SP_ROWS] = std::max(p[SP_ROWS], f.rows);
+  }
   size_t total = 0;
   for (int i = 0; i < SP_COUNT; ++i) {
     if (parts) parts[i] = align_up(p[i], 256);
@@ -309,6 +351,41 @@ extern "C" mok_status mok_workspace_create(const mok_config* c, int device, mok_
     const size_t rb = align_up((size_t)ws->layout.rows_cap_max * c->hidden * 2, 256);
     b.x_rows = (uint16_t*)p;
     b.dout_rows = (uint16_t*)(p + rb);
+    if (mxfp8_shapes_ok(*c)) {
+      const Fp8BwdPlan f = fp8_bwd_plan(*c, ws->layout);
+      uint8_t* w = (uint8_t*)b.wdT;  // start of the WT region
+      uint8_t** wc[6] = {&b.wdTq, &b.wgTq, &b.wuTq, &b.sdTq, &b.sgTq, &b.suTq};
+      uint8_t** wsc[6] = {&b.wdTs, &b.wgTs, &b.wuTs, &b.sdTs, &b.sgTs, &b.suTs};
+      for (int i = 0; i < 6; ++i) {
+        *wc[i] = w;
+        w += i < 3 ? f.w_c : f.sw_c;
+        *wsc[i] = w;
+        w += i < 3 ? f.w_s : f.sw_s;
+      }
+      // DGUH region: fp32 dG, fp32 dU, then dU's MXFP8 codes and scales
+      b.dg32 = (float*)b.dg;
+      b.du32 = (float*)((char*)b.dg + align_up(ce * 4, 256));
+      b.duq = (uint8_t*)b.dg + 2 * align_up(ce * 4, 256);
+      b.duq_scale = b.duq + align_up(ce, 256);
+      uint8_t* r = (uint8_t*)b.x_rows;  // start of the ROWS region
+      TqArrays& q = b.tq;
+      q.x = r;
+      q.xs = r + f.xc;
+      r += f.xc + f.xs;
+      q.dy = r;
+      q.dys = r + f.xc;
+      r += f.xc + f.xs;
+      q.h = r;
+      q.hs = r + f.ic;
+      r += f.ic + f.is;
+      q.dg = r;
+      q.dgs = r + f.ic;
+      r += f.ic + f.is;
+      q.du = r;
+      q.dus = r + f.ic;
+      q.kr_cap = f.kr_cap;
+      b.mxfp8_ready = true;
+    }
     p += parts[SP_ROWS];
   }
   *out = ws;
@@ -344,12 +421,6 @@ extern "C" mok_status mok_build_schedule(mok_workspace* ws, const int64_t* top_e
   DeviceGuard g(ws->device);
   if (!g.ok) return MOK_ERR_HIP;
   return launch_schedule(ws, top_experts, T, schedule, (hipStream_t)stream) == hipSuccess ? MOK_OK : MOK_ERR_HIP;
-}
-
-// MXFP8 GEMMs load one dword of E8M0 scales (4 blocks of 32) per row and
-// two K steps, so every contraction length must be a multiple of 128.
-static bool mxfp8_shapes_ok(const mok_config& c) {
-  return c.hidden % 128 == 0 && c.intermediate % 128 == 0 && c.shared_intermediate % 128 == 0;
 }
 
 static mok_status check_weights(const mok_config& c, mok_mode mode, const mok_weights* w, bool need_scales) {
@@ -407,6 +478,7 @@ extern "C" mok_status mok_backward(mok_workspace* ws, mok_mode mode, const void*
   if (context_bytes < mok_context_bytes(&ws->cfg, mode)) return MOK_ERR_BUFFER_TOO_SMALL;
   mok_status st = check_weights(ws->cfg, mode, weights, false);
   if (st != MOK_OK) return st;
+  if (mode == MOK_MODE_MXFP8 && (!mxfp8_shapes_ok(ws->cfg) || !ws->bwd.mxfp8_ready)) return MOK_ERR_UNSUPPORTED;
   const bool sh = ws->cfg.shared_intermediate > 0;
   if (!grads->dx || !grads->d_router_weights || !grads->d_routed_gate || !grads->d_routed_up ||
       !grads->d_routed_down)

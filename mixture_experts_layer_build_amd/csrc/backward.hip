@@ -158,8 +158,150 @@ int dw_parts(const mok_config& c) {
   return nt::kDwPartsPerNTile * ((Imax + nt::BN - 1) / nt::BN);
 }
 
+// MXFP8 backward: every GEMM operand quantized along that GEMM's own
+// contraction dimension (blocks of 32, E8M0 scales), fp32 accumulation.
+//   dh_hat = Q_H(grad_out rows) Q_H(W_down)            -> dG, dU (fp32), partial dw
+//   dA     = Q_I(dG) Q_I(W_gate) + Q_I(dU) Q_I(W_up)   -> dx (fixed-order sum)
+//   dW_down = Q_r(w grad_out rows)^T Q_r(h),  dW_gate = Q_r(dG)^T Q_r(x rows),  dW_up likewise
+// with Q_r in 32-row blocks of each expert's segment and h the forward's
+// MXFP8 h. dw = <dh_hat, h>.
+static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, const BwdArgs& a, hipStream_t s) {
+  const mok_config& c = ws->cfg;
+  const int E = c.num_experts, H = c.hidden, I = c.intermediate, Is = c.shared_intermediate, k = c.topk;
+  const SchedView v = sched_view(const_cast<void*>(sched), ws->layout);
+  const int64_t rcm = ws->layout.rows_cap_max;
+  const size_t ce = ctx_elems(c, ws->layout);
+  const mok_weights* w = a.w;
+  const mok_grads* g = a.g;
+  BwdScratch& b = ws->bwd;
+  const int qgrid = ws->num_cus * 4;
+  {
+    LaunchTimer tm(ws, MOK_K_BWD_TRANSPOSE, s);
+    // W_down [E,H,I] -> [E,I,H] along H; W_gate / W_up [E,I,H] -> [E,H,I] along I
+    MOK_HIP_TRY(launch_quantize_t_matrix(w->routed_down, E, H, I, b.wdTq, b.wdTs, qgrid, s));
+    MOK_HIP_TRY(launch_quantize_t_matrix(w->routed_gate, E, I, H, b.wgTq, b.wgTs, qgrid, s));
+    MOK_HIP_TRY(launch_quantize_t_matrix(w->routed_up, E, I, H, b.wuTq, b.wuTs, qgrid, s));
+    if (Is > 0) {
+      MOK_HIP_TRY(launch_quantize_t_matrix(w->shared_down, 1, H, Is, b.sdTq, b.sdTs, qgrid, s));
+      MOK_HIP_TRY(launch_quantize_t_matrix(w->shared_gate, 1, Is, H, b.sgTq, b.sgTs, qgrid, s));
+      MOK_HIP_TRY(launch_quantize_t_matrix(w->shared_up, 1, Is, H, b.suTq, b.suTs, qgrid, s));
+    }
+  }
+  {
+    LaunchTimer tm(ws, MOK_K_BWD_QUANT, s);
+    MOK_HIP_TRY(launch_quantize_rows_dev(a.grad_out, v.header, c.max_tokens, H, ws->xq, ws->xq_scale, s));
+  }
+  const int grid = ws->num_cus;
+  auto sched_params = [&](nt::Params& p, int bm) {
+    p.hdr = v.header;
+    p.offsets = v.offsets;
+    p.kept = v.kept;
+    p.tiles = v.tiles + tile_bm_index(bm) * (E + 2);
+    p.row_src = v.row_src;
+    p.E = E;
+    p.k = k;
+    p.H = H;
+    p.I = I;
+    p.Is = Is;
+    p.rows_cap_max = rcm;
+  };
+  {
+    nt::Params p{};
+    sched_params(p, nt::BM);
+    p.router_w = a.router_w;
+    p.a_tok = ws->xq;
+    p.a_tok_scale = ws->xq_scale;
+    p.b0 = b.wdTq;
+    p.b0s = b.wdTs;
+    p.sb0 = b.sdTq;
+    p.sb0s = b.sdTs;
+    p.g_in = (const uint16_t*)a.ctx_g;
+    p.u_in = (const uint16_t*)a.ctx_u;
+    p.hq_in = (const uint8_t*)a.ctx_h;
+    p.hq_scale_in = (const uint8_t*)a.ctx_h + ce;
+    p.dg_out32 = b.dg32;
+    p.du_out32 = b.du32;
+    p.dw_part = b.dw_part;
+    p.dw_parts = dw_parts(c);
+    LaunchTimer tm(ws, MOK_K_BWD_DH, s);
+    nt::grouped_gemm_nt<nt::BWD_DH, true><<<grid, nt::NTHR, 0, s>>>(p);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  {
+    LaunchTimer tm(ws, MOK_K_BWD_DW_REDUCE, s);
+    const int n_used = nt::kDwPartsPerNTile * ((I + nt::BN - 1) / nt::BN);
+    const int64_t n = c.max_tokens * k;
+    const int rgrid = (int)std::min<int64_t>((n + 255) / 256, (int64_t)ws->num_cus * 16);
+    reduce_dw<<<rgrid, 256, 0, s>>>(v.header, v.slot_row, b.dw_part, dw_parts(c), n_used, k, g->d_router_weights);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  {
+    LaunchTimer tm(ws, MOK_K_BWD_QUANT, s);
+    MOK_HIP_TRY(launch_quantize_rows_sched(b.dg32, v.header, rcm, I, Is, c.max_tokens, ws->hq, ws->hq_scale, s));
+    MOK_HIP_TRY(launch_quantize_rows_sched(b.du32, v.header, rcm, I, Is, c.max_tokens, b.duq, b.duq_scale, s));
+  }
+  {
+    nt::Params p{};
+    sched_params(p, nt::BM);
+    p.a_row = ws->hq;
+    p.a_row_scale = ws->hq_scale;
+    p.a_row2 = b.duq;
+    p.a_row2_scale = b.duq_scale;
+    p.b0 = b.wgTq;
+    p.b0s = b.wgTs;
+    p.b1 = b.wuTq;
+    p.b1s = b.wuTs;
+    p.sb0 = b.sgTq;
+    p.sb0s = b.sgTs;
+    p.sb1 = b.suTq;
+    p.sb1s = b.suTs;
+    p.out = ws->ybuf;
+    LaunchTimer tm(ws, MOK_K_BWD_DX_ROWS, s);
+    nt::grouped_gemm_nt<nt::BWD_DX, true><<<grid, nt::NTHR, 0, s>>>(p);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  {
+    LaunchTimer tm(ws, MOK_K_BWD_DX_SUM, s);
+    const int cgrid = (int)std::min<int64_t>(c.max_tokens, (int64_t)ws->num_cus * 8);
+    const uint16_t* y = (const uint16_t*)ws->ybuf;
+    gather_sum_rows<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, Is > 0 ? y + rcm * H : nullptr,
+                                          (uint16_t*)g->dx, H, k);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  {
+    LaunchTimer tm(ws, MOK_K_BWD_QUANT, s);
+    const TqArrays& q = b.tq;
+    const uint8_t* hq = (const uint8_t*)a.ctx_h;
+    MOK_HIP_TRY(launch_quantize_t_rows(0, v, a.x, nullptr, nullptr, nullptr, E, k, H, H, rcm, q.kr_cap, q.x, q.xs,
+                                       qgrid, s));
+    MOK_HIP_TRY(launch_quantize_t_rows(1, v, a.grad_out, nullptr, nullptr, a.router_w, E, k, H, H, rcm, q.kr_cap,
+                                       q.dy, q.dys, qgrid, s));
+    MOK_HIP_TRY(launch_quantize_t_rows(3, v, nullptr, hq, hq + ce, nullptr, E, k, I, Is, rcm, q.kr_cap, q.h, q.hs,
+                                       qgrid, s));
+    MOK_HIP_TRY(launch_quantize_t_rows(4, v, b.dg32, nullptr, nullptr, nullptr, E, k, I, Is, rcm, q.kr_cap, q.dg,
+                                       q.dgs, qgrid, s));
+    MOK_HIP_TRY(launch_quantize_t_rows(4, v, b.du32, nullptr, nullptr, nullptr, E, k, I, Is, rcm, q.kr_cap, q.du,
+                                       q.dus, qgrid, s));
+  }
+  {
+    nt::Params p{};
+    sched_params(p, 128);  // the 128-row tile table gives each expert's K offset and length
+    p.tq = b.tq;
+    p.d_wd = (uint16_t*)g->d_routed_down;
+    p.d_wg = (uint16_t*)g->d_routed_gate;
+    p.d_wu = (uint16_t*)g->d_routed_up;
+    p.d_sd = (uint16_t*)g->d_shared_down;
+    p.d_sg = (uint16_t*)g->d_shared_gate;
+    p.d_su = (uint16_t*)g->d_shared_up;
+    LaunchTimer tm(ws, MOK_K_BWD_DW, s);
+    nt::grouped_gemm_nt<nt::BWD_DW, true><<<grid, nt::NTHR, 0, s>>>(p);
+    MOK_HIP_TRY(hipGetLastError());
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& a, hipStream_t s) {
-  if (a.mxfp8) return hipErrorNotSupported;
+  if (a.mxfp8) return launch_backward_mxfp8(ws, sched, a, s);
   const mok_config& c = ws->cfg;
   const int E = c.num_experts, H = c.hidden, I = c.intermediate, Is = c.shared_intermediate, k = c.topk;
   const SchedView v = sched_view(const_cast<void*>(sched), ws->layout);

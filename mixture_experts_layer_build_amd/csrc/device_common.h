@@ -90,6 +90,14 @@ __host__ __device__ __forceinline__ uint32_t e4m3_encode_scaled(float v, int X) 
   return code | sign;
 }
 
+// Value of E4M3 code `code` (low 8 bits) times 2^X: a 4-bit significand
+// scaled by a power of two, so the fp32 result is exact (subnormals too).
+__host__ __device__ __forceinline__ float e4m3_decode_scaled(uint32_t code, int X) {
+  const uint32_t e = (code >> 3) & 15u, m = code & 7u;
+  const float mag = e == 0 ? __builtin_ldexpf((float)m, X - 9) : __builtin_ldexpf((float)(8u + m), (int)e - 10 + X);
+  return (code & 0x80u) ? -mag : mag;
+}
+
 typedef unsigned int u32x4 __attribute__((vector_size(16)));
 
 // Raw buffer resource over [base, base + bytes): loads at offsets at or past

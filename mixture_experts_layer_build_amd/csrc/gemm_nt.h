@@ -46,7 +46,9 @@ enum Mode : int {
   GATE_UP = 0,  // A = tokens of x, B = gate | up rows, epilogue h = silu(g) * u
   DOWN = 1,     // A = h rows, B = down rows, epilogue y = w * acc
   BWD_DH = 2,   // A = tokens of grad_out, B = rows of down^T, epilogue dG, dU, w*h, partial dw
-  BWD_DX = 3    // A = [dG | dU] rows, B = rows of [gate^T | up^T], epilogue dA rows
+  BWD_DX = 3,   // A = [dG | dU] rows, B = rows of [gate^T | up^T], epilogue dA rows
+  BWD_DW = 4    // per expert, K = its rows: dW_down = dY^T h, dW_gate = dG^T X, dW_up = dU^T X (MXFP8,
+                // operands stored transposed, [cols, K_e], quantized in 32-row blocks)
 };
 
 struct Params {
@@ -64,6 +66,7 @@ struct Params {
   const void* a_row;            // schedule-row-indexed rows: routed [rows_cap_max, K], shared after it
   const uint8_t* a_row_scale;
   const void* a_row2;           // second half of K (dU) for BWD_DX
+  const uint8_t* a_row2_scale;
   // B operand: routed [E, N, K] and shared [N, K]; b1 = up (GATE_UP) or up^T (BWD_DX)
   const void *b0, *b1, *sb0, *sb1;
   const uint8_t *b0s, *b1s, *sb0s, *sb1s;
@@ -79,9 +82,21 @@ struct Params {
   const uint16_t* h_in;
   uint16_t* dg_out;
   uint16_t* du_out;
+  float* dg_out32;              // MXFP8: dG, dU in fp32 (quantized from these afterwards)
+  float* du_out32;
   uint16_t* hw_out;
+  const uint8_t* hq_in;         // MXFP8: h codes and scales saved by the forward (instead of h_in)
+  const uint8_t* hq_scale_in;
   float* dw_part;               // [rows_cap_max + T_max, dw_parts]
   int dw_parts;
+  // BWD_DW
+  TqArrays tq;
+  uint16_t* d_wd;               // routed weight gradients [E, H, I], [E, I, H], [E, I, H]
+  uint16_t* d_wg;
+  uint16_t* d_wu;
+  uint16_t* d_sd;               // shared [H, I_s], [I_s, H], [I_s, H]
+  uint16_t* d_sg;
+  uint16_t* d_su;
 };
 
 struct Tile {
@@ -89,6 +104,9 @@ struct Tile {
   int m0;     // first row (schedule row, or token for the shared expert)
   int m_end;  // one past the last valid row
   int nt;     // N tile
+  int job;    // BWD_DW: 0 = dW_down, 1 = dW_gate, 2 = dW_up
+  int kdim;   // BWD_DW: the expert's K (rows, a multiple of 128)
+  int kofs;   // BWD_DW: the expert's K offset in the transposed arrays
 };
 
 struct alignas(16) Lds {
@@ -142,7 +160,12 @@ grouped_gemm_nt(Params p) {
   const int ntw = n_tile_width<MODE>();
   const int nt_r = (n_of<MODE>(p, false) + ntw - 1) / ntw;
   const int nt_s = p.Is > 0 ? (n_of<MODE>(p, true) + ntw - 1) / ntw : 1;
-  const int ntiles = n_routed_mt * nt_r + (n_all_mt - n_routed_mt) * nt_s;
+  // BWD_DW: per expert (the shared expert last) 3 jobs of tpj 256 x 256 tiles
+  const int hb = (p.H + BM - 1) / BM;
+  const int tpj_r = hb * ((p.I + BN - 1) / BN);
+  const int tpj_s = hb * ((p.Is + BN - 1) / BN);
+  const int ntiles = MODE == BWD_DW ? E * 3 * tpj_r + (p.Is > 0 ? 3 * tpj_s : 0)
+                                    : n_routed_mt * nt_r + (n_all_mt - n_routed_mt) * nt_s;
 
   // XCD-aware split of the tile range: workgroup b runs on XCD b % 8.
   int stop, step, first;
@@ -162,7 +185,32 @@ grouped_gemm_nt(Params p) {
   for (int id = first; id < stop; id += step) {
     // ---- decode the tile ----
     Tile t;
-    {
+    if constexpr (MODE == BWD_DW) {
+      const int n_routed = E * 3 * tpj_r;
+      const bool sh = id >= n_routed;
+      const int tpj = sh ? tpj_s : tpj_r;
+      const int rem0 = sh ? id - n_routed : id % (3 * tpj_r);
+      t.e = sh ? -1 : id / (3 * tpj_r);
+      t.job = rem0 / tpj;
+      const int tt = rem0 - t.job * tpj;
+      const int Ivt = sh ? p.Is : p.I;
+      const int nn = t.job == 0 ? (Ivt + BN - 1) / BN : hb;  // N tiles of the job
+      const int mt = tt / nn;
+      t.nt = tt - mt * nn;
+      t.m0 = mt * BM;
+      t.m_end = t.job == 0 ? p.H : Ivt;
+      const int k0t = sh ? tile_at(E) : tile_at(t.e);
+      const int k1t = sh ? tile_at(E + 1) : tile_at(t.e + 1);
+      t.kdim = 128 * (k1t - k0t);
+      t.kofs = sh ? 0 : 128 * k0t;
+      t.e = __builtin_amdgcn_readfirstlane(t.e);
+      t.job = __builtin_amdgcn_readfirstlane(t.job);
+      t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+      t.m_end = __builtin_amdgcn_readfirstlane(t.m_end);
+      t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+      t.kdim = __builtin_amdgcn_readfirstlane(t.kdim);
+      t.kofs = __builtin_amdgcn_readfirstlane(t.kofs);
+    } else {
       const int n_routed = n_routed_mt * nt_r;
       if (id < n_routed) {
         const int mt = id / nt_r;
@@ -192,9 +240,9 @@ grouped_gemm_nt(Params p) {
       t.nt = __builtin_amdgcn_readfirstlane(t.nt);
     }
     const bool shared = t.e < 0;
-    const int K = k_of<MODE>(p, shared);
-    const int Nd = n_of<MODE>(p, shared);  // valid output columns
     const int Iv = shared ? p.Is : p.I;
+    const int K = MODE == BWD_DW ? t.kdim : k_of<MODE>(p, shared);
+    const int Nd = MODE == BWD_DW ? (t.job == 0 ? Iv : p.H) : n_of<MODE>(p, shared);  // valid output columns
     const int rows_here = t.m_end - t.m0;
     // this wave's 128 rows hold valid rows (uniform across the wave)
     const bool wave_live = wm * 128 < rows_here;
@@ -205,7 +253,9 @@ grouped_gemm_nt(Params p) {
       int src = -1;
       float w = 0.f;
       if (r < t.m_end) {
-        if (shared) {
+        if (MODE == BWD_DW) {
+          src = tid;  // tile-local row of the transposed operand
+        } else if (shared) {
           src = (MODE == GATE_UP || MODE == BWD_DH) ? r : tid;
           w = 1.f;
         } else {
@@ -225,7 +275,24 @@ grouped_gemm_nt(Params p) {
     const uint8_t* a_base;
     const uint8_t* a_base2 = nullptr;
     uint32_t a_bytes;
-    if (a_by_token) {
+    // BWD_DW: the job's transposed arrays (A = [M, K_e], B = [N, K_e]) and
+    // the routed column count that places the shared expert's blocks
+    const uint8_t *dw_a = nullptr, *dw_as = nullptr, *dw_b = nullptr, *dw_bs = nullptr;
+    int64_t dw_a_blk = 0, dw_as_blk = 0, dw_b_blk = 0, dw_bs_blk = 0;
+    if constexpr (MODE == BWD_DW) {
+      const int Mc = t.m_end;  // M columns of the job's A array
+      const int colsA_r = t.job == 0 ? p.H : p.I, colsB_r = t.job == 0 ? p.I : p.H;
+      dw_a = t.job == 0 ? p.tq.dy : t.job == 1 ? p.tq.dg : p.tq.du;
+      dw_as = t.job == 0 ? p.tq.dys : t.job == 1 ? p.tq.dgs : p.tq.dus;
+      dw_b = t.job == 0 ? p.tq.h : p.tq.x;
+      dw_bs = t.job == 0 ? p.tq.hs : p.tq.xs;
+      dw_a_blk = shared ? p.tq.kr_cap * colsA_r : (int64_t)t.kofs * Mc;
+      dw_as_blk = shared ? p.tq.kr_cap / 32 * colsA_r : (int64_t)(t.kofs / 32) * Mc;
+      dw_b_blk = shared ? p.tq.kr_cap * colsB_r : (int64_t)t.kofs * Nd;
+      dw_bs_blk = shared ? p.tq.kr_cap / 32 * colsB_r : (int64_t)(t.kofs / 32) * Nd;
+      a_base = dw_a + dw_a_blk + (int64_t)t.m0 * K;
+      a_bytes = (uint32_t)((int64_t)rows_here * K);
+    } else if (a_by_token) {
       a_base = (const uint8_t*)p.a_tok;
       a_bytes = (uint32_t)((int64_t)T * K * ES);
     } else {
@@ -242,7 +309,10 @@ grouped_gemm_nt(Params p) {
     const uint8_t *b_base, *b_base2 = nullptr;
     uint32_t b_bytes;
     const int b_k = MODE == BWD_DX ? Iv : K;
-    {
+    if constexpr (MODE == BWD_DW) {
+      b_base = dw_b + dw_b_blk;
+      b_bytes = (uint32_t)((int64_t)Nd * K);
+    } else {
       const int64_t estride = (int64_t)Nd * b_k * ES;
       const void* r0 = (MODE == GATE_UP && wave >= 4) ? p.b1 : p.b0;
       const void* s0 = (MODE == GATE_UP && wave >= 4) ? p.sb1 : p.sb0;
@@ -276,22 +346,43 @@ grouped_gemm_nt(Params p) {
     // MXFP8 scales: one dword per row holds the E8M0 scales of the step's 4
     // blocks of 32. Waves 0-3 load A rows 64*wave + lane, waves 4-7 load B
     // rows 64*(wave-4) + lane (GATE_UP: waves 4-5 gate rows, 6-7 up rows).
-    i32x4v rs_s = rs_a;
+    // BWD_DX: the dG / gate^T scales serve the first half of K, the dU / up^T
+    // scales (rs_s2) the second; each has Iv / 32 scale bytes per row.
+    i32x4v rs_s = rs_a, rs_s2 = rs_a;
     uint32_t s_off = kOff;
     if (FP8) {
-      const int kb = K / 32;
+      const int kb = (MODE == BWD_DX ? Iv : K) / 32;
       if (wave < 4) {
-        const uint8_t* sa_base =
-            a_by_token ? p.a_tok_scale
-                       : p.a_row_scale + (shared ? p.rows_cap_max * (p.I / 32) : 0) + (int64_t)t.m0 * kb;
-        rs_s = rsrc(sa_base, a_by_token ? (uint32_t)T * kb : (uint32_t)(rows_here * kb));
+        const uint8_t* sa_base;
+        const uint8_t* sa_base2 = nullptr;
+        uint32_t sa_bytes = (uint32_t)(rows_here * kb);
+        if (MODE == BWD_DW) {
+          sa_base = dw_as + dw_as_blk + (int64_t)t.m0 * kb;
+        } else if (a_by_token) {
+          sa_base = p.a_tok_scale;
+          sa_bytes = (uint32_t)T * kb;
+        } else {
+          const int64_t so = (shared ? p.rows_cap_max * (p.I / 32) : 0) + (int64_t)t.m0 * kb;
+          sa_base = p.a_row_scale + so;
+          if (MODE == BWD_DX) sa_base2 = p.a_row2_scale + so;
+        }
+        rs_s = rsrc(sa_base, sa_bytes);
+        rs_s2 = rsrc(MODE == BWD_DX ? sa_base2 : sa_base, sa_bytes);
         const int src = L.row_src[64 * wave + lane];
         if (src >= 0) s_off = (uint32_t)src * kb;
       } else {
         const int lb = 64 * (wave - 4) + lane;
         const bool up = MODE == GATE_UP && wave >= 6;
-        const uint8_t* bsb = shared ? (up ? p.sb1s : p.sb0s) : (up ? p.b1s : p.b0s) + (int64_t)t.e * Nd * kb;
+        const uint8_t* bsb;
+        const uint8_t* bsb2 = nullptr;
+        if (MODE == BWD_DW) {
+          bsb = dw_bs + dw_bs_blk;
+        } else {
+          bsb = shared ? (up ? p.sb1s : p.sb0s) : (up ? p.b1s : p.b0s) + (int64_t)t.e * Nd * kb;
+          if (MODE == BWD_DX) bsb2 = shared ? p.sb1s : p.b1s + (int64_t)t.e * Nd * kb;
+        }
         rs_s = rsrc(bsb, (uint32_t)Nd * kb);
+        rs_s2 = rsrc(MODE == BWD_DX ? bsb2 : bsb, (uint32_t)Nd * kb);
         const int n = MODE == GATE_UP ? t.nt * 128 + (lb & 127) : t.nt * BN + lb;
         s_off = n < Nd ? (uint32_t)n * kb : kOff;
       }
@@ -312,7 +403,7 @@ grouped_gemm_nt(Params p) {
         lds_dma16(second ? rs_b2 : rs_b, b_off[i], kb, sbase + A_BYTES + (uint32_t)(32 * wave + 8 * i) * ROWB);
       if (FP8) {
         const uint32_t sb = ldss0 + (uint32_t)stage * (SA_BYTES + SB_BYTES);
-        lds_dma4(rs_s, s_off, (uint32_t)(k0 / 32), sb + (uint32_t)(64 * wave) * 4u);
+        lds_dma4(second ? rs_s2 : rs_s, s_off, (uint32_t)((second ? k0 - Iv : k0) / 32), sb + (uint32_t)(64 * wave) * 4u);
       }
     };
 
@@ -385,7 +476,7 @@ grouped_gemm_nt(Params p) {
     // ---- main loop: two stages, step kt+1 in flight while kt is consumed ----
     const int nk = K / KS;
     wait_vmcnt<0>();  // stores of the previous tile's epilogue are older than these loads
-    issue(0, 0);
+    if (nk > 0) issue(0, 0);
     for (int kt = 0; kt < nk; ++kt) {
       wait_vmcnt<0>();
       __syncthreads();  // every wave's loads of step kt landed; step kt-1's stage is free
@@ -488,11 +579,21 @@ grouped_gemm_nt(Params p) {
           }
         }
       }
-    } else if constexpr (MODE == DOWN || MODE == BWD_DX) {
+    } else if constexpr (MODE == DOWN || MODE == BWD_DX || MODE == BWD_DW) {
       // wave tile: 128 rows x 64 columns, staged 64 rows at a time
       constexpr int SW = 64 + 8;  // 144 bytes
       uint16_t* reg = reinterpret_cast<uint16_t*>(&L.stage[0][0]) + wave * 64 * SW;
-      uint16_t* ob = (uint16_t*)p.out + (shared ? p.rows_cap_max * p.H : 0);
+      uint16_t* ob;
+      int64_t ldo = p.H;  // output row stride (elements)
+      if constexpr (MODE == BWD_DW) {
+        // the job's weight gradient: dW_down [H, Iv], dW_gate / dW_up [Iv, H]
+        ldo = Nd;
+        const int64_t eo = (int64_t)t.e * p.H * p.I;
+        ob = t.job == 0 ? (shared ? p.d_sd : p.d_wd + eo) : t.job == 1 ? (shared ? p.d_sg : p.d_wg + eo)
+                                                                      : (shared ? p.d_su : p.d_wu + eo);
+      } else {
+        ob = (uint16_t*)p.out + (shared ? p.rows_cap_max * p.H : 0);
+      }
       const int col = t.nt * BN + wn * 64 + (lane & 7) * 8;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -514,7 +615,7 @@ grouped_gemm_nt(Params p) {
           const int r = it * 8 + (lane >> 3);
           const int ml = wm * 128 + half * 64 + r;
           const u32x4 v = *reinterpret_cast<const u32x4*>(reg + r * SW + (lane & 7) * 8);
-          if (ml < rows_here && col < Nd) *reinterpret_cast<u32x4*>(ob + (int64_t)(t.m0 + ml) * p.H + col) = v;
+          if (ml < rows_here && col < Nd) *reinterpret_cast<u32x4*>(ob + (int64_t)(t.m0 + ml) * ldo + col) = v;
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
@@ -522,7 +623,10 @@ grouped_gemm_nt(Params p) {
       // dh_hat[row, col] = acc (fp32). With the saved G, U, h of the row:
       //   dw partial += dh_hat * h,   dh = w * dh_hat,
       //   dG = dh * u * s * (1 + g * (1 - s)) (s = sigmoid(g)),  dU = dh * silu(g),
-      //   hw = w * h (the down-weight gradient's right operand).
+      //   hw = w * h (the down-weight gradient's right operand; BF16 only).
+      // MXFP8: h is the forward's E4M3 h (codes and block scales); dG and dU
+      // are stored in fp32, so their two quantizations (along I for dA, along
+      // rows for the weight gradients) start from the accumulator values.
       const int64_t sh = shared ? p.rows_cap_max * p.I : 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -539,14 +643,27 @@ grouped_gemm_nt(Params p) {
             if (!live || n >= Nd) continue;
             const uint2 gv = *reinterpret_cast<const uint2*>(p.g_in + rowo + n);
             const uint2 uv = *reinterpret_cast<const uint2*>(p.u_in + rowo + n);
-            const uint2 hv = *reinterpret_cast<const uint2*>(p.h_in + rowo + n);
-            const uint32_t gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y}, hw2[2] = {hv.x, hv.y};
+            const uint32_t gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
+            uint32_t hw2[2] = {0, 0};
+            uint32_t hcodes = 0;
+            int hX = 0;
+            if constexpr (FP8) {
+              // the forward's MXFP8 h: 4 codes and the scale of their block of 32
+              hcodes = *reinterpret_cast<const uint32_t*>(p.hq_in + rowo + n);
+              const int64_t srow = (shared ? p.rows_cap_max * (p.I / 32) : 0) + (int64_t)(t.m0 + ml) * (Nd / 32);
+              hX = (int)p.hq_scale_in[srow + n / 32] - 127;
+            } else {
+              const uint2 hv = *reinterpret_cast<const uint2*>(p.h_in + rowo + n);
+              hw2[0] = hv.x;
+              hw2[1] = hv.y;
+            }
             float dg[4], du[4], hwv[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               const float g = (c & 1) ? u2f(gw[c >> 1] & 0xFFFF0000u) : u2f(gw[c >> 1] << 16);
               const float u = (c & 1) ? u2f(uw[c >> 1] & 0xFFFF0000u) : u2f(uw[c >> 1] << 16);
-              const float h = (c & 1) ? u2f(hw2[c >> 1] & 0xFFFF0000u) : u2f(hw2[c >> 1] << 16);
+              const float h = FP8 ? e4m3_decode_scaled(hcodes >> (8 * c), hX)
+                                  : ((c & 1) ? u2f(hw2[c >> 1] & 0xFFFF0000u) : u2f(hw2[c >> 1] << 16));
               const float d = acc[i][j][4 * q + c];
               part += d * h;
               const float dh = w * d;
@@ -555,10 +672,16 @@ grouped_gemm_nt(Params p) {
               du[c] = dh * g * s;
               hwv[c] = w * h;
             }
-            *reinterpret_cast<uint2*>(p.dg_out + rowo + n) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-            *reinterpret_cast<uint2*>(p.du_out + rowo + n) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-            *reinterpret_cast<uint2*>(p.hw_out + rowo + n) =
-                make_uint2(pack_bf16x2(hwv[0], hwv[1]), pack_bf16x2(hwv[2], hwv[3]));
+            if constexpr (FP8) {
+              *reinterpret_cast<float4*>(p.dg_out32 + rowo + n) = make_float4(dg[0], dg[1], dg[2], dg[3]);
+              *reinterpret_cast<float4*>(p.du_out32 + rowo + n) = make_float4(du[0], du[1], du[2], du[3]);
+            } else {
+              *reinterpret_cast<uint2*>(p.dg_out + rowo + n) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+              *reinterpret_cast<uint2*>(p.du_out + rowo + n) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+            }
+            if constexpr (!FP8)
+              *reinterpret_cast<uint2*>(p.hw_out + rowo + n) =
+                  make_uint2(pack_bf16x2(hwv[0], hwv[1]), pack_bf16x2(hwv[2], hwv[3]));
           }
         // the row's 64 columns of this wave: lanes lh = 0 and 1 hold halves
         part += __shfl_xor(part, 32);

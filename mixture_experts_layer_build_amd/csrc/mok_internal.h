@@ -68,7 +68,29 @@ struct TimedLaunch {
   hipEvent_t start, stop;
 };
 
-// Device scratch of the backward, sized for the configuration.
+// Transposed, row-block-quantized operands of the MXFP8 weight-gradient
+// GEMMs. Expert e's block of an array with `cols` columns starts at code
+// element kofs_e * cols (kofs_e = 128 * the expert's first 128-row tile) and
+// is [cols, K_e] with K_e = 128 * its 128-row tile count; its scales start
+// at kofs_e / 32 * cols and are [cols, K_e / 32]. The shared expert's block
+// sits at K offset kr_cap (a static bound on the routed total).
+struct TqArrays {
+  uint8_t* x;       // cols H: x rows of the expert (shared: all tokens)
+  uint8_t* dy;      // cols H: w * grad_out rows
+  uint8_t* h;       // cols I (shared: I_s): h rows (dequantized forward codes)
+  uint8_t* dg;      // cols I: dG rows
+  uint8_t* du;      // cols I: dU rows
+  uint8_t* xs;      // scales of each
+  uint8_t* dys;
+  uint8_t* hs;
+  uint8_t* dgs;
+  uint8_t* dus;
+  int64_t kr_cap;   // K offset of the shared expert's blocks (multiple of 128)
+};
+
+// Device scratch of the backward, sized for the configuration. The MXFP8
+// backward's buffers are carved from the same regions as the BF16 ones
+// (a backward runs in one mode at a time).
 struct BwdScratch {
   uint16_t* wdT = nullptr;  // [E, I, H] transposed routed down weights
   uint16_t* wgT = nullptr;  // [E, H, I]
@@ -82,6 +104,18 @@ struct BwdScratch {
   float* dw_part = nullptr;      // [rows_cap_max + T_max, dw_parts(cfg)]
   uint16_t* x_rows = nullptr;    // [rows_cap_max, H]
   uint16_t* dout_rows = nullptr;
+  // MXFP8: transposed weights quantized along their new rows (codes, scales)
+  uint8_t *wdTq = nullptr, *wgTq = nullptr, *wuTq = nullptr, *sdTq = nullptr, *sgTq = nullptr, *suTq = nullptr;
+  uint8_t *wdTs = nullptr, *wgTs = nullptr, *wuTs = nullptr, *sdTs = nullptr, *sgTs = nullptr, *suTs = nullptr;
+  // MXFP8: dG, dU in fp32 (routed rows then shared rows, as dg / du)
+  float* dg32 = nullptr;
+  float* du32 = nullptr;
+  // MXFP8: dU quantized along I (dG uses the workspace's hq buffer)
+  uint8_t* duq = nullptr;
+  uint8_t* duq_scale = nullptr;
+  // MXFP8: operands of the weight-gradient GEMMs
+  TqArrays tq{};
+  bool mxfp8_ready = false;  // the configuration admits the MXFP8 backward and its buffers exist
 };
 
 }  // namespace mok
@@ -144,6 +178,23 @@ struct FwdArgs {
   int mxfp8;
 };
 hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a, hipStream_t s);
+
+// Transposed MXFP8 quantization of bf16 matrices [B][R][C] -> [B][C][R]
+// codes with [B][C][R/32] scales (R % 128 == 0, C % 64 == 0).
+hipError_t launch_quantize_t_matrix(const void* src, int64_t batches, int64_t R, int64_t C, uint8_t* dst,
+                                    uint8_t* dst_scale, int grid_cap, hipStream_t s);
+// The weight-gradient GEMM operands (TqArrays layout) from one source:
+// src_kind 0 = x token rows, 1 = router weight times grad_out token rows,
+// 2 = schedule-row bf16 rows, 3 = schedule-row MXFP8 rows (h), 4 =
+// schedule-row fp32 rows (dG, dU).
+hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* src, const uint8_t* src_codes,
+                                  const uint8_t* src_scale, const float* router_w, int E, int k, int cols_r, int cols_s,
+                                  int64_t rows_cap_max, int64_t kr_cap, uint8_t* dst, uint8_t* dst_scale, int grid,
+                                  hipStream_t s);
+// dG / dU rows (fp32) quantized along I: routed rows [0, offsets[E]) and
+// shared rows [rows_cap_max, rows_cap_max + T).
+hipError_t launch_quantize_rows_sched(const void* src, const int32_t* hdr, int64_t rows_cap_max, int I, int Is,
+                                      int64_t max_tokens, uint8_t* dst, uint8_t* dst_scale, hipStream_t s);
 
 // Axis-1 MXFP8 quantization of a bf16 [T, cols] tensor whose row count T is
 // read on the device from a schedule header; the grid covers max_rows.

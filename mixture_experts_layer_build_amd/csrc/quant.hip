@@ -10,6 +10,8 @@
 // HBM-bound streaming kernels: 16-byte loads per lane, consecutive lanes on
 // consecutive 16-byte chunks, the block maximum reduced across the lanes that
 // share a block with cross-lane shuffles.
+#include <algorithm>
+
 #include "device_common.h"
 #include "mok_internal.h"
 
@@ -182,7 +184,286 @@ __global__ void __launch_bounds__(256) quant_axis0(const T* __restrict__ src, in
     *reinterpret_cast<uint32_t*>(s) = sc[0];
 }
 
+// ---- transposed quantization (blocks of 32 along the source's rows) ----
+//
+// A workgroup of 256 threads takes a tile of 128 source rows x 64 columns:
+// each thread loads 32 consecutive values of one row into LDS (fp32), then
+// thread (column c = tid / 4, block b = tid % 4) reduces rows 32b .. 32b+31
+// of column c and writes their 32 codes as one contiguous run of the output
+// row c (4 threads fill one 128-byte line) plus the block's scale byte.
+
+constexpr int kTqRows = 128, kTqCols = 64, kTqLd = kTqCols + 1;
+
+__device__ __forceinline__ void tq_store(const float (*tile)[kTqLd], uint8_t* out_row, uint8_t* scale_row) {
+  const int c = threadIdx.x >> 2, b = threadIdx.x & 3;
+  float v[32];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] = tile[32 * b + i][c];
+    amax = max(amax, f2u(v[i]) & 0x7FFFFFFFu);
+  }
+  const int X = mx_block_exponent(amax);
+  uint32_t w[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    w[q] = e4m3_encode_scaled(v[4 * q], X) | (e4m3_encode_scaled(v[4 * q + 1], X) << 8) |
+           (e4m3_encode_scaled(v[4 * q + 2], X) << 16) | (e4m3_encode_scaled(v[4 * q + 3], X) << 24);
+  // out_row / scale_row: the output row of this thread's column c, at the tile's first block
+  *reinterpret_cast<uint4*>(out_row + 32 * b) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(out_row + 32 * b + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  scale_row[b] = (uint8_t)(X + 127);
+}
+
+__device__ __forceinline__ void bf16x32_to_tile(float (*tile)[kTqLd], int r, int half, const uint16_t* src, float mul) {
+  // src: 32 consecutive bf16 values (64 bytes, 16-byte aligned), or nullptr for a zero row
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint4 raw = src ? *reinterpret_cast<const uint4*>(src + 8 * q) : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[r][32 * half + 8 * q + 2 * j] = mul * u2f(w[j] << 16);
+      tile[r][32 * half + 8 * q + 2 * j + 1] = mul * u2f(w[j] & 0xFFFF0000u);
+    }
+  }
+}
+
+// Weights: src [B][R][C] bf16 -> dst codes [B][C][R], scales [B][C][R/32]
+// (R % 128 == 0, C % 64 == 0).
+__global__ void __launch_bounds__(256) quant_t_matrix(const uint16_t* __restrict__ src, int64_t B, int64_t R, int64_t C,
+                                                      uint8_t* __restrict__ dst, uint8_t* __restrict__ dst_scale) {
+  __shared__ float tile[kTqRows][kTqLd];
+  const int64_t nkb = R / kTqRows, ncc = C / kTqCols;
+  const int64_t units = B * nkb * ncc;
+  const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int64_t b = u / (nkb * ncc);
+    const int64_t rem = u - b * nkb * ncc;
+    const int64_t kb = rem / ncc, cc = rem - kb * ncc;
+    const uint16_t* s = src + b * R * C + (kb * kTqRows + r) * C + cc * kTqCols + 32 * half;
+    bf16x32_to_tile(tile, r, half, s, 1.0f);
+    __syncthreads();
+    const int64_t c = cc * kTqCols + (threadIdx.x >> 2);
+    tq_store(tile, dst + b * C * R + c * R + kb * kTqRows, dst_scale + b * C * (R / 32) + c * (R / 32) + kb * 4);
+    __syncthreads();
+  }
+}
+
+enum TqSrc : int {
+  TQ_X = 0,     // x rows of the segment's tokens (bf16)
+  TQ_DY = 1,    // router weight times grad_out rows (bf16 source, fp32 product)
+  TQ_ROWS = 2,  // schedule-row-indexed bf16 rows (dG, dU)
+  TQ_MX = 3,    // schedule-row-indexed MXFP8 rows (the forward's h codes and scales)
+  TQ_ROWS32 = 4 // schedule-row-indexed fp32 rows (dG, dU of the MXFP8 backward)
+};
+
+struct TqParams {
+  const int32_t* hdr;
+  const int32_t* offsets;
+  const int32_t* kept;
+  const int32_t* tiles128;  // prefix sums of 128-row tiles per expert, [E] routed, [E+1] with shared
+  const int32_t* row_src;
+  const float* router_w;
+  int E, k, cols_r, cols_s;
+  int64_t rows_cap_max, kr_cap;
+  const uint16_t* src;       // TQ_X / TQ_DY: token rows [T, cols]; TQ_ROWS: routed rows then shared rows
+  const float* src32;        // TQ_ROWS32: routed rows then shared rows
+  const uint8_t* src_codes;  // TQ_MX
+  const uint8_t* src_scale;
+  uint8_t* dst;
+  uint8_t* dst_scale;
+};
+
+// The weight-gradient GEMMs' operands: for expert e, rows of its segment in
+// 128-row blocks (rows past kept[e] are zero) -> [cols, K_e] codes at
+// 128 * tiles128[e] * cols_r, quantized along the rows; the shared expert's
+// all-token segment -> [cols_s, K_s] at kr_cap * cols_r.
+template <int SRC>
+__global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
+  __shared__ float tile[kTqRows][kTqLd];
+  const int E = p.E;
+  const int T = p.hdr[HDR_T];
+  const int nkb = p.tiles128[E + 1];
+  const int ncc = (max(p.cols_r, p.cols_s) + kTqCols - 1) / kTqCols;
+  const int64_t units = (int64_t)nkb * ncc;
+  const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int kb = (int)(u / ncc), cc = (int)(u - (int64_t)kb * ncc);
+    const bool shared = kb >= p.tiles128[E];
+    int e = E;
+    if (!shared) {
+      int lo = 0, hi = E;  // largest e with tiles128[e] <= kb
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.tiles128[mid] <= kb) lo = mid; else hi = mid;
+      }
+      e = lo;
+    }
+    const int cols = shared ? p.cols_s : p.cols_r;
+    if (cc * kTqCols >= cols) continue;  // uniform across the workgroup
+    const int kl = kb - p.tiles128[e];    // block index inside the segment
+    const int lr = kl * kTqRows + r;      // row inside the segment
+    const int c0 = cc * kTqCols + 32 * half;
+    if constexpr (SRC == TQ_ROWS32) {
+      const float* s = nullptr;
+      if (shared) {
+        if (lr < T) s = p.src32 + p.rows_cap_max * p.cols_r + (int64_t)lr * cols + c0;
+      } else if (lr < p.kept[e]) {
+        s = p.src32 + (p.offsets[e] + (int64_t)lr) * cols + c0;
+      }
+      float* trow = &tile[r][32 * half];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = s ? *reinterpret_cast<const float4*>(s + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+        trow[4 * q] = v.x;
+        trow[4 * q + 1] = v.y;
+        trow[4 * q + 2] = v.z;
+        trow[4 * q + 3] = v.w;
+      }
+    } else if constexpr (SRC == TQ_MX) {
+      int64_t ro = -1;
+      if (shared) {
+        if (lr < T) ro = lr;
+      } else if (lr < p.kept[e]) {
+        ro = p.offsets[e] + lr;
+      }
+      float* trow = &tile[r][32 * half];
+      if (ro >= 0) {
+        const int64_t code0 = shared ? p.rows_cap_max * p.cols_r + ro * cols : ro * cols;
+        const int64_t sc0 = shared ? p.rows_cap_max * (p.cols_r / 32) + ro * (cols / 32) : ro * (cols / 32);
+        const int X = (int)p.src_scale[sc0 + c0 / 32] - 127;
+        const uint4 q0 = *reinterpret_cast<const uint4*>(p.src_codes + code0 + c0);
+        const uint4 q1 = *reinterpret_cast<const uint4*>(p.src_codes + code0 + c0 + 16);
+        const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) trow[i] = e4m3_decode_scaled(w[i >> 2] >> (8 * (i & 3)), X);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) trow[i] = 0.f;
+      }
+    } else {
+      const uint16_t* s = nullptr;
+      float mul = 1.0f;
+      if (shared) {
+        if (lr < T) s = SRC == TQ_ROWS ? p.src + p.rows_cap_max * p.cols_r + (int64_t)lr * cols + c0
+                                       : p.src + (int64_t)lr * cols + c0;
+      } else if (lr < p.kept[e]) {
+        const int64_t row = p.offsets[e] + lr;
+        if (SRC == TQ_ROWS) {
+          s = p.src + row * cols + c0;
+        } else {
+          const int a = p.row_src[row];
+          s = p.src + (int64_t)(a / p.k) * cols + c0;
+          if (SRC == TQ_DY) mul = p.router_w[a];
+        }
+      }
+      bf16x32_to_tile(tile, r, half, s, mul);
+    }
+    __syncthreads();
+    const int64_t Kp = 128 * (int64_t)(shared ? nkb - p.tiles128[E] : p.tiles128[e + 1] - p.tiles128[e]);
+    const int64_t kofs = shared ? 0 : 128 * (int64_t)p.tiles128[e];
+    const int64_t base = shared ? p.kr_cap * p.cols_r : kofs * cols;
+    const int64_t sbase = shared ? p.kr_cap / 32 * p.cols_r : kofs / 32 * cols;
+    const int64_t c = cc * kTqCols + (threadIdx.x >> 2);
+    tq_store(tile, p.dst + base + c * Kp + (int64_t)kl * kTqRows, p.dst_scale + sbase + c * (Kp / 32) + kl * 4);
+    __syncthreads();
+  }
+}
+
+// dG / dU rows (fp32) along their I columns: the routed rows [0, offsets[E])
+// of width I and the shared rows [rows_cap_max, rows_cap_max + T) of width
+// I_s, laid out as the forward's h codes (scales [rows, cols / 32]).
+__global__ void __launch_bounds__(256) quant_rows_sched_f32(const float* __restrict__ src, const int32_t* __restrict__ hdr,
+                                                            int64_t rcm, int I, int Is, uint8_t* __restrict__ dst,
+                                                            uint8_t* __restrict__ scale) {
+  // 8 lanes per 32-element block, 4 fp32 elements per lane
+  const int64_t nb_r = rcm * (I / 32);
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = g >> 3;
+  const int part = (int)(g & 7);
+  bool live;
+  int64_t eoff, soff;
+  if (b < nb_r) {
+    const int64_t row = b / (I / 32), blk = b - row * (I / 32);
+    live = row < hdr[HDR_ROWS_TOTAL];
+    eoff = row * I + blk * 32;
+    soff = row * (I / 32) + blk;
+  } else {
+    const int64_t bs = b - nb_r;
+    const int64_t row = Is > 0 ? bs / (Is / 32) : 0, blk = Is > 0 ? bs - row * (Is / 32) : 0;
+    live = Is > 0 && row < hdr[HDR_T];
+    eoff = rcm * I + row * Is + blk * 32;
+    soff = rcm * (I / 32) + row * (Is / 32) + blk;
+  }
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (live) v = *reinterpret_cast<const float4*>(src + eoff + part * 4);
+  uint32_t amax = max(max(f2u(v.x) & 0x7FFFFFFFu, f2u(v.y) & 0x7FFFFFFFu),
+                      max(f2u(v.z) & 0x7FFFFFFFu, f2u(v.w) & 0x7FFFFFFFu));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 4));
+  if (!live) return;
+  const int X = mx_block_exponent(amax);
+  const uint32_t c = e4m3_encode_scaled(v.x, X) | (e4m3_encode_scaled(v.y, X) << 8) |
+                     (e4m3_encode_scaled(v.z, X) << 16) | (e4m3_encode_scaled(v.w, X) << 24);
+  *reinterpret_cast<uint32_t*>(dst + eoff + part * 4) = c;
+  if (part == 0) scale[soff] = (uint8_t)(X + 127);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_t_matrix(const void* src, int64_t batches, int64_t R, int64_t C, uint8_t* dst,
+                                    uint8_t* dst_scale, int grid_cap, hipStream_t s) {
+  const int64_t units = batches * (R / kTqRows) * (C / kTqCols);
+  if (units == 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>(units, grid_cap);
+  quant_t_matrix<<<grid, 256, 0, s>>>((const uint16_t*)src, batches, R, C, dst, dst_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* src, const uint8_t* src_codes,
+                                  const uint8_t* src_scale, const float* router_w, int E, int k, int cols_r, int cols_s,
+                                  int64_t rows_cap_max, int64_t kr_cap, uint8_t* dst, uint8_t* dst_scale, int grid,
+                                  hipStream_t s) {
+  TqParams p{};
+  p.hdr = v.header;
+  p.offsets = v.offsets;
+  p.kept = v.kept;
+  p.tiles128 = v.tiles + tile_bm_index(128) * (E + 2);
+  p.row_src = v.row_src;
+  p.router_w = router_w;
+  p.E = E;
+  p.k = k;
+  p.cols_r = cols_r;
+  p.cols_s = cols_s;
+  p.rows_cap_max = rows_cap_max;
+  p.kr_cap = kr_cap;
+  p.src = (const uint16_t*)src;
+  p.src32 = (const float*)src;
+  p.src_codes = src_codes;
+  p.src_scale = src_scale;
+  p.dst = dst;
+  p.dst_scale = dst_scale;
+  switch (src_kind) {
+    case TQ_X: quant_t_rows<TQ_X><<<grid, 256, 0, s>>>(p); break;
+    case TQ_DY: quant_t_rows<TQ_DY><<<grid, 256, 0, s>>>(p); break;
+    case TQ_ROWS: quant_t_rows<TQ_ROWS><<<grid, 256, 0, s>>>(p); break;
+    case TQ_ROWS32: quant_t_rows<TQ_ROWS32><<<grid, 256, 0, s>>>(p); break;
+    default: quant_t_rows<TQ_MX><<<grid, 256, 0, s>>>(p); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows_sched(const void* src, const int32_t* hdr, int64_t rows_cap_max, int I, int Is,
+                                      int64_t max_tokens, uint8_t* dst, uint8_t* dst_scale, hipStream_t s) {
+  const int64_t blocks = rows_cap_max * (I / 32) + (Is > 0 ? max_tokens * (Is / 32) : 0);
+  const int64_t grid = (blocks * 8 + 255) / 256;
+  if (grid == 0) return hipSuccess;
+  quant_rows_sched_f32<<<dim3((unsigned)grid), dim3(256), 0, s>>>((const float*)src, hdr, rows_cap_max, I, Is, dst,
+                                                                   dst_scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_rows_dev(const void* src, const int32_t* hdr, int64_t max_rows, int64_t cols, uint8_t* dst,
                                     uint8_t* dst_scale, hipStream_t s) {

@@ -1,0 +1,163 @@
+"""GPU parity of mok_backward in MXFP8 mode against the oracle's MXFP8
+backward (every GEMM operand quantized along that GEMM's contraction
+dimension; the weight-gradient GEMMs' operands in 32-row blocks of each
+expert's segment): every gradient within max|err| <= 6e-2 * max|ref| of its
+tensor. The forward runs in MXFP8 with pre-quantized weights and keeps its
+context; the backward takes the BF16 weights and quantizes them on the
+device.
+
+Small cases are compared over whole tensors (ragged segments of several
+32-row blocks, drops and invalid ids, no shared expert, experts that get no
+rows). The 8192-token workload runs at full size with slices computed one by
+one by the oracle: dx and router-weight gradients of sampled tokens, rows of
+dW_gate / dW_up and columns of dW_down of sampled (expert, i) pairs, and the
+shared expert's slices."""
+import numpy as np
+import pytest
+
+from mokutil import TOL_MXFP8, Bf16Array, assert_close_inf, f64, to_dev
+
+from oracle import moe as omoe
+from oracle.schedule import build_schedule as oracle_schedule
+from workloads import CONFIGS, MoEShape, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import mixture_experts_layer_build_amd as mok  # noqa: E402
+from mixture_experts_layer_build_amd._lib import MOK_ERR_UNSUPPORTED  # noqa: E402
+
+
+def quantize_weights(wdev: dict) -> dict:
+    q = {}
+    for name, t in wdev.items():
+        codes, sc = mok.mxfp8_quantize(t.reshape(-1, t.shape[-1]), axis=1)
+        q[name] = codes.view(t.shape)
+        q[name + "_scale"] = sc
+    return q
+
+
+def gpu_fwd_bwd_mxfp8(c: MoEShape, inp: dict, mult: float):
+    d = to_dev(inp)
+    cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=c.T,
+                        shared_intermediate=c.I_s, capacity_multiplier=mult)
+    ws = mok.Workspace(cfg)
+    mode = mok.MOK_MODE_MXFP8
+    sched = mok.build_schedule(ws, d["top_experts"])
+    ctx = torch.empty(mok.context_bytes(cfg, mode), dtype=torch.uint8, device="cuda")
+    out = mok.forward(ws, sched, d["x"], d["router_weights"], quantize_weights(d["weights"]), mode=mode,
+                      context=ctx)
+    g = mok.backward(ws, sched, ctx, d["grad_out"], d["x"], d["router_weights"], d["weights"], mode=mode)
+    torch.cuda.synchronize()
+    return out, g, (ws, sched, ctx, d)
+
+
+def np64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+SMALL = [
+    ("ragged", 300, 256, 256, 5, 3, 128, 1.0, False),
+    ("drops_invalid", 300, 256, 128, 5, 3, 128, 0.3, True),
+    ("no_shared", 200, 384, 256, 3, 2, 0, 1.0, False),
+    ("many_experts", 513, 128, 128, 40, 4, 128, 1.0, True),
+    ("deep", 130, 1024, 256, 4, 2, 512, 0.6, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[s[0] for s in SMALL])
+def test_backward_mxfp8_small(case):
+    name, T, H, I, E, k, Is, mult, invalid = case
+    c = MoEShape(name, T=T, H=H, I=I, E=E, k=k, I_s=Is, seed=81, w_std=0.05, mode="mxfp8", passes="fwd+bwd")
+    inp = make_inputs(c)
+    if invalid:
+        top = inp["top_experts"].copy()
+        top[::7, 0] = -1
+        top[3::11, -1] = E + 3
+        inp["top_experts"] = top
+    print(f"mxfp8 backward small {name}", flush=True)
+    _, g, _ = gpu_fwd_bwd_mxfp8(c, inp, mult)
+    ref = omoe.backward_mxfp8(f64(inp["grad_out"]), f64(inp["x"]), inp["top_experts"], inp["router_weights"],
+                              f64(inp["w_gate"]), f64(inp["w_up"]), f64(inp["w_down"]), f64(inp["s_gate"]),
+                              f64(inp["s_up"]), f64(inp["s_down"]), capacity_multiplier=mult)
+    pairs = [("dx", "dx"), ("d_router_weights", "d_router_weights"), ("d_routed_gate", "d_w_gate"),
+             ("d_routed_up", "d_w_up"), ("d_routed_down", "d_w_down")]
+    if Is:
+        pairs += [("d_shared_gate", "d_s_gate"), ("d_shared_up", "d_s_up"), ("d_shared_down", "d_s_down")]
+    for gname, rname in pairs:
+        err, scale = assert_close_inf(np64(g[gname]), ref[rname], TOL_MXFP8, f"{name}:{gname}")
+        print(f"  {gname}: max err {err:.3g} of max {scale:.3g}")
+    sched = oracle_schedule(inp["top_experts"], E, mult, 32)
+    not_kept = sched["slot_row"].reshape(T, k) < 0
+    assert np.all(np64(g["d_router_weights"])[not_kept] == 0.0)
+    # experts with no kept rows get exactly zero weight gradients
+    for e in np.flatnonzero(sched["kept"] == 0):
+        for gname in ("d_routed_gate", "d_routed_up", "d_routed_down"):
+            assert not torch.any(g[gname][int(e)] != 0), (gname, int(e))
+
+
+def test_backward_mxfp8_deterministic():
+    c = MoEShape("det", T=400, H=256, I=256, E=6, k=3, I_s=128, seed=13, w_std=0.05, mode="mxfp8",
+                 passes="fwd+bwd")
+    inp = make_inputs(c)
+    _, g1, (ws, sched, ctx, d) = gpu_fwd_bwd_mxfp8(c, inp, 1.0)
+    g1 = {k_: v.clone() for k_, v in g1.items()}
+    g2 = mok.backward(ws, sched, ctx, d["grad_out"], d["x"], d["router_weights"], d["weights"],
+                      mode=mok.MOK_MODE_MXFP8)
+    torch.cuda.synchronize()
+    for k_ in g1:
+        assert torch.equal(g1[k_].view(torch.uint8), g2[k_].view(torch.uint8)), k_
+
+
+def test_backward_mxfp8_rejects_unsupported_shapes():
+    # I = 64 is a valid BF16 shape but not an MXFP8 one (contractions must be multiples of 128)
+    cfg = mok.MoKConfig(hidden=128, intermediate=64, num_experts=4, topk=2, max_tokens=64,
+                        shared_intermediate=0)
+    ws = mok.Workspace(cfg)
+    c = MoEShape("bad", T=64, H=128, I=64, E=4, k=2, I_s=0, seed=3, passes="fwd+bwd")
+    d = to_dev(make_inputs(c))
+    sched = mok.build_schedule(ws, d["top_experts"])
+    ctx = torch.zeros(mok.context_bytes(cfg, mok.MOK_MODE_MXFP8), dtype=torch.uint8, device="cuda")
+    with pytest.raises(mok.MokError) as ei:
+        mok.backward(ws, sched, ctx, d["grad_out"], d["x"], d["router_weights"], d["weights"],
+                     mode=mok.MOK_MODE_MXFP8)
+    assert ei.value.status == MOK_ERR_UNSUPPORTED
+
+
+def test_backward_mxfp8_8192_tokens_sampled():
+    c = CONFIGS["t8192_mxfp8_fwdbwd"]
+    inp = make_inputs(c)
+    print("generated 8192-token inputs", flush=True)
+    _, g, _ = gpu_fwd_bwd_mxfp8(c, inp, c.capacity_multiplier)
+    print("gpu forward+backward done", flush=True)
+    sched = oracle_schedule(inp["top_experts"], c.E, c.capacity_multiplier, c.expert_pad)
+    rng = np.random.default_rng(5)
+    toks = sorted(set([0, c.T - 1] + list(rng.integers(0, c.T, size=4))))
+    cols = [(0, 0), (37, int(rng.integers(0, c.I))), (c.E - 1, c.I - 1)]
+    scols = [0, int(rng.integers(0, c.I_s))]
+    sl = omoe.backward_slices_mxfp8(Bf16Array(inp["grad_out"]), Bf16Array(inp["x"]), inp["top_experts"],
+                                    inp["router_weights"], Bf16Array(inp["w_gate"]), Bf16Array(inp["w_up"]),
+                                    Bf16Array(inp["w_down"]), f64(inp["s_gate"]), f64(inp["s_up"]),
+                                    f64(inp["s_down"]), slot_row=sched["slot_row"], tokens=toks, expert_cols=cols,
+                                    shared_cols=scols)
+    print("oracle slices done", flush=True)
+    def check(got, ref, name):
+        err, scale = assert_close_inf(got, ref, TOL_MXFP8, name)
+        print(f"  {name}: max err {err:.3g} of max {scale:.3g}", flush=True)
+
+    check(np64(g["dx"][toks]), np.stack([sl["dx"][t] for t in toks]), "dx")
+    check(np64(g["d_router_weights"][toks]), np.stack([sl["d_router_weights"][t] for t in toks]), "d_router_weights")
+    wg, wu, wd = g["d_routed_gate"], g["d_routed_up"], g["d_routed_down"]
+    check(np.stack([np64(wg[e, i]) for e, i in cols]), np.stack([sl["d_w_gate_rows"][p] for p in cols]),
+          "dW_gate rows")
+    check(np.stack([np64(wu[e, i]) for e, i in cols]), np.stack([sl["d_w_up_rows"][p] for p in cols]), "dW_up rows")
+    check(np.stack([np64(wd[e, :, i]) for e, i in cols]), np.stack([sl["d_w_down_cols"][p] for p in cols]),
+          "dW_down cols")
+    check(np.stack([np64(g["d_shared_gate"][i]) for i in scols]), np.stack([sl["d_s_gate_rows"][i] for i in scols]),
+          "dS_gate rows")
+    check(np.stack([np64(g["d_shared_up"][i]) for i in scols]), np.stack([sl["d_s_up_rows"][i] for i in scols]),
+          "dS_up rows")
+    check(np.stack([np64(g["d_shared_down"][:, i]) for i in scols]),
+          np.stack([sl["d_s_down_cols"][i] for i in scols]), "dS_down cols")
+    for k_, v in g.items():
+        assert torch.isfinite(v.float()).all(), k_
