@@ -26,6 +26,8 @@
 // runs of 4 consecutive columns of one row.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "gemm_common.h"
 #include "mok_internal.h"
@@ -113,6 +115,9 @@ struct alignas(16) Lds {
   uint8_t stage[NSTAGE][A_BYTES + B_BYTES];
   uint8_t scale[NSTAGE][SA_BYTES + SB_BYTES];  // used in MXFP8 mode
   int32_t tiles[kMaxLdsE + 2];
+  int32_t fullp[kMaxLdsE + 2];  // exclusive prefix over experts (shared last) of full M tiles
+  int32_t tailp[kMaxLdsE + 2];  // ... and of tail M tiles (a segment's last tile with <= 128 rows)
+  int32_t wsum[2][NTHR / 64];   // per-wave partial sums of the two scans
   int32_t row_src[BM];  // per tile row: source row (token, or tile-local row), -1 = none
   float row_w[BM];      // per tile row: router weight (1 for the shared expert)
 };
@@ -167,25 +172,111 @@ grouped_gemm_nt(Params p) {
   const int ntiles = MODE == BWD_DW ? E * 3 * tpj_r + (p.Is > 0 ? 3 * tpj_s : 0)
                                     : n_routed_mt * nt_r + (n_all_mt - n_routed_mt) * nt_s;
 
-  // XCD-aware split of the tile range: workgroup b runs on XCD b % 8.
-  int stop, step, first;
-  if ((gridDim.x % kNumXcd) == 0) {
-    const int xcd = blockIdx.x % kNumXcd, slots = gridDim.x / kNumXcd;
-    const int chunk = (ntiles + kNumXcd - 1) / kNumXcd;
-    const int start = xcd * chunk;
-    stop = min(ntiles, start + chunk);
-    step = slots;
-    first = start + (int)(blockIdx.x / kNumXcd);
+  // ---- work lists ----
+  // Workgroup b runs on XCD b % 8 and works through that XCD's list of
+  // tiles, taking positions slot, slot + slots, ... (slot = b / 8), so the
+  // tiles of one expert, which share its weights, run together on one XCD and
+  // hit its L2. The modes whose A rows are gathered tokens (gate/up and the
+  // backward's grad_out GEMM) order each list longest first: the XCD's share
+  // of the full M tiles (more than 128 valid rows), then its share of the
+  // tail tiles (a segment's last M tile, at most 128 rows, whose MFMAs the
+  // idle wave half skips), which then fill the last round. The other modes
+  // keep the natural order (an expert's tiles together, its tail tile right
+  // after its full ones), which reads each expert's weights once.
+  const int nq = (gridDim.x % kNumXcd) == 0 ? kNumXcd : 1;
+  const int xq = blockIdx.x % nq;
+  const int slot = blockIdx.x / nq, slots = gridDim.x / nq;
+  const bool lpt = (MODE == GATE_UP || MODE == BWD_DH) && lds_tiles;
+  int TFr = 0, TF = 0, TTr = 0, TT = 0, f0 = 0, nf = 0, u0 = 0, qlen = 0, id0 = 0;
+  if (lpt) {
+    // counts of full and tail M tiles per expert (index E = shared expert),
+    // exclusive scans across the workgroup (waves scan with shuffles)
+    int cf = 0, ct = 0;
+    if (tid <= E) {
+      const int nm = L.tiles[tid + 1] - L.tiles[tid];
+      const int rows = tid < E ? p.kept[tid] : (p.Is > 0 ? T : 0);
+      const int tail = (nm > 0 && rows - BM * (nm - 1) <= BM / 2) ? 1 : 0;
+      cf = nm - tail;
+      ct = tail;
+    }
+    int sf = cf, st = ct;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int af = __shfl_up(sf, d), at = __shfl_up(st, d);
+      if (lane >= d) {
+        sf += af;
+        st += at;
+      }
+    }
+    if (lane == 63) {
+      L.wsum[0][wave] = sf;
+      L.wsum[1][wave] = st;
+    }
+    __syncthreads();
+    int bf = 0, bt = 0;
+    for (int w = 0; w < wave; ++w) {
+      bf += L.wsum[0][w];
+      bt += L.wsum[1][w];
+    }
+    if (tid <= E + 1) {
+      L.fullp[tid] = bf + sf - cf;  // exclusive
+      L.tailp[tid] = bt + st - ct;
+    }
+    __syncthreads();
+    TFr = L.fullp[E] * nt_r;
+    TF = TFr + (L.fullp[E + 1] - L.fullp[E]) * nt_s;
+    TTr = L.tailp[E] * nt_r;
+    TT = TTr + (L.tailp[E + 1] - L.tailp[E]) * nt_s;
+    const int cfq = (TF + nq - 1) / nq, ctq = (TT + nq - 1) / nq;
+    f0 = min(TF, xq * cfq);
+    nf = min(TF, f0 + cfq) - f0;
+    u0 = min(TT, xq * ctq);
+    qlen = nf + min(TT, u0 + ctq) - u0;
   } else {
-    stop = ntiles;
-    step = gridDim.x;
-    first = blockIdx.x;
+    const int chunk = (ntiles + nq - 1) / nq;
+    id0 = min(ntiles, xq * chunk);
+    qlen = min(ntiles, id0 + chunk) - id0;
   }
+  auto search = [&](const int32_t* pre, int v) {  // largest e in [0, E) with pre[e] <= v
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] <= v)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    return lo;
+  };
 
-  for (int id = first; id < stop; id += step) {
+  for (int q = slot; q < qlen; q += slots) {
     // ---- decode the tile ----
     Tile t;
-    if constexpr (MODE == BWD_DW) {
+    const int id = id0 + q;  // natural-order id (BWD_DW, or more experts than the LDS tables hold)
+    if (lpt) {
+      const bool full = q < nf;
+      const int v = full ? f0 + q : u0 + (q - nf);
+      const int vr = full ? TFr : TTr;
+      if (v < vr) {
+        const int mi = v / nt_r;
+        t.nt = v - mi * nt_r;
+        const int e = __builtin_amdgcn_readfirstlane(search(full ? L.fullp : L.tailp, mi));
+        t.e = e;
+        const int base = p.offsets[e];
+        const int mt = full ? mi - L.fullp[e] : L.tiles[e + 1] - L.tiles[e] - 1;
+        t.m0 = base + mt * BM;
+        t.m_end = base + p.kept[e];
+      } else {
+        const int mi = (v - vr) / nt_s;
+        t.nt = (v - vr) - mi * nt_s;
+        t.e = -1;
+        t.m0 = (full ? mi : L.tiles[E + 1] - L.tiles[E] - 1) * BM;
+        t.m_end = T;
+      }
+      t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+      t.m_end = __builtin_amdgcn_readfirstlane(t.m_end);
+      t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+    } else if constexpr (MODE == BWD_DW) {
       const int n_routed = E * 3 * tpj_r;
       const bool sh = id >= n_routed;
       const int tpj = sh ? tpj_s : tpj_r;
@@ -494,9 +585,9 @@ grouped_gemm_nt(Params p) {
       if constexpr (!FP8) {
         constexpr int SW = 32 + 8;  // staged row stride (bf16): 80 bytes
         uint16_t* reg = reinterpret_cast<uint16_t*>(&L.stage[0][0]) + wave * 128 * SW;
-        uint16_t* outs[3] = {(uint16_t*)p.out + sh, p.ctx_g ? p.ctx_g + sh : nullptr, p.ctx_u ? p.ctx_u + sh : nullptr};
-        const int nout = p.ctx_g ? 3 : 1;
-        for (int b = 0; b < nout; ++b) {
+        // output sel: 0 = h, 1 = G, 2 = U (G and U only when a context is kept)
+        auto store_out = [&](uint16_t* ob, auto sel_c) {
+          constexpr int SEL = decltype(sel_c)::value;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -505,7 +596,7 @@ grouped_gemm_nt(Params p) {
 #pragma unroll
               for (int c = 0; c < 4; ++c) {
                 const float g = acc[i][0][4 * q + c], u = acc[i][1][4 * q + c];
-                v[c] = b == 0 ? silu_f(g) * u : (b == 1 ? g : u);
+                v[c] = SEL == 0 ? silu_f(g) * u : (SEL == 1 ? g : u);
               }
               *reinterpret_cast<uint2*>(reg + (i * 32 + lr) * SW + 8 * q + 4 * lh) =
                   make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -517,9 +608,14 @@ grouped_gemm_nt(Params p) {
             const int r = it * 16 + (lane >> 2);
             const int ml = wm * 128 + r;
             const u32x4 v = *reinterpret_cast<const u32x4*>(reg + r * SW + (lane & 3) * 8);
-            if (ml < rows_here && col < Nd) *reinterpret_cast<u32x4*>(outs[b] + (int64_t)(t.m0 + ml) * Nd + col) = v;
+            if (ml < rows_here && col < Nd) *reinterpret_cast<u32x4*>(ob + (int64_t)(t.m0 + ml) * Nd + col) = v;
           }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        };
+        store_out((uint16_t*)p.out + sh, std::integral_constant<int, 0>{});
+        if (p.ctx_g) {
+          store_out(p.ctx_g + sh, std::integral_constant<int, 1>{});
+          store_out(p.ctx_u + sh, std::integral_constant<int, 2>{});
         }
       } else {
         // h = silu(g) * u in fp32, quantized along I in blocks of 32: the
