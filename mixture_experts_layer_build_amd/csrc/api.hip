@@ -135,7 +135,7 @@ enum ScratchPart : int {
   SP_WT,         // transposed weights for the backward (routed + shared)
   SP_DGUH,       // dG, dU, w*h (3 x context-sized)
   SP_DWP,        // partial router-weight gradients
-  SP_ROWS,       // x and grad_out rows in schedule order
+  SP_ROWS,       // transposed operands of the weight-gradient GEMMs
   SP_COUNT
 };
 
@@ -175,6 +175,24 @@ Fp8BwdPlan fp8_bwd_plan(const mok_config& c, const Layout& L) {
   return f;
 }
 
+// bf16 operands of the BF16 weight-gradient GEMMs (the TqArrays layout
+// without scales), in the ROWS region.
+struct Bf16DwPlan {
+  int64_t kr_cap, ks_cap;
+  size_t xc, ic, rows;
+};
+
+Bf16DwPlan bf16_dw_plan(const mok_config& c, const Layout& L) {
+  const int64_t Tm = c.max_tokens, H = c.hidden, E = c.num_experts, I = c.intermediate, Is = c.shared_intermediate;
+  Bf16DwPlan f{};
+  f.kr_cap = (int64_t)align_up((size_t)(L.rows_cap_max + 128 * E), 128);
+  f.ks_cap = Is > 0 ? (int64_t)align_up((size_t)Tm, 128) : 0;
+  f.xc = align_up((size_t)H * (f.kr_cap + f.ks_cap) * 2, 256);
+  f.ic = align_up(((size_t)I * f.kr_cap + (size_t)Is * f.ks_cap) * 2, 256);
+  f.rows = 2 * f.xc + 3 * f.ic;
+  return f;
+}
+
 size_t workspace_bytes(const mok_config& c, const Layout& L, size_t* parts) {
   const int64_t Tm = c.max_tokens, H = c.hidden, E = c.num_experts, I = c.intermediate, Is = c.shared_intermediate;
   const int64_t rowsR = L.rows_cap_max;
@@ -189,7 +207,7 @@ size_t workspace_bytes(const mok_config& c, const Layout& L, size_t* parts) {
       3 * align_up((size_t)E * I * H * 2, 256) + 3 * align_up((size_t)Is * H * 2, 256),
       3 * align_up(ce * 2, 256),
       (size_t)(rowsR + Tm) * dw_parts(c) * 4,
-      2 * align_up((size_t)rowsR * H * 2, 256)};
+      bf16_dw_plan(c, L).rows};
   if (mxfp8_shapes_ok(c)) {
     const Fp8BwdPlan f = fp8_bwd_plan(c, L);
     p[SP_WT] = std::max(p[SP_WT], f.wt);
@@ -348,9 +366,17 @@ extern "C" mok_status mok_workspace_create(const mok_config* c, int device, mok_
     p += parts[SP_DGUH];
     b.dw_part = (float*)p;
     p += parts[SP_DWP];
-    const size_t rb = align_up((size_t)ws->layout.rows_cap_max * c->hidden * 2, 256);
-    b.x_rows = (uint16_t*)p;
-    b.dout_rows = (uint16_t*)(p + rb);
+    {
+      const Bf16DwPlan f = bf16_dw_plan(*c, ws->layout);
+      uint8_t* r = (uint8_t*)p;  // start of the ROWS region
+      TqArrays& q = b.tq16;
+      q.x = r;
+      q.dy = r + f.xc;
+      q.h = r + 2 * f.xc;
+      q.dg = r + 2 * f.xc + f.ic;
+      q.du = r + 2 * f.xc + 2 * f.ic;
+      q.kr_cap = f.kr_cap;
+    }
     if (mxfp8_shapes_ok(*c)) {
       const Fp8BwdPlan f = fp8_bwd_plan(*c, ws->layout);
       uint8_t* w = (uint8_t*)b.wdT;  // start of the WT region
@@ -367,7 +393,7 @@ extern "C" mok_status mok_workspace_create(const mok_config* c, int device, mok_
       b.du32 = (float*)((char*)b.dg + align_up(ce * 4, 256));
       b.duq = (uint8_t*)b.dg + 2 * align_up(ce * 4, 256);
       b.duq_scale = b.duq + align_up(ce, 256);
-      uint8_t* r = (uint8_t*)b.x_rows;  // start of the ROWS region
+      uint8_t* r = b.tq16.x;  // start of the ROWS region
       TqArrays& q = b.tq;
       q.x = r;
       q.xs = r + f.xc;

@@ -28,7 +28,6 @@
 //   bwd_dw    : TN grouped GEMM, the three weight gradients per expert
 #include "device_common.h"
 #include "gemm_nt.h"
-#include "gemm_tn.h"
 #include "mok_internal.h"
 
 namespace mok {
@@ -64,26 +63,6 @@ __global__ void __launch_bounds__(256) transpose_bf16(const uint16_t* __restrict
 #pragma unroll
     for (int q = 0; q < 4; ++q) w[q] = (uint32_t)tile[r + 2 * q][c] | ((uint32_t)tile[r + 2 * q + 1][c] << 16);
     *reinterpret_cast<uint4*>(dst + (int64_t)(tc * 64 + c) * R + tr * 64 + r) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-// x_rows[r] = x[token(r)], dout_rows[r] = grad_out[token(r)] for the kept
-// rows of the schedule (padding rows are never read).
-__global__ void __launch_bounds__(256) gather_rows(const int32_t* __restrict__ hdr, const int32_t* __restrict__ row_src,
-                                                   const uint16_t* __restrict__ x, const uint16_t* __restrict__ dout,
-                                                   uint16_t* __restrict__ x_rows, uint16_t* __restrict__ dout_rows,
-                                                   int H, int k) {
-  const int rows = hdr[HDR_ROWS_TOTAL];
-  const int nch = H / 8;
-  for (int r = blockIdx.x; r < rows; r += gridDim.x) {
-    const int a = row_src[r];
-    if (a < 0) continue;
-    const int64_t tok = a / k;
-    for (int c = threadIdx.x; c < nch; c += blockDim.x) {
-      *reinterpret_cast<uint4*>(x_rows + (int64_t)r * H + c * 8) = *reinterpret_cast<const uint4*>(x + tok * H + c * 8);
-      *reinterpret_cast<uint4*>(dout_rows + (int64_t)r * H + c * 8) =
-          *reinterpret_cast<const uint4*>(dout + tok * H + c * 8);
-    }
   }
 }
 
@@ -320,13 +299,6 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
       MOK_HIP_TRY(transpose(w->shared_up, b.suT, 1, Is, H, s));
     }
   }
-  const int rows_grid = (int)std::min<int64_t>(rcm, (int64_t)ws->num_cus * 8);
-  {
-    LaunchTimer tm(ws, MOK_K_BWD_GATHER, s);
-    gather_rows<<<rows_grid, 256, 0, s>>>(v.header, v.row_src, (const uint16_t*)a.x, (const uint16_t*)a.grad_out,
-                                          b.x_rows, b.dout_rows, H, k);
-    MOK_HIP_TRY(hipGetLastError());
-  }
   const int grid = ws->num_cus;  // one 512-thread workgroup per compute unit
   auto sched_params = [&](nt::Params& p) {
     p.hdr = v.header;
@@ -353,7 +325,6 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
     p.h_in = (const uint16_t*)a.ctx_h;
     p.dg_out = b.dg;
     p.du_out = b.du;
-    p.hw_out = b.hw;
     p.dw_part = b.dw_part;
     p.dw_parts = dw_parts(c);
     LaunchTimer tm(ws, MOK_K_BWD_DH, s);
@@ -391,22 +362,27 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
     MOK_HIP_TRY(hipGetLastError());
   }
   {
-    tn::Params p{};
-    p.offsets = v.offsets;
-    p.kept = v.kept;
-    p.hdr = v.header;
-    p.E = E;
-    p.H = H;
-    p.I = I;
-    p.Is = Is;
-    p.rows_cap_max = rcm;
-    p.dout_rows = b.dout_rows;
-    p.x_rows = b.x_rows;
-    p.dout = (const uint16_t*)a.grad_out;
-    p.x = (const uint16_t*)a.x;
-    p.hw = b.hw;
-    p.dg = b.dg;
-    p.du = b.du;
+    // weight-gradient operands, transposed per expert ([cols, K_e] bf16):
+    // x rows, router weight times grad_out rows, h, dG, dU
+    LaunchTimer tm(ws, MOK_K_BWD_GATHER, s);
+    const TqArrays& q = b.tq16;
+    const int qgrid = ws->num_cus * 4;
+    MOK_HIP_TRY(launch_quantize_t_rows(0, v, a.x, nullptr, nullptr, nullptr, E, k, H, H, rcm, q.kr_cap, q.x, nullptr,
+                                       qgrid, s, true));
+    MOK_HIP_TRY(launch_quantize_t_rows(1, v, a.grad_out, nullptr, nullptr, a.router_w, E, k, H, H, rcm, q.kr_cap, q.dy,
+                                       nullptr, qgrid, s, true));
+    MOK_HIP_TRY(launch_quantize_t_rows(2, v, a.ctx_h, nullptr, nullptr, nullptr, E, k, I, Is, rcm, q.kr_cap, q.h, nullptr,
+                                       qgrid, s, true));
+    MOK_HIP_TRY(launch_quantize_t_rows(2, v, b.dg, nullptr, nullptr, nullptr, E, k, I, Is, rcm, q.kr_cap, q.dg, nullptr,
+                                       qgrid, s, true));
+    MOK_HIP_TRY(launch_quantize_t_rows(2, v, b.du, nullptr, nullptr, nullptr, E, k, I, Is, rcm, q.kr_cap, q.du, nullptr,
+                                       qgrid, s, true));
+  }
+  {
+    nt::Params p{};
+    sched_params(p);
+    p.tiles = v.tiles + tile_bm_index(128) * (E + 2);  // each expert's K offset and length
+    p.tq = b.tq16;
     p.d_wd = (uint16_t*)g->d_routed_down;
     p.d_wg = (uint16_t*)g->d_routed_gate;
     p.d_wu = (uint16_t*)g->d_routed_up;
@@ -414,7 +390,7 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
     p.d_sg = (uint16_t*)g->d_shared_gate;
     p.d_su = (uint16_t*)g->d_shared_up;
     LaunchTimer tm(ws, MOK_K_BWD_DW, s);
-    tn::grouped_gemm_tn<<<ws->num_cus * tn::kBlocksPerCu, tn::NTHR, 0, s>>>(p);
+    nt::grouped_gemm_nt<nt::BWD_DW, false><<<grid, nt::NTHR, 0, s>>>(p);
     MOK_HIP_TRY(hipGetLastError());
   }
   return hipSuccess;

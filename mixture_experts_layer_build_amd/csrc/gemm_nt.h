@@ -41,6 +41,7 @@ constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;       // 32 KiB + 32 KiB
 constexpr int SA_BYTES = BM * 4, SB_BYTES = BN * 4;           // E8M0 scale dwords of a K step (MXFP8)
 constexpr int kNumXcd = 8;
 constexpr int kMaxLdsE = 256;  // schedules with more experts search the tile table in global memory
+constexpr int kGroupM = 4;  // BWD_DW tile order: 4 M tiles per group
 constexpr int kDwPartsPerNTile = 4;  // partial router-weight gradients per N tile (one per wave column)
 constexpr uint32_t kOff = 0x80000000u;  // offset past every resource: loads return 0
 
@@ -49,8 +50,8 @@ enum Mode : int {
   DOWN = 1,     // A = h rows, B = down rows, epilogue y = w * acc
   BWD_DH = 2,   // A = tokens of grad_out, B = rows of down^T, epilogue dG, dU, w*h, partial dw
   BWD_DX = 3,   // A = [dG | dU] rows, B = rows of [gate^T | up^T], epilogue dA rows
-  BWD_DW = 4    // per expert, K = its rows: dW_down = dY^T h, dW_gate = dG^T X, dW_up = dU^T X (MXFP8,
-                // operands stored transposed, [cols, K_e], quantized in 32-row blocks)
+  BWD_DW = 4    // per expert, K = its rows: dW_down = dY^T h, dW_gate = dG^T X, dW_up = dU^T X, the
+                // operands stored transposed, [cols, K_e] (bf16, or MXFP8 quantized in 32-row blocks)
 };
 
 struct Params {
@@ -286,8 +287,14 @@ grouped_gemm_nt(Params p) {
       const int tt = rem0 - t.job * tpj;
       const int Ivt = sh ? p.Is : p.I;
       const int nn = t.job == 0 ? (Ivt + BN - 1) / BN : hb;  // N tiles of the job
-      const int mt = tt / nn;
-      t.nt = tt - mt * nn;
+      const int nm = t.job == 0 ? hb : (Ivt + BM - 1) / BM;  // M tiles of the job
+      // grouped order: runs of kGroupM M tiles x all N tiles, M fastest, so
+      // the tiles in flight together share both operands' rows in L2
+      const int grp = tt / (kGroupM * nn);
+      const int gm = min(kGroupM, nm - grp * kGroupM);
+      const int rr = tt - grp * kGroupM * nn;
+      const int mt = grp * kGroupM + rr % gm;
+      t.nt = rr / gm;
       t.m0 = mt * BM;
       t.m_end = t.job == 0 ? p.H : Ivt;
       const int k0t = sh ? tile_at(E) : tile_at(t.e);
@@ -374,15 +381,15 @@ grouped_gemm_nt(Params p) {
       const int Mc = t.m_end;  // M columns of the job's A array
       const int colsA_r = t.job == 0 ? p.H : p.I, colsB_r = t.job == 0 ? p.I : p.H;
       dw_a = t.job == 0 ? p.tq.dy : t.job == 1 ? p.tq.dg : p.tq.du;
-      dw_as = t.job == 0 ? p.tq.dys : t.job == 1 ? p.tq.dgs : p.tq.dus;
+      dw_as = t.job == 0 ? p.tq.dys : t.job == 1 ? p.tq.dgs : p.tq.dus;  // MXFP8 only
       dw_b = t.job == 0 ? p.tq.h : p.tq.x;
       dw_bs = t.job == 0 ? p.tq.hs : p.tq.xs;
       dw_a_blk = shared ? p.tq.kr_cap * colsA_r : (int64_t)t.kofs * Mc;
       dw_as_blk = shared ? p.tq.kr_cap / 32 * colsA_r : (int64_t)(t.kofs / 32) * Mc;
       dw_b_blk = shared ? p.tq.kr_cap * colsB_r : (int64_t)t.kofs * Nd;
       dw_bs_blk = shared ? p.tq.kr_cap / 32 * colsB_r : (int64_t)(t.kofs / 32) * Nd;
-      a_base = dw_a + dw_a_blk + (int64_t)t.m0 * K;
-      a_bytes = (uint32_t)((int64_t)rows_here * K);
+      a_base = dw_a + (dw_a_blk + (int64_t)t.m0 * K) * ES;
+      a_bytes = (uint32_t)((int64_t)rows_here * K * ES);
     } else if (a_by_token) {
       a_base = (const uint8_t*)p.a_tok;
       a_bytes = (uint32_t)((int64_t)T * K * ES);
@@ -401,8 +408,8 @@ grouped_gemm_nt(Params p) {
     uint32_t b_bytes;
     const int b_k = MODE == BWD_DX ? Iv : K;
     if constexpr (MODE == BWD_DW) {
-      b_base = dw_b + dw_b_blk;
-      b_bytes = (uint32_t)((int64_t)Nd * K);
+      b_base = dw_b + dw_b_blk * ES;
+      b_bytes = (uint32_t)((int64_t)Nd * K * ES);
     } else {
       const int64_t estride = (int64_t)Nd * b_k * ES;
       const void* r0 = (MODE == GATE_UP && wave >= 4) ? p.b1 : p.b0;
@@ -775,7 +782,7 @@ grouped_gemm_nt(Params p) {
               *reinterpret_cast<uint2*>(p.dg_out + rowo + n) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
               *reinterpret_cast<uint2*>(p.du_out + rowo + n) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
             }
-            if constexpr (!FP8)
+            if (!FP8 && p.hw_out)
               *reinterpret_cast<uint2*>(p.hw_out + rowo + n) =
                   make_uint2(pack_bf16x2(hwv[0], hwv[1]), pack_bf16x2(hwv[2], hwv[3]));
           }

@@ -68,12 +68,13 @@ struct TimedLaunch {
   hipEvent_t start, stop;
 };
 
-// Transposed, row-block-quantized operands of the MXFP8 weight-gradient
-// GEMMs. Expert e's block of an array with `cols` columns starts at code
-// element kofs_e * cols (kofs_e = 128 * the expert's first 128-row tile) and
-// is [cols, K_e] with K_e = 128 * its 128-row tile count; its scales start
-// at kofs_e / 32 * cols and are [cols, K_e / 32]. The shared expert's block
-// sits at K offset kr_cap (a static bound on the routed total).
+// Transposed operands of the weight-gradient GEMMs (bf16 elements, or MXFP8
+// codes quantized in 32-row blocks with their scales). Expert e's block of an
+// array with `cols` columns starts at element kofs_e * cols (kofs_e = 128 *
+// the expert's first 128-row tile) and is [cols, K_e] with K_e = 128 * its
+// 128-row tile count (rows past the segment are zero); MXFP8 scales start at
+// kofs_e / 32 * cols and are [cols, K_e / 32]. The shared expert's block sits
+// at K offset kr_cap (a static bound on the routed total).
 struct TqArrays {
   uint8_t* x;       // cols H: x rows of the expert (shared: all tokens)
   uint8_t* dy;      // cols H: w * grad_out rows
@@ -98,12 +99,10 @@ struct BwdScratch {
   uint16_t* sdT = nullptr;  // [I_s, H]
   uint16_t* sgT = nullptr;  // [H, I_s]
   uint16_t* suT = nullptr;
-  uint16_t* dg = nullptr;   // dG, dU, w*h: routed [rows_cap_max, I] then shared [T_max, I_s]
+  uint16_t* dg = nullptr;   // dG, dU: routed [rows_cap_max, I] then shared [T_max, I_s]
   uint16_t* du = nullptr;
-  uint16_t* hw = nullptr;
+  uint16_t* hw = nullptr;   // (third slot of the region; the MXFP8 backward keeps dU's codes there)
   float* dw_part = nullptr;      // [rows_cap_max + T_max, dw_parts(cfg)]
-  uint16_t* x_rows = nullptr;    // [rows_cap_max, H]
-  uint16_t* dout_rows = nullptr;
   // MXFP8: transposed weights quantized along their new rows (codes, scales)
   uint8_t *wdTq = nullptr, *wgTq = nullptr, *wuTq = nullptr, *sdTq = nullptr, *sgTq = nullptr, *suTq = nullptr;
   uint8_t *wdTs = nullptr, *wgTs = nullptr, *wuTs = nullptr, *sdTs = nullptr, *sgTs = nullptr, *suTs = nullptr;
@@ -113,8 +112,9 @@ struct BwdScratch {
   // MXFP8: dU quantized along I (dG uses the workspace's hq buffer)
   uint8_t* duq = nullptr;
   uint8_t* duq_scale = nullptr;
-  // MXFP8: operands of the weight-gradient GEMMs
+  // operands of the weight-gradient GEMMs: MXFP8 (tq) and bf16 (tq16)
   TqArrays tq{};
+  TqArrays tq16{};
   bool mxfp8_ready = false;  // the configuration admits the MXFP8 backward and its buffers exist
 };
 
@@ -183,14 +183,15 @@ hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a
 // codes with [B][C][R/32] scales (R % 128 == 0, C % 64 == 0).
 hipError_t launch_quantize_t_matrix(const void* src, int64_t batches, int64_t R, int64_t C, uint8_t* dst,
                                     uint8_t* dst_scale, int grid_cap, hipStream_t s);
-// The weight-gradient GEMM operands (TqArrays layout) from one source:
+// The weight-gradient GEMM operands (TqArrays layout; bf16 elements without
+// scales when out_bf16, kinds 0-2 only) from one source:
 // src_kind 0 = x token rows, 1 = router weight times grad_out token rows,
 // 2 = schedule-row bf16 rows, 3 = schedule-row MXFP8 rows (h), 4 =
 // schedule-row fp32 rows (dG, dU).
 hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* src, const uint8_t* src_codes,
                                   const uint8_t* src_scale, const float* router_w, int E, int k, int cols_r, int cols_s,
                                   int64_t rows_cap_max, int64_t kr_cap, uint8_t* dst, uint8_t* dst_scale, int grid,
-                                  hipStream_t s);
+                                  hipStream_t s, bool out_bf16 = false);
 // dG / dU rows (fp32) quantized along I: routed rows [0, offsets[E]) and
 // shared rows [rows_cap_max, rows_cap_max + T).
 hipError_t launch_quantize_rows_sched(const void* src, const int32_t* hdr, int64_t rows_cap_max, int I, int Is,

@@ -215,6 +215,18 @@ __device__ __forceinline__ void tq_store(const float (*tile)[kTqLd], uint8_t* ou
   scale_row[b] = (uint8_t)(X + 127);
 }
 
+// The same tile transposed without quantization: thread (c, b) writes the 32
+// values of column c, rows 32b .. 32b+31, as bf16 (round to nearest even).
+__device__ __forceinline__ void tq_store_bf16(const float (*tile)[kTqLd], uint16_t* out_row) {
+  const int c = threadIdx.x >> 2, b = threadIdx.x & 3;
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = pack_bf16x2(tile[32 * b + 2 * i][c], tile[32 * b + 2 * i + 1][c]);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<uint4*>(out_row + 32 * b + 8 * q) = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+}
+
 __device__ __forceinline__ void bf16x32_to_tile(float (*tile)[kTqLd], int r, int half, const uint16_t* src, float mul) {
   // src: 32 consecutive bf16 values (64 bytes, 16-byte aligned), or nullptr for a zero row
 #pragma unroll
@@ -276,10 +288,11 @@ struct TqParams {
 };
 
 // The weight-gradient GEMMs' operands: for expert e, rows of its segment in
-// 128-row blocks (rows past kept[e] are zero) -> [cols, K_e] codes at
-// 128 * tiles128[e] * cols_r, quantized along the rows; the shared expert's
-// all-token segment -> [cols_s, K_s] at kr_cap * cols_r.
-template <int SRC>
+// 128-row blocks (rows past kept[e] are zero) -> [cols, K_e] elements at
+// 128 * tiles128[e] * cols_r, either MXFP8 (quantized along the rows, with
+// scales) or bf16 (OUT_BF16); the shared expert's all-token segment ->
+// [cols_s, K_s] at kr_cap * cols_r.
+template <int SRC, bool OUT_BF16>
 __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
   __shared__ float tile[kTqRows][kTqLd];
   const int E = p.E;
@@ -366,7 +379,10 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
     const int64_t base = shared ? p.kr_cap * p.cols_r : kofs * cols;
     const int64_t sbase = shared ? p.kr_cap / 32 * p.cols_r : kofs / 32 * cols;
     const int64_t c = cc * kTqCols + (threadIdx.x >> 2);
-    tq_store(tile, p.dst + base + c * Kp + (int64_t)kl * kTqRows, p.dst_scale + sbase + c * (Kp / 32) + kl * 4);
+    if constexpr (OUT_BF16)
+      tq_store_bf16(tile, reinterpret_cast<uint16_t*>(p.dst) + base + c * Kp + (int64_t)kl * kTqRows);
+    else
+      tq_store(tile, p.dst + base + c * Kp + (int64_t)kl * kTqRows, p.dst_scale + sbase + c * (Kp / 32) + kl * 4);
     __syncthreads();
   }
 }
@@ -425,7 +441,7 @@ hipError_t launch_quantize_t_matrix(const void* src, int64_t batches, int64_t R,
 hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* src, const uint8_t* src_codes,
                                   const uint8_t* src_scale, const float* router_w, int E, int k, int cols_r, int cols_s,
                                   int64_t rows_cap_max, int64_t kr_cap, uint8_t* dst, uint8_t* dst_scale, int grid,
-                                  hipStream_t s) {
+                                  hipStream_t s, bool out_bf16) {
   TqParams p{};
   p.hdr = v.header;
   p.offsets = v.offsets;
@@ -445,12 +461,21 @@ hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* 
   p.src_scale = src_scale;
   p.dst = dst;
   p.dst_scale = dst_scale;
-  switch (src_kind) {
-    case TQ_X: quant_t_rows<TQ_X><<<grid, 256, 0, s>>>(p); break;
-    case TQ_DY: quant_t_rows<TQ_DY><<<grid, 256, 0, s>>>(p); break;
-    case TQ_ROWS: quant_t_rows<TQ_ROWS><<<grid, 256, 0, s>>>(p); break;
-    case TQ_ROWS32: quant_t_rows<TQ_ROWS32><<<grid, 256, 0, s>>>(p); break;
-    default: quant_t_rows<TQ_MX><<<grid, 256, 0, s>>>(p); break;
+  if (out_bf16) {
+    switch (src_kind) {
+      case TQ_X: quant_t_rows<TQ_X, true><<<grid, 256, 0, s>>>(p); break;
+      case TQ_DY: quant_t_rows<TQ_DY, true><<<grid, 256, 0, s>>>(p); break;
+      case TQ_ROWS: quant_t_rows<TQ_ROWS, true><<<grid, 256, 0, s>>>(p); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (src_kind) {
+      case TQ_X: quant_t_rows<TQ_X, false><<<grid, 256, 0, s>>>(p); break;
+      case TQ_DY: quant_t_rows<TQ_DY, false><<<grid, 256, 0, s>>>(p); break;
+      case TQ_ROWS: quant_t_rows<TQ_ROWS, false><<<grid, 256, 0, s>>>(p); break;
+      case TQ_ROWS32: quant_t_rows<TQ_ROWS32, false><<<grid, 256, 0, s>>>(p); break;
+      default: quant_t_rows<TQ_MX, false><<<grid, 256, 0, s>>>(p); break;
+    }
   }
   return hipGetLastError();
 }
