@@ -64,6 +64,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(CONFIGS))
     ap.add_argument("--mult", type=float, default=None, help="override the capacity multiplier")
+    ap.add_argument("--minibatch", type=int, default=0, help="minibatch_size of the forward's minibatch pipeline (0 = off)")
+    ap.add_argument("--movers", type=int, default=0, help="compute units given to the combine in the pipeline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="oracle chunk size; 0 = automatic")
     ap.add_argument("--all", action="store_true", help="one line per workload (diagnostics)")
@@ -148,14 +150,16 @@ def copy_calibration(mib: int) -> None:
     torch.cuda.synchronize()
 
 
-def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sample_tokens: int) -> dict:
+def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sample_tokens: int,
+        minibatch: int = 0, movers: int = 0) -> dict:
     import torch
     import mixture_experts_layer_build_amd as mok
 
     inp = make_inputs(c)
     d = to_device(inp, torch)
     cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=c.T,
-                        shared_intermediate=c.I_s, capacity_multiplier=mult, expert_pad=c.expert_pad)
+                        shared_intermediate=c.I_s, capacity_multiplier=mult, expert_pad=c.expert_pad,
+                        minibatch_size=minibatch, num_mover_wgs=movers)
     ws = mok.Workspace(cfg)
     mode = mok.MOK_MODE_MXFP8 if c.mode == "mxfp8" else mok.MOK_MODE_BF16
     training = c.passes != "fwd"
@@ -216,6 +220,7 @@ def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sampl
         "config": {"workload": c.name, "tokens": c.T, "hidden": c.H, "intermediate": c.I, "experts": c.E,
                    "topk": c.k, "shared_intermediate": c.I_s, "capacity_multiplier": mult,
                    "expert_pad": c.expert_pad, "passes": c.passes, "kept_assignments": R_kept,
+                   "minibatch_size": minibatch, "num_mover_wgs": movers,
                    "parallelism": "single GPU (one GPU's share; no all-to-all)"},
         "tflops": round(flops / (dt / steps) / 1e12, 2),
         "frac_of_peak_layer": round(flops / (dt / steps) / 1e12 / peak, 4),
@@ -244,7 +249,8 @@ def main():
     for n in names:
         c = CONFIGS[n]
         mult = c.capacity_multiplier if a.mult is None else a.mult
-        line = run(c, a.steps, a.warmup, mult, not a.no_cpu_baseline and not a.all, a.cpu_sample_tokens)
+        line = run(c, a.steps, a.warmup, mult, not a.no_cpu_baseline and not a.all, a.cpu_sample_tokens,
+                   a.minibatch, a.movers)
         print(json.dumps(line), flush=True)
     if a.copy_calibration:
         copy_calibration(a.copy_calibration)

@@ -79,8 +79,14 @@ typedef struct mok_config {
   int64_t max_tokens;           /* T_max: sizes every buffer for the worst case */
   float capacity_multiplier;    /* per-expert capacity C = min(T, ceil(mult * T)) ([R] "Tuning...": schedule_capacity_multiplier) */
   int32_t expert_pad;           /* P: each expert segment padded to a multiple of P rows ([R] "Tuning...": expert padding) */
-  int32_t minibatch_size;       /* tokens per minibatch of the schedule's sub-offsets; 0 = one minibatch ([R] "Tuning...": minibatch_size) */
-  int32_t num_mover_wgs;        /* reserved for the pipelined forward; 0 = automatic */
+  int32_t minibatch_size;       /* tokens per minibatch: the schedule's sub-offsets, and the granularity of the
+                                   forward's minibatch pipeline; 0 = one minibatch ([R] "Tuning...": minibatch_size) */
+  int32_t num_mover_wgs;        /* compute units given to the combine in the minibatch pipeline (rounded down to a
+                                   multiple of 8); 0 = no pipeline. With minibatch_size > 0 and num_mover_wgs >= 8,
+                                   mok_forward runs the down GEMM of minibatch b on the other compute units while
+                                   the combine of minibatch b-1 runs on these, on a stream the workspace owns
+                                   ([R] "Tuning...": fwd_num_comm_sms, minibatch_size). The result bits do not
+                                   depend on either value. */
 } mok_config;
 
 /* Routed and shared expert weights, layouts of [A] _MoKRuntime.forward:

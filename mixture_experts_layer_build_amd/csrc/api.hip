@@ -414,6 +414,21 @@ extern "C" mok_status mok_workspace_create(const mok_config* c, int device, mok_
     }
     p += parts[SP_ROWS];
   }
+  // minibatch pipeline: an auxiliary stream (default priority) for the
+  // combine and one event per minibatch plus a join event
+  if (c->minibatch_size > 0 && c->num_mover_wgs > 0 && (int64_t)c->minibatch_size < c->max_tokens) {
+    const int64_t n_mbq = (c->max_tokens + c->minibatch_size - 1) / c->minibatch_size;
+    bool ok = hipStreamCreateWithFlags(&ws->aux_stream, hipStreamNonBlocking) == hipSuccess;
+    for (int64_t i = 0; ok && i <= n_mbq; ++i) {
+      hipEvent_t e;
+      ok = hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+      if (ok) ws->mb_events.push_back(e);
+    }
+    if (!ok) {
+      (void)mok_workspace_destroy(ws);
+      return MOK_ERR_HIP;
+    }
+  }
   *out = ws;
   return MOK_OK;
 }
@@ -429,6 +444,8 @@ extern "C" mok_status mok_workspace_destroy(mok_workspace* ws) {
       (void)hipEventDestroy(l.stop);
     }
     for (auto e : ws->event_pool) (void)hipEventDestroy(e);
+    for (auto e : ws->mb_events) (void)hipEventDestroy(e);
+    if (ws->aux_stream && hipStreamDestroy(ws->aux_stream) != hipSuccess) st = MOK_ERR_HIP;
     if (ws->scratch && hipFree(ws->scratch) != hipSuccess) st = MOK_ERR_HIP;
   }
   delete ws;

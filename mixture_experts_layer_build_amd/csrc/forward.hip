@@ -26,13 +26,16 @@
 namespace mok {
 namespace {
 
-// out[t] = bf16(sum_j y[slot_row[t*k + j]] (kept slots, slot order) + y_shared[t]).
+// out[t] = bf16(sum_j y[slot_row[t*k + j]] (kept slots, slot order) + y_shared[t]),
+// for every token (mb == 0) or the tokens of minibatch mb_index.
 __global__ void __launch_bounds__(256) combine_bf16(const int32_t* __restrict__ hdr, const int32_t* __restrict__ slot_row,
                                                     const uint16_t* __restrict__ y, const uint16_t* __restrict__ y_shared,
-                                                    uint16_t* __restrict__ out, int H, int k) {
+                                                    uint16_t* __restrict__ out, int H, int k, int mb_index, int mb) {
   const int T = hdr[HDR_T];
+  const int t0 = mb > 0 ? min(T, mb_index * mb) : 0;
+  const int t1 = mb > 0 ? min(T, t0 + mb) : T;
   const int nchunk = H / 8;
-  for (int t = blockIdx.x; t < T; t += gridDim.x) {
+  for (int t = t0 + (int)blockIdx.x; t < t1; t += gridDim.x) {
     const int32_t* sl = slot_row + (int64_t)t * k;
     for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
       float acc[8];
@@ -77,12 +80,25 @@ static void fill_schedule(nt::Params& p, const mok_workspace* ws, const SchedVie
   p.kept = v.kept;
   p.tiles = v.tiles + tile_bm_index(nt::BM) * (c.num_experts + 2);
   p.row_src = v.row_src;
+  p.mb_offsets = v.mb_offsets;
   p.E = c.num_experts;
   p.k = c.topk;
   p.H = c.hidden;
   p.I = c.intermediate;
   p.Is = c.shared_intermediate;
   p.rows_cap_max = ws->layout.rows_cap_max;
+}
+
+// Compute units given to the combine in the minibatch pipeline (0 = no
+// pipeline): num_mover_wgs rounded down to a multiple of the XCD count, with
+// at least one XCD's worth left to the GEMMs; the pipeline needs the tile
+// tables in LDS and more than one minibatch.
+int mover_units(const mok_workspace* ws) {
+  const mok_config& c = ws->cfg;
+  if (c.minibatch_size <= 0 || c.num_mover_wgs <= 0 || c.num_experts > nt::kMaxLdsE) return 0;
+  if ((int64_t)c.minibatch_size >= c.max_tokens || ws->aux_stream == nullptr) return 0;
+  const int m = c.num_mover_wgs / nt::kNumXcd * nt::kNumXcd;
+  return std::min(m, ws->num_cus - nt::kNumXcd);
 }
 
 hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a, hipStream_t s) {
@@ -142,22 +158,57 @@ hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a
   d.b0s = a.w->routed_down_scale;
   d.sb0s = a.w->shared_down_scale;
   d.out = a.y;
-  {
-    LaunchTimer tm(ws, MOK_K_DOWN, s);
-    if (a.mxfp8)
-      nt::grouped_gemm_nt<nt::DOWN, true><<<grid, nt::NTHR, 0, s>>>(d);
-    else
-      nt::grouped_gemm_nt<nt::DOWN, false><<<grid, nt::NTHR, 0, s>>>(d);
-    MOK_HIP_TRY(hipGetLastError());
-  }
-  {
+  const uint16_t* y = (const uint16_t*)a.y;
+  const uint16_t* ys = c.shared_intermediate > 0 ? y + ws->layout.rows_cap_max * c.hidden : nullptr;
+  const int cgrid = (int)std::min<int64_t>(c.max_tokens, (int64_t)ws->num_cus * 8);
+  const int movers = mover_units(ws);
+  if (movers == 0) {
+    {
+      LaunchTimer tm(ws, MOK_K_DOWN, s);
+      if (a.mxfp8)
+        nt::grouped_gemm_nt<nt::DOWN, true><<<grid, nt::NTHR, 0, s>>>(d);
+      else
+        nt::grouped_gemm_nt<nt::DOWN, false><<<grid, nt::NTHR, 0, s>>>(d);
+      MOK_HIP_TRY(hipGetLastError());
+    }
     LaunchTimer tm(ws, MOK_K_COMBINE, s);
-    const int cgrid = (int)std::min<int64_t>(c.max_tokens, (int64_t)ws->num_cus * 8);
-    const uint16_t* y = (const uint16_t*)a.y;
-    const uint16_t* ys = c.shared_intermediate > 0 ? y + ws->layout.rows_cap_max * c.hidden : nullptr;
-    combine_bf16<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, ys, (uint16_t*)a.out, c.hidden, c.topk);
+    combine_bf16<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, ys, (uint16_t*)a.out, c.hidden, c.topk, 0, 0);
+    MOK_HIP_TRY(hipGetLastError());
+    return hipSuccess;
+  }
+  // Minibatch pipeline ("Tuning the five hyperparameters before production":
+  // minibatch_size sets the granularity of the overlap, a set of SMs is
+  // given to the exchange). The down GEMM of minibatch b runs on the other
+  // compute units on the caller's stream; when it is done, the combine of
+  // minibatch b runs on `movers` compute units on the workspace's auxiliary
+  // stream while the down GEMM of minibatch b+1 proceeds. The host does not
+  // know T, so it launches every minibatch T_max allows; launches past the
+  // schedule's minibatch count find no rows. Each output row is computed by
+  // the same code whatever the split, so the result bits do not depend on
+  // minibatch_size or num_mover_wgs.
+  const int mb = c.minibatch_size;
+  const int n_mbq = (int)((c.max_tokens + mb - 1) / mb);
+  const int dgrid = ws->num_cus - movers;
+  d.mb = mb;
+  hipStream_t aux = ws->aux_stream;
+  for (int b = 0; b < n_mbq; ++b) {
+    d.mb_index = b;
+    {
+      LaunchTimer tm(ws, MOK_K_DOWN, s);
+      if (a.mxfp8)
+        nt::grouped_gemm_nt<nt::DOWN, true><<<dgrid, nt::NTHR, 0, s>>>(d);
+      else
+        nt::grouped_gemm_nt<nt::DOWN, false><<<dgrid, nt::NTHR, 0, s>>>(d);
+      MOK_HIP_TRY(hipGetLastError());
+    }
+    MOK_HIP_TRY(hipEventRecord(ws->mb_events[b], s));
+    MOK_HIP_TRY(hipStreamWaitEvent(aux, ws->mb_events[b], 0));
+    LaunchTimer tm(ws, MOK_K_COMBINE, aux);
+    combine_bf16<<<movers * 4, 256, 0, aux>>>(v.header, v.slot_row, y, ys, (uint16_t*)a.out, c.hidden, c.topk, b, mb);
     MOK_HIP_TRY(hipGetLastError());
   }
+  MOK_HIP_TRY(hipEventRecord(ws->mb_events[n_mbq], aux));
+  MOK_HIP_TRY(hipStreamWaitEvent(s, ws->mb_events[n_mbq], 0));
   return hipSuccess;
 }
 

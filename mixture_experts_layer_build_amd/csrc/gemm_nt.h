@@ -61,6 +61,9 @@ struct Params {
   const int32_t* kept;
   const int32_t* tiles;    // prefix sums of 256-row tiles per expert; [E] routed total, [E+1] with shared
   const int32_t* row_src;
+  const int32_t* mb_offsets;    // per (minibatch, expert) first rows, [(n_mb + 1) * E]
+  int mb_index;                 // DOWN with mb > 0: only the rows of minibatch mb_index (minibatch pipeline)
+  int mb;                       // tokens per minibatch; 0 = every row
   int E, k, H, I, Is;
   int64_t rows_cap_max;
   // A operand
@@ -118,6 +121,8 @@ struct alignas(16) Lds {
   int32_t tiles[kMaxLdsE + 2];
   int32_t fullp[kMaxLdsE + 2];  // exclusive prefix over experts (shared last) of full M tiles
   int32_t tailp[kMaxLdsE + 2];  // ... and of tail M tiles (a segment's last tile with <= 128 rows)
+  int32_t offs[kMaxLdsE];       // per expert: first row and row count of this launch's segment
+  int32_t keptl[kMaxLdsE];
   int32_t wsum[2][NTHR / 64];   // per-wave partial sums of the two scans
   int32_t row_src[BM];  // per tile row: source row (token, or tile-local row), -1 = none
   float row_w[BM];      // per tile row: router weight (1 for the shared expert)
@@ -156,11 +161,52 @@ grouped_gemm_nt(Params p) {
   const int E = p.E;
 
   const bool lds_tiles = E <= kMaxLdsE;
-  if (lds_tiles)
+  if (lds_tiles) {
     for (int i = tid; i < E + 2; i += NTHR) L.tiles[i] = p.tiles[i];
+    for (int i = tid; i < E; i += NTHR) {
+      L.offs[i] = p.offsets[i];
+      L.keptl[i] = p.kept[i];
+    }
+  }
   const int T = p.hdr[HDR_T];
   __syncthreads();
+  // shared-expert rows of this launch: every token, or one minibatch's tokens
+  int sh0 = 0, sh1 = T;
+  if (MODE == DOWN && p.mb > 0) {
+    // minibatch pipeline: only minibatch b's rows, expert e's being rows
+    // [mb_offsets[b][e], mb_offsets[b+1][e]) of its segment (the schedule
+    // has n_mb minibatches; launches past them get no tiles). The tile table
+    // of these row ranges is built here (the launcher keeps E <= kMaxLdsE).
+    const int b = p.mb_index;
+    const bool real = b < p.hdr[HDR_NMB];
+    sh0 = real ? min(T, b * p.mb) : T;
+    sh1 = real ? min(T, sh0 + p.mb) : T;
+    int cnt = 0;
+    if (tid < E) {
+      const int lo = real ? p.mb_offsets[b * E + tid] : 0;
+      const int hi = real ? p.mb_offsets[(b + 1) * E + tid] : 0;
+      L.offs[tid] = lo;
+      L.keptl[tid] = hi - lo;
+      cnt = (hi - lo + BM - 1) / BM;
+    } else if (tid == E) {
+      cnt = p.Is > 0 ? (sh1 - sh0 + BM - 1) / BM : 0;
+    }
+    int sc = cnt;
+#pragma unroll
+    for (int dd = 1; dd < 64; dd <<= 1) {
+      const int av = __shfl_up(sc, dd);
+      if (lane >= dd) sc += av;
+    }
+    if (lane == 63) L.wsum[0][wave] = sc;
+    __syncthreads();
+    int bs = 0;
+    for (int w = 0; w < wave; ++w) bs += L.wsum[0][w];
+    if (tid <= E + 1) L.tiles[tid] = bs + sc - cnt;  // exclusive prefix; [E + 1] = total with the shared expert
+    __syncthreads();
+  }
   auto tile_at = [&](int e) { return lds_tiles ? L.tiles[e] : p.tiles[e]; };
+  auto offset_at = [&](int e) { return lds_tiles ? L.offs[e] : p.offsets[e]; };
+  auto kept_at = [&](int e) { return lds_tiles ? L.keptl[e] : p.kept[e]; };
   const int n_routed_mt = tile_at(E);
   const int n_all_mt = tile_at(E + 1);
   const int ntw = n_tile_width<MODE>();
@@ -263,16 +309,16 @@ grouped_gemm_nt(Params p) {
         t.nt = v - mi * nt_r;
         const int e = __builtin_amdgcn_readfirstlane(search(full ? L.fullp : L.tailp, mi));
         t.e = e;
-        const int base = p.offsets[e];
+        const int base = offset_at(e);
         const int mt = full ? mi - L.fullp[e] : L.tiles[e + 1] - L.tiles[e] - 1;
         t.m0 = base + mt * BM;
-        t.m_end = base + p.kept[e];
+        t.m_end = base + kept_at(e);
       } else {
         const int mi = (v - vr) / nt_s;
         t.nt = (v - vr) - mi * nt_s;
         t.e = -1;
-        t.m0 = (full ? mi : L.tiles[E + 1] - L.tiles[E] - 1) * BM;
-        t.m_end = T;
+        t.m0 = sh0 + (full ? mi : L.tiles[E + 1] - L.tiles[E] - 1) * BM;
+        t.m_end = sh1;
       }
       t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
       t.m_end = __builtin_amdgcn_readfirstlane(t.m_end);
@@ -322,16 +368,16 @@ grouped_gemm_nt(Params p) {
             hi = mid;
         }
         t.e = __builtin_amdgcn_readfirstlane(lo);
-        const int base = p.offsets[t.e];
+        const int base = offset_at(t.e);
         t.m0 = base + (mt - tile_at(t.e)) * BM;
-        t.m_end = base + p.kept[t.e];
+        t.m_end = base + kept_at(t.e);
       } else {
         const int sid = id - n_routed;
         const int mt = sid / nt_s;
         t.nt = sid - mt * nt_s;
         t.e = -1;
-        t.m0 = mt * BM;
-        t.m_end = T;
+        t.m0 = sh0 + mt * BM;
+        t.m_end = sh1;
       }
       t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
       t.m_end = __builtin_amdgcn_readfirstlane(t.m_end);

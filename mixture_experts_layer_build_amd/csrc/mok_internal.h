@@ -140,6 +140,10 @@ struct mok_workspace {
   uint8_t* hq_scale = nullptr;     // its E8M0 scales, one per 32 along I
   // backward scratch
   mok::BwdScratch bwd;
+  // minibatch pipeline: the combine runs on aux_stream (mover compute units)
+  // while the down GEMM of the next minibatch runs on the caller's stream
+  hipStream_t aux_stream = nullptr;
+  std::vector<hipEvent_t> mb_events;  // one per minibatch (down done), then the join
   // timing
   bool timing = false;
   std::vector<mok::TimedLaunch> launches;
