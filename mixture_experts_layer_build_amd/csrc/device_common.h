@@ -90,6 +90,32 @@ __host__ __device__ __forceinline__ uint32_t e4m3_encode_scaled(float v, int X) 
   return code | sign;
 }
 
+#if defined(__HIP_DEVICE_COMPILE__)
+// E4M3 codes of v0..v3 / 2^X, byte i = code of v_i, with exactly the
+// rounding and saturation of e4m3_encode_scaled, on the scaled conversion
+// instruction of gfx950 (two codes per instruction). The instruction divides
+// by its scale operand and rounds to nearest even, but turns magnitudes
+// above the E4M3 range into NaN, so each input is first clamped to
+// +-448 * 2^X (everything up to the 464 tie rounds to 448 anyway). Checked
+// bit for bit against e4m3_encode_scaled over every block exponent,
+// rounding ties, subnormals, signed zeros and the saturation band.
+__device__ __forceinline__ uint32_t e4m3x4_encode_scaled(float v0, float v1, float v2, float v3, int X) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const float s = __builtin_ldexpf(1.0f, X);
+  const float lim = __builtin_ldexpf(448.0f, X);
+  v0 = __builtin_fminf(__builtin_fmaxf(v0, -lim), lim);
+  v1 = __builtin_fminf(__builtin_fmaxf(v1, -lim), lim);
+  v2 = __builtin_fminf(__builtin_fmaxf(v2, -lim), lim);
+  v3 = __builtin_fminf(__builtin_fmaxf(v3, -lim), lim);
+  s16x2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, v0, v1, s, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, v2, v3, s, true);
+  return (uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
+}
+#else
+__device__ uint32_t e4m3x4_encode_scaled(float v0, float v1, float v2, float v3, int X);  // device only
+#endif
+
 // Value of E4M3 code `code` (low 8 bits) times 2^X: a 4-bit significand
 // scaled by a power of two, so the fp32 result is exact (subnormals too).
 __host__ __device__ __forceinline__ float e4m3_decode_scaled(uint32_t code, int X) {

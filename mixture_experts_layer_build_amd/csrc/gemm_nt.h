@@ -128,8 +128,10 @@ struct alignas(16) Lds {
   float row_w[BM];      // per tile row: router weight (1 for the shared expert)
 };
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
-__device__ __forceinline__ float sigmoid_f(float g) { return 1.0f / (1.0f + __expf(-g)); }
+// SiLU and the logistic function with the hardware reciprocal (1 ulp): the
+// results are rounded to bf16 or E4M3 right after.
+__device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu_f(float g) { return g * sigmoid_f(g); }
 
 template <int MODE>
 __device__ __forceinline__ int n_tile_width() {
@@ -693,9 +695,7 @@ grouped_gemm_nt(Params p) {
           const int X = mx_block_exponent(amax);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) w |= e4m3_encode_scaled(hv[4 * q + c], X) << (8 * c);
+            const uint32_t w = e4m3x4_encode_scaled(hv[4 * q], hv[4 * q + 1], hv[4 * q + 2], hv[4 * q + 3], X);
             *reinterpret_cast<uint32_t*>(reg + (i * 32 + lr) * SW + 8 * q + 4 * lh) = w;
           }
           const int ml = wm * 128 + i * 32 + lr;

@@ -9,7 +9,9 @@
 //
 // HBM-bound streaming kernels: 16-byte loads per lane, consecutive lanes on
 // consecutive 16-byte chunks, the block maximum reduced across the lanes that
-// share a block with cross-lane shuffles.
+// share a block with cross-lane shuffles. Codes of a block come from the
+// hardware scaled conversion (e4m3x4_encode_scaled), bit-identical to the
+// integer encoder, which the axis-0 kernel (a scale per column) keeps.
 #include <algorithm>
 
 #include "device_common.h"
@@ -45,13 +47,11 @@ __global__ void __launch_bounds__(256) quant_axis1_bf16(const uint16_t* __restri
   amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
   if (!live) return;
   const int X = mx_block_exponent(amax);
-  uint32_t c[2] = {0, 0};
+  uint32_t c[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t e0 = e4m3_encode_scaled(u2f(w[i] << 16), X);
-    uint32_t e1 = e4m3_encode_scaled(u2f(w[i] & 0xFFFF0000u), X);
-    c[i >> 1] |= (e0 | (e1 << 8)) << ((i & 1) * 16);
-  }
+  for (int h = 0; h < 2; ++h)
+    c[h] = e4m3x4_encode_scaled(u2f(w[2 * h] << 16), u2f(w[2 * h] & 0xFFFF0000u), u2f(w[2 * h + 1] << 16),
+                                u2f(w[2 * h + 1] & 0xFFFF0000u), X);
   *reinterpret_cast<uint2*>(dst + row * ld_dst + blk * 32 + part * 8) = make_uint2(c[0], c[1]);
   if (part == 0) scale[row * nblk_row + blk] = (uint8_t)(X + 127);
 }
@@ -85,13 +85,11 @@ __global__ void __launch_bounds__(256) quant_rows_dev_bf16(const uint16_t* __res
   amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
   if (!live) return;
   const int X = mx_block_exponent(amax);
-  uint32_t c[2] = {0, 0};
+  uint32_t c[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t e0 = e4m3_encode_scaled(u2f(w[i] << 16), X);
-    uint32_t e1 = e4m3_encode_scaled(u2f(w[i] & 0xFFFF0000u), X);
-    c[i >> 1] |= (e0 | (e1 << 8)) << ((i & 1) * 16);
-  }
+  for (int h = 0; h < 2; ++h)
+    c[h] = e4m3x4_encode_scaled(u2f(w[2 * h] << 16), u2f(w[2 * h] & 0xFFFF0000u), u2f(w[2 * h + 1] << 16),
+                                u2f(w[2 * h + 1] & 0xFFFF0000u), X);
   *reinterpret_cast<uint2*>(dst + row * cols + blk * 32 + part * 8) = make_uint2(c[0], c[1]);
   if (part == 0) scale[row * nblk_row + blk] = (uint8_t)(X + 127);
 }
@@ -119,8 +117,7 @@ __global__ void __launch_bounds__(256) quant_axis1_f32(const float* __restrict__
   amax = max(amax, (uint32_t)__shfl_xor((int)amax, 4));
   if (!live) return;
   const int X = mx_block_exponent(amax);
-  uint32_t c = e4m3_encode_scaled(v.x, X) | (e4m3_encode_scaled(v.y, X) << 8) |
-               (e4m3_encode_scaled(v.z, X) << 16) | (e4m3_encode_scaled(v.w, X) << 24);
+  const uint32_t c = e4m3x4_encode_scaled(v.x, v.y, v.z, v.w, X);
   *reinterpret_cast<uint32_t*>(dst + row * ld_dst + blk * 32 + part * 4) = c;
   if (part == 0) scale[row * nblk_row + blk] = (uint8_t)(X + 127);
 }
@@ -207,8 +204,7 @@ __device__ __forceinline__ void tq_store(const float (*tile)[kTqLd], uint8_t* ou
   uint32_t w[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q)
-    w[q] = e4m3_encode_scaled(v[4 * q], X) | (e4m3_encode_scaled(v[4 * q + 1], X) << 8) |
-           (e4m3_encode_scaled(v[4 * q + 2], X) << 16) | (e4m3_encode_scaled(v[4 * q + 3], X) << 24);
+    w[q] = e4m3x4_encode_scaled(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], X);
   // out_row / scale_row: the output row of this thread's column c, at the tile's first block
   *reinterpret_cast<uint4*>(out_row + 32 * b) = make_uint4(w[0], w[1], w[2], w[3]);
   *reinterpret_cast<uint4*>(out_row + 32 * b + 16) = make_uint4(w[4], w[5], w[6], w[7]);
@@ -421,8 +417,7 @@ __global__ void __launch_bounds__(256) quant_rows_sched_f32(const float* __restr
   amax = max(amax, (uint32_t)__shfl_xor((int)amax, 4));
   if (!live) return;
   const int X = mx_block_exponent(amax);
-  const uint32_t c = e4m3_encode_scaled(v.x, X) | (e4m3_encode_scaled(v.y, X) << 8) |
-                     (e4m3_encode_scaled(v.z, X) << 16) | (e4m3_encode_scaled(v.w, X) << 24);
+  const uint32_t c = e4m3x4_encode_scaled(v.x, v.y, v.z, v.w, X);
   *reinterpret_cast<uint32_t*>(dst + eoff + part * 4) = c;
   if (part == 0) scale[soff] = (uint8_t)(X + 127);
 }
