@@ -92,3 +92,32 @@ def test_quantize_strided_source_and_destination():
     np.testing.assert_array_equal(o[:, :128], rc)
     assert np.all(o[:, 128:] == 0xAB)  # padding columns untouched
     np.testing.assert_array_equal(sc.cpu().numpy(), rs)
+
+
+def test_quantize_every_block_exponent():
+    # one 32-element fp32 block per block exponent X = -127 .. 127 (several
+    # blocks each): magnitudes up to 2^(X+8) .. 448 * 2^X with E4M3 rounding
+    # ties and values in the saturation band, down to fp32 subnormals
+    rng = np.random.default_rng(11)
+    blocks = []
+    grid = np.array([(m / 8.0) * 2.0 ** (-6) if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+                     for e in range(16) for m in range(8)][:127])  # E4M3 magnitudes up to 448
+    for X in range(-127, 128):
+        for rep in range(4):
+            b = np.empty(32)
+            kind = rep % 4
+            if kind == 0:      # random magnitudes below the block maximum
+                b[:] = rng.uniform(0, 1, 32) * 2.0 ** (X + 8) * rng.choice([-1, 1], 32)
+            elif kind == 1:    # rounding ties between neighbouring E4M3 values
+                i = rng.integers(0, 126, 32)
+                b[:] = 0.5 * (grid[i] + grid[i + 1]) * 2.0 ** X * rng.choice([-1, 1], 32)
+            elif kind == 2:    # saturation band 448 .. 480 (times 2^X)
+                b[:] = rng.uniform(440, 480, 32) * 2.0 ** X * rng.choice([-1, 1], 32)
+            else:              # exact grid values
+                b[:] = grid[rng.integers(0, 127, 32)] * 2.0 ** X * rng.choice([-1, 1], 32)
+            b[0] = 2.0 ** (X + 8) * 1.5  # pins the block maximum's binade at X + 8
+            blocks.append(b)
+    v = np.stack(blocks).astype(np.float32)  # fp32 rounding of each value
+    v[~np.isfinite(v)] = 0.0
+    v = v.reshape(-1, 64)  # two blocks per row
+    check(v.astype(np.float64), torch.from_numpy(np.ascontiguousarray(v)).cuda(), 1)
