@@ -199,7 +199,7 @@ size_t workspace_bytes(const mok_config& c, const Layout& L, size_t* parts) {
   const int64_t n_chunks_max = std::max<int64_t>(1, 24 * 1024 / c.num_experts);
   const size_t ce = ctx_elems(c, L);
   size_t p[SP_COUNT] = {
-      (size_t)n_chunks_max * E * 4 + (size_t)n_chunks_max * 4,
+      (size_t)n_chunks_max * E * 4,
       ce * 2,
       (size_t)(rowsR + Tm) * H * 2,
       (size_t)Tm * H + (size_t)Tm * (H / 32),
@@ -334,7 +334,6 @@ extern "C" mok_status mok_workspace_create(const mok_config* c, int device, mok_
   char* p = ws->scratch;
   ws->n_chunks_max = std::max<int64_t>(1, 24 * 1024 / c->num_experts);
   ws->chunk_hist = (int32_t*)p;
-  ws->chunk_invalid = (int32_t*)(p + (size_t)ws->n_chunks_max * c->num_experts * 4);
   p += parts[SP_SCHED];
   ws->hbuf = p;
   ws->hbuf_bytes = parts[SP_H];

@@ -14,9 +14,11 @@
 // LDS-DMA loads. Wave (wm = wave / 4, wn = wave % 4) owns 128 rows x 64
 // B-rows: 4 x 2 MFMA tiles of 32 x 32 (v_mfma_f32_32x32x16_bf16, or
 // v_mfma_scale_f32_32x32x64_f8f6f4 with per-lane E8M0 scales), 128 fp32
-// accumulators per lane. A wave whose 128 rows are all past the segment's
-// end (the ragged last tile of an expert) skips its MFMAs, so its SIMD runs
-// the partner wave at full rate. Workgroup b runs on XCD b % 8; tile ids are
+// accumulators per lane. In an expert's ragged last tile a wave runs only
+// the 32-row blocks that hold valid rows (the K loop is instantiated per
+// count of live blocks): a tile with 32 valid rows issues 1/8 of a full
+// tile's MFMAs and A-fragment reads, and a wave with no valid rows only
+// loads and waits, so its SIMD runs the partner wave at full rate. Workgroup b runs on XCD b % 8; tile ids are
 // split into 8 contiguous ranges so the tiles of one expert (which share
 // its weights) run on one XCD and hit its L2.
 //
@@ -390,8 +392,9 @@ grouped_gemm_nt(Params p) {
     const int K = MODE == BWD_DW ? t.kdim : k_of<MODE>(p, shared);
     const int Nd = MODE == BWD_DW ? (t.job == 0 ? Iv : p.H) : n_of<MODE>(p, shared);  // valid output columns
     const int rows_here = t.m_end - t.m0;
-    // this wave's 128 rows hold valid rows (uniform across the wave)
-    const bool wave_live = wm * 128 < rows_here;
+    // 32-row MFMA blocks of this wave's 128 rows that hold valid rows
+    // (uniform across the wave): 4 except in a segment's last tile
+    const int live_blocks = min(4, max(0, (rows_here - wm * 128 + 31) / 32));
 
     // ---- row metadata, one thread per tile row ----
     if (tid < BM) {
@@ -563,21 +566,25 @@ grouped_gemm_nt(Params p) {
 
     const int sw = swz(lr);  // rows read by this lane are lr mod 32
     auto b_row = [&](int j) { return MODE == GATE_UP ? j * 128 + wn * 32 : wn * 64 + j * 32; };
-    auto compute = [&](int stage) {
+    // NI = live 32-row blocks (compile time, so that a ragged tile's wave
+    // runs only its valid blocks' LDS reads and MFMAs without a per-block
+    // branch in the unrolled step)
+    auto compute = [&](auto ni_c, int stage) {
+      constexpr int NI = decltype(ni_c)::value;
       const uint8_t* As = &L.stage[stage][0];
       const uint8_t* Bs = As + A_BYTES;
       if constexpr (!FP8) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const int pc = ((2 * ks + lh) ^ sw) * 16;
-          bf16x8 fa[4], fb[2];
+          bf16x8 fa[NI], fb[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < NI; ++i)
             fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + i * 32 + lr) * ROWB + pc);
 #pragma unroll
           for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(Bs + (b_row(j) + lr) * ROWB + pc);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < NI; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
@@ -591,10 +598,10 @@ grouped_gemm_nt(Params p) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int p0 = ((4 * ks + lh) ^ sw) * 16, p1 = ((4 * ks + 2 + lh) ^ sw) * 16;
-          i32x8 fa[4], fb[2];
-          int sa[4], sbv[2];
+          i32x8 fa[NI], fb[2];
+          int sa[NI], sbv[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < NI; ++i) {
             const int row = wm * 128 + i * 32 + lr;
             const i32x4 lo = *reinterpret_cast<const i32x4*>(As + row * ROWB + p0);
             const i32x4 hi = *reinterpret_cast<const i32x4*>(As + row * ROWB + p1);
@@ -610,7 +617,7 @@ grouped_gemm_nt(Params p) {
             sbv[j] = Ss[SA_BYTES + row * 4 + 2 * ks + lh];
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < NI; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, sbv[j],
@@ -621,13 +628,23 @@ grouped_gemm_nt(Params p) {
 
     // ---- main loop: two stages, step kt+1 in flight while kt is consumed ----
     const int nk = K / KS;
-    wait_vmcnt<0>();  // stores of the previous tile's epilogue are older than these loads
-    if (nk > 0) issue(0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt<0>();
-      __syncthreads();  // every wave's loads of step kt landed; step kt-1's stage is free
-      if (kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
-      if (wave_live) compute(kt & 1);
+    auto k_loop = [&](auto ni_c) {
+      wait_vmcnt<0>();  // stores of the previous tile's epilogue are older than these loads
+      if (nk > 0) issue(0, 0);
+      for (int kt = 0; kt < nk; ++kt) {
+        wait_vmcnt<0>();
+        __syncthreads();  // every wave's loads of step kt landed; step kt-1's stage is free
+        if (kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
+        if constexpr (decltype(ni_c)::value > 0) compute(ni_c, kt & 1);
+      }
+    };
+    // every wave runs the same loads and barriers; only its MFMA blocks differ
+    switch (live_blocks) {
+      case 4: k_loop(std::integral_constant<int, 4>{}); break;
+      case 3: k_loop(std::integral_constant<int, 3>{}); break;
+      case 2: k_loop(std::integral_constant<int, 2>{}); break;
+      case 1: k_loop(std::integral_constant<int, 1>{}); break;
+      default: k_loop(std::integral_constant<int, 0>{}); break;
     }
 
     // ---- epilogue ----

@@ -129,7 +129,6 @@ struct mok_workspace {
   char* scratch = nullptr;
   size_t scratch_bytes = 0;
   int32_t* chunk_hist = nullptr;   // [n_chunks_max * E]
-  int32_t* chunk_invalid = nullptr;  // [n_chunks_max]
   int64_t n_chunks_max = 0;
   void* hbuf = nullptr;            // h (bf16) or MXFP8 h codes + scales when no context is kept
   size_t hbuf_bytes = 0;

@@ -82,6 +82,17 @@ def test_build_schedule_small_random(seed, mult, E, k, T):
     check(f, ref, T, k, E)
 
 
+@pytest.mark.parametrize("seed,mult", [(0, 1.0), (1, 0.05)])
+def test_build_schedule_max_experts_large_chunks(seed, mult):
+    # 1024 experts (the largest count) and 32000 assignments: the per-chunk
+    # histograms only fit the count pass's LDS with 2048-assignment chunks
+    E, k, T = 1024, 8, 4000
+    rng = np.random.default_rng(seed + 31)
+    top = rng.integers(-3, E + 3, size=(T, k)).astype(np.int64)
+    _, _, _, f, ref = run_case(top, E, mult)
+    check(f, ref, T, k, E)
+
+
 @pytest.mark.parametrize("mb", [1, 100, 512, 4096])
 def test_build_schedule_minibatches(mb):
     rng = np.random.default_rng(5)
