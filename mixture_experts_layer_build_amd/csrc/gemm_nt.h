@@ -216,7 +216,7 @@ grouped_gemm_nt(Params p) {
   const int ntw = n_tile_width<MODE>();
   const int nt_r = (n_of<MODE>(p, false) + ntw - 1) / ntw;
   const int nt_s = p.Is > 0 ? (n_of<MODE>(p, true) + ntw - 1) / ntw : 1;
-  // BWD_DW: per expert (the shared expert last) 3 jobs of tpj 256 x 256 tiles
+  // BWD_DW: per expert (the shared expert first) 3 jobs of tpj 256 x 256 tiles
   const int hb = (p.H + BM - 1) / BM;
   const int tpj_r = hb * ((p.I + BN - 1) / BN);
   const int tpj_s = hb * ((p.Is + BN - 1) / BN);
@@ -283,6 +283,41 @@ grouped_gemm_nt(Params p) {
     nf = min(TF, f0 + cfq) - f0;
     u0 = min(TT, xq * ctq);
     qlen = nf + min(TT, u0 + ctq) - u0;
+  } else if (MODE == BWD_DW) {
+    // A weight-gradient tile's work is its K: its expert's rows (the shared
+    // expert's are every token, several times a routed expert's). Ids run
+    // over the shared expert's tiles first (the longest ones start first),
+    // then the routed experts'; XCD xq takes the ids whose work starts in
+    // [xq W / nq, (xq + 1) W / nq), W = the total work, in 128-row blocks.
+    const int64_t units_r = 3LL * tpj_r;                 // tiles per routed expert
+    const int64_t sh_tiles = p.Is > 0 ? 3LL * tpj_s : 0;
+    const int64_t ks = tile_at(E + 1) - tile_at(E);     // the shared expert's K blocks
+    const int64_t Wsh = sh_tiles * ks;
+    const int64_t W = Wsh + units_r * tile_at(E);
+    // smallest id whose work starts at or after wpos (ntiles if none)
+    auto first_id = [&](int64_t wpos) -> int {
+      if (wpos <= 0) return 0;
+      if (wpos <= Wsh - ks) return (int)((wpos + ks - 1) / ks);  // a shared tile (ks > 0 here)
+      const int64_t wr = wpos - Wsh;
+      // routed expert e's last tile starts at units_r * tiles[e + 1] - kd(e),
+      // which does not decrease with e: the first e where that is >= wr
+      int lo = 0, hi = E;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const int64_t kd = tile_at(mid + 1) - tile_at(mid);
+        if (units_r * tile_at(mid + 1) - kd >= wr)
+          hi = mid;
+        else
+          lo = mid + 1;
+      }
+      if (lo >= E) return ntiles;
+      const int64_t kd = tile_at(lo + 1) - tile_at(lo);
+      const int64_t rel = wr - units_r * tile_at(lo);
+      const int64_t local = (kd == 0 || rel <= 0) ? 0 : (rel + kd - 1) / kd;
+      return (int)(sh_tiles + lo * units_r + local);
+    };
+    id0 = first_id(W * xq / nq);
+    qlen = (xq == nq - 1 ? ntiles : first_id(W * (xq + 1) / nq)) - id0;
   } else {
     const int chunk = (ntiles + nq - 1) / nq;
     id0 = min(ntiles, xq * chunk);
@@ -328,11 +363,11 @@ grouped_gemm_nt(Params p) {
       t.m_end = __builtin_amdgcn_readfirstlane(t.m_end);
       t.nt = __builtin_amdgcn_readfirstlane(t.nt);
     } else if constexpr (MODE == BWD_DW) {
-      const int n_routed = E * 3 * tpj_r;
-      const bool sh = id >= n_routed;
+      const int n_shared = p.Is > 0 ? 3 * tpj_s : 0;  // the shared expert's tiles come first
+      const bool sh = id < n_shared;
       const int tpj = sh ? tpj_s : tpj_r;
-      const int rem0 = sh ? id - n_routed : id % (3 * tpj_r);
-      t.e = sh ? -1 : id / (3 * tpj_r);
+      const int rem0 = sh ? id : (id - n_shared) % (3 * tpj_r);
+      t.e = sh ? -1 : (id - n_shared) / (3 * tpj_r);
       t.job = rem0 / tpj;
       const int tt = rem0 - t.job * tpj;
       const int Ivt = sh ? p.Is : p.I;
@@ -793,68 +828,90 @@ grouped_gemm_nt(Params p) {
       // MXFP8: h is the forward's E4M3 h (codes and block scales); dG and dU
       // are stored in fp32, so their two quantizations (along I for dA, along
       // rows for the weight gradients) start from the accumulator values.
+      // The wave's 128 x 64 tile is staged through LDS one 32-row block at a
+      // time (fp32), so that each lane then takes 8 consecutive columns of
+      // one row: the saved G, U, h reads and the dG, dU, hw writes of a wave
+      // instruction cover whole 128-byte lines of 8 rows.
+      constexpr int SWF = 64 + 4;  // staged row stride (floats)
+      float* reg = reinterpret_cast<float*>(&L.stage[0][0]) + wave * 32 * SWF;
       const int64_t sh = shared ? p.rows_cap_max * p.I : 0;
+      const int rr = lane >> 3, cc = (lane & 7) * 8;  // read-back: rows rr + 8 it, columns cc .. cc + 7
+      const int n = t.nt * BN + wn * 64 + cc;        // Nd is a multiple of 64: all 8 columns valid or none
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int ml = wm * 128 + i * 32 + lr;
-        const bool live = ml < rows_here;
-        const float w = L.row_w[ml];
-        const int64_t rowo = sh + (int64_t)(t.m0 + ml) * Nd;
-        float part = 0.f;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = t.nt * BN + wn * 64 + j * 32 + 8 * q + 4 * lh;
-            if (!live || n >= Nd) continue;
-            const uint2 gv = *reinterpret_cast<const uint2*>(p.g_in + rowo + n);
-            const uint2 uv = *reinterpret_cast<const uint2*>(p.u_in + rowo + n);
-            const uint32_t gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
-            uint32_t hw2[2] = {0, 0};
-            uint32_t hcodes = 0;
-            int hX = 0;
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(reg + lr * SWF + j * 32 + 8 * q + 4 * lh) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 2
+        for (int it = 0; it < 4; ++it) {
+          const int r = it * 8 + rr;
+          const int ml = wm * 128 + i * 32 + r;
+          const bool row_live = ml < rows_here;
+          float part = 0.f;
+          if (row_live && n < Nd) {
+            const float w = L.row_w[ml];
+            const int64_t rowo = sh + (int64_t)(t.m0 + ml) * Nd + n;
+            const float4 d0 = *reinterpret_cast<const float4*>(reg + r * SWF + cc);
+            const float4 d1 = *reinterpret_cast<const float4*>(reg + r * SWF + cc + 4);
+            const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            const uint4 gv = *reinterpret_cast<const uint4*>(p.g_in + rowo);
+            const uint4 uv = *reinterpret_cast<const uint4*>(p.u_in + rowo);
+            const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+            float h[8];
             if constexpr (FP8) {
-              // the forward's MXFP8 h: 4 codes and the scale of their block of 32
-              hcodes = *reinterpret_cast<const uint32_t*>(p.hq_in + rowo + n);
+              // the forward's MXFP8 h: 8 codes, all in one block of 32
+              const uint2 hc = *reinterpret_cast<const uint2*>(p.hq_in + rowo);
               const int64_t srow = (shared ? p.rows_cap_max * (p.I / 32) : 0) + (int64_t)(t.m0 + ml) * (Nd / 32);
-              hX = (int)p.hq_scale_in[srow + n / 32] - 127;
-            } else {
-              const uint2 hv = *reinterpret_cast<const uint2*>(p.h_in + rowo + n);
-              hw2[0] = hv.x;
-              hw2[1] = hv.y;
-            }
-            float dg[4], du[4], hwv[4];
+              const int hX = (int)p.hq_scale_in[srow + n / 32] - 127;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float g = (c & 1) ? u2f(gw[c >> 1] & 0xFFFF0000u) : u2f(gw[c >> 1] << 16);
-              const float u = (c & 1) ? u2f(uw[c >> 1] & 0xFFFF0000u) : u2f(uw[c >> 1] << 16);
-              const float h = FP8 ? e4m3_decode_scaled(hcodes >> (8 * c), hX)
-                                  : ((c & 1) ? u2f(hw2[c >> 1] & 0xFFFF0000u) : u2f(hw2[c >> 1] << 16));
-              const float d = acc[i][j][4 * q + c];
-              part += d * h;
-              const float dh = w * d;
-              const float s = sigmoid_f(g);
-              dg[c] = dh * u * s * (1.0f + g * (1.0f - s));
-              du[c] = dh * g * s;
-              hwv[c] = w * h;
-            }
-            if constexpr (FP8) {
-              *reinterpret_cast<float4*>(p.dg_out32 + rowo + n) = make_float4(dg[0], dg[1], dg[2], dg[3]);
-              *reinterpret_cast<float4*>(p.du_out32 + rowo + n) = make_float4(du[0], du[1], du[2], du[3]);
+              for (int c = 0; c < 8; ++c) h[c] = e4m3_decode_scaled((c < 4 ? hc.x : hc.y) >> (8 * (c & 3)), hX);
             } else {
-              *reinterpret_cast<uint2*>(p.dg_out + rowo + n) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-              *reinterpret_cast<uint2*>(p.du_out + rowo + n) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+              const uint4 hv = *reinterpret_cast<const uint4*>(p.h_in + rowo);
+              const uint32_t hw4[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+              for (int c = 0; c < 8; ++c) h[c] = (c & 1) ? u2f(hw4[c >> 1] & 0xFFFF0000u) : u2f(hw4[c >> 1] << 16);
             }
-            if (!FP8 && p.hw_out)
-              *reinterpret_cast<uint2*>(p.hw_out + rowo + n) =
-                  make_uint2(pack_bf16x2(hwv[0], hwv[1]), pack_bf16x2(hwv[2], hwv[3]));
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {  // two halves of 4 columns: fewer live registers
+              float dg[4], du[4], hwv[4];
+#pragma unroll
+              for (int c4 = 0; c4 < 4; ++c4) {
+                const int c = 4 * hh + c4;
+                const float g = (c & 1) ? u2f(gw[c >> 1] & 0xFFFF0000u) : u2f(gw[c >> 1] << 16);
+                const float u = (c & 1) ? u2f(uw[c >> 1] & 0xFFFF0000u) : u2f(uw[c >> 1] << 16);
+                part += d[c] * h[c];
+                const float dh = w * d[c];
+                const float sg = sigmoid_f(g);
+                dg[c4] = dh * u * sg * (1.0f + g * (1.0f - sg));
+                du[c4] = dh * g * sg;
+                hwv[c4] = w * h[c];
+              }
+              if constexpr (FP8) {
+                *reinterpret_cast<float4*>(p.dg_out32 + rowo + 4 * hh) = make_float4(dg[0], dg[1], dg[2], dg[3]);
+                *reinterpret_cast<float4*>(p.du_out32 + rowo + 4 * hh) = make_float4(du[0], du[1], du[2], du[3]);
+              } else {
+                *reinterpret_cast<uint2*>(p.dg_out + rowo + 4 * hh) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+                *reinterpret_cast<uint2*>(p.du_out + rowo + 4 * hh) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+                if (p.hw_out)
+                  *reinterpret_cast<uint2*>(p.hw_out + rowo + 4 * hh) =
+                      make_uint2(pack_bf16x2(hwv[0], hwv[1]), pack_bf16x2(hwv[2], hwv[3]));
+              }
+            }
           }
-        // the row's 64 columns of this wave: lanes lh = 0 and 1 hold halves
-        part += __shfl_xor(part, 32);
-        if (live && lh == 0) {
-          const int64_t prow = shared ? p.rows_cap_max + t.m0 + ml : t.m0 + ml;
-          p.dw_part[prow * p.dw_parts + t.nt * kDwPartsPerNTile + wn] = part;
+          // the row's 64 columns of this wave: 8 lanes of 8 columns
+          part += __shfl_xor(part, 1);
+          part += __shfl_xor(part, 2);
+          part += __shfl_xor(part, 4);
+          if (row_live && (lane & 7) == 0) {
+            const int64_t prow = shared ? p.rows_cap_max + t.m0 + ml : t.m0 + ml;
+            p.dw_part[prow * p.dw_parts + t.nt * kDwPartsPerNTile + wn] = part;
+          }
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
     }
     __syncthreads();  // row metadata and LDS stages are reused by the next tile
