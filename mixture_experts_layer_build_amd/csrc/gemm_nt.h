@@ -335,6 +335,28 @@ grouped_gemm_nt(Params p) {
     return lo;
   };
 
+  // When experts have many M tiles (at least kGroupM on average), tiles go
+  // in runs of kGroupM M tiles x all N tiles, M fastest: the tiles in flight
+  // together on one XCD share both operands' rows in its L2 (N fastest
+  // streams each weight N-tile once per M tile). With few M tiles per expert
+  // an XCD's round already spans whole experts and the natural order (N
+  // fastest) measured faster; the grad-out GEMM keeps it too (slower
+  // grouped at 32768 tokens). The weight gradients are always grouped.
+  const bool grp_order = MODE == BWD_DW || (MODE != BWD_DH && n_routed_mt >= kGroupM * E);
+  auto grouped = [&](int v, int n_m, int n_n, int& mi, int& ni) {
+    if (!grp_order) {
+      mi = v / n_n;
+      ni = v - mi * n_n;
+      return;
+    }
+    const int grp = v / (kGroupM * n_n);
+    const int base = grp * kGroupM;
+    const int gm = min(kGroupM, n_m - base);
+    const int r = v - grp * kGroupM * n_n;
+    mi = base + r % gm;
+    ni = r / gm;
+  };
+
   for (int q = slot; q < qlen; q += slots) {
     // ---- decode the tile ----
     Tile t;
@@ -344,8 +366,9 @@ grouped_gemm_nt(Params p) {
       const int v = full ? f0 + q : u0 + (q - nf);
       const int vr = full ? TFr : TTr;
       if (v < vr) {
-        const int mi = v / nt_r;
-        t.nt = v - mi * nt_r;
+        int mi, ni;
+        grouped(v, full ? L.fullp[E] : L.tailp[E], nt_r, mi, ni);
+        t.nt = ni;
         const int e = __builtin_amdgcn_readfirstlane(search(full ? L.fullp : L.tailp, mi));
         t.e = e;
         const int base = offset_at(e);
@@ -353,8 +376,9 @@ grouped_gemm_nt(Params p) {
         t.m0 = base + mt * BM;
         t.m_end = base + kept_at(e);
       } else {
-        const int mi = (v - vr) / nt_s;
-        t.nt = (v - vr) - mi * nt_s;
+        int mi, ni;
+        grouped(v - vr, full ? L.fullp[E + 1] - L.fullp[E] : L.tailp[E + 1] - L.tailp[E], nt_s, mi, ni);
+        t.nt = ni;
         t.e = -1;
         t.m0 = sh0 + (full ? mi : L.tiles[E + 1] - L.tiles[E] - 1) * BM;
         t.m_end = sh1;
@@ -373,13 +397,9 @@ grouped_gemm_nt(Params p) {
       const int Ivt = sh ? p.Is : p.I;
       const int nn = t.job == 0 ? (Ivt + BN - 1) / BN : hb;  // N tiles of the job
       const int nm = t.job == 0 ? hb : (Ivt + BM - 1) / BM;  // M tiles of the job
-      // grouped order: runs of kGroupM M tiles x all N tiles, M fastest, so
-      // the tiles in flight together share both operands' rows in L2
-      const int grp = tt / (kGroupM * nn);
-      const int gm = min(kGroupM, nm - grp * kGroupM);
-      const int rr = tt - grp * kGroupM * nn;
-      const int mt = grp * kGroupM + rr % gm;
-      t.nt = rr / gm;
+      int mt, ni;
+      grouped(tt, nm, nn, mt, ni);
+      t.nt = ni;
       t.m0 = mt * BM;
       t.m_end = t.job == 0 ? p.H : Ivt;
       const int k0t = sh ? tile_at(E) : tile_at(t.e);
@@ -396,8 +416,9 @@ grouped_gemm_nt(Params p) {
     } else {
       const int n_routed = n_routed_mt * nt_r;
       if (id < n_routed) {
-        const int mt = id / nt_r;
-        t.nt = id - mt * nt_r;
+        int mt, ni;
+        grouped(id, n_routed_mt, nt_r, mt, ni);
+        t.nt = ni;
         int lo = 0, hi = E;  // largest e with tiles[e] <= mt
         while (hi - lo > 1) {
           const int mid = (lo + hi) >> 1;
@@ -411,9 +432,9 @@ grouped_gemm_nt(Params p) {
         t.m0 = base + (mt - tile_at(t.e)) * BM;
         t.m_end = base + kept_at(t.e);
       } else {
-        const int sid = id - n_routed;
-        const int mt = sid / nt_s;
-        t.nt = sid - mt * nt_s;
+        int mt, ni;
+        grouped(id - n_routed, n_all_mt - n_routed_mt, nt_s, mt, ni);
+        t.nt = ni;
         t.e = -1;
         t.m0 = sh0 + mt * BM;
         t.m_end = sh1;
