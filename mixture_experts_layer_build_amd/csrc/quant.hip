@@ -211,18 +211,6 @@ __device__ __forceinline__ void tq_store(const float (*tile)[kTqLd], uint8_t* ou
   scale_row[b] = (uint8_t)(X + 127);
 }
 
-// The same tile transposed without quantization: thread (c, b) writes the 32
-// values of column c, rows 32b .. 32b+31, as bf16 (round to nearest even).
-__device__ __forceinline__ void tq_store_bf16(const float (*tile)[kTqLd], uint16_t* out_row) {
-  const int c = threadIdx.x >> 2, b = threadIdx.x & 3;
-  uint32_t w[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) w[i] = pack_bf16x2(tile[32 * b + 2 * i][c], tile[32 * b + 2 * i + 1][c]);
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    *reinterpret_cast<uint4*>(out_row + 32 * b + 8 * q) = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
-}
-
 __device__ __forceinline__ void bf16x32_to_tile(float (*tile)[kTqLd], int r, int half, const uint16_t* src, float mul) {
   // src: 32 consecutive bf16 values (64 bytes, 16-byte aligned), or nullptr for a zero row
 #pragma unroll
@@ -285,10 +273,10 @@ struct TqParams {
 
 // The weight-gradient GEMMs' operands: for expert e, rows of its segment in
 // 128-row blocks (rows past kept[e] are zero) -> [cols, K_e] elements at
-// 128 * tiles128[e] * cols_r, either MXFP8 (quantized along the rows, with
-// scales) or bf16 (OUT_BF16); the shared expert's all-token segment ->
-// [cols_s, K_s] at kr_cap * cols_r.
-template <int SRC, bool OUT_BF16>
+// 128 * tiles128[e] * cols_r, quantized to MXFP8 along the rows (with
+// scales); the shared expert's all-token segment -> [cols_s, K_s] at
+// kr_cap * cols_r.
+template <int SRC>
 __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
   __shared__ float tile[kTqRows][kTqLd];
   const int E = p.E;
@@ -375,10 +363,103 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
     const int64_t base = shared ? p.kr_cap * p.cols_r : kofs * cols;
     const int64_t sbase = shared ? p.kr_cap / 32 * p.cols_r : kofs / 32 * cols;
     const int64_t c = cc * kTqCols + (threadIdx.x >> 2);
-    if constexpr (OUT_BF16)
-      tq_store_bf16(tile, reinterpret_cast<uint16_t*>(p.dst) + base + c * Kp + (int64_t)kl * kTqRows);
-    else
-      tq_store(tile, p.dst + base + c * Kp + (int64_t)kl * kTqRows, p.dst_scale + sbase + c * (Kp / 32) + kl * 4);
+    tq_store(tile, p.dst + base + c * Kp + (int64_t)kl * kTqRows, p.dst_scale + sbase + c * (Kp / 32) + kl * 4);
+    __syncthreads();
+  }
+}
+
+// The BF16 weight gradients' operands: the same per-expert transposes
+// without quantization, as pure data movement. Tile: 128 segment rows x 128
+// columns. A thread loads 16 bytes (8 columns) from each of two adjacent
+// rows, for 4 row pairs (8 loads in flight); 16 lanes cover 256 contiguous
+// bytes of a row. LDS holds the tile column-major as dwords that pair rows
+// 2j and 2j + 1 (65 dwords per column: the writes are at most 2-way bank
+// conflicts, the reads none). A thread then writes 16 bytes (8 rows) of one
+// output row, 16 lanes per 256-byte run of it.
+constexpr int kTbRows = 128, kTbCols = 128, kTbLd = kTbRows / 2 + 1;
+
+template <int SRC>
+__global__ void __launch_bounds__(256) transpose_rows_bf16(TqParams p) {
+  __shared__ uint32_t tile[kTbCols][kTbLd];
+  const int E = p.E;
+  const int T = p.hdr[HDR_T];
+  const int nkb = p.tiles128[E + 1];
+  const int ncc = (max(p.cols_r, p.cols_s) + kTbCols - 1) / kTbCols;
+  const int64_t units = (int64_t)nkb * ncc;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cch = lane & 15, jq = lane >> 4;  // load phase: 8-column chunk, row pair within the wave's 4
+  const int m = threadIdx.x & 15;             // store phase: output rows' 8-element chunk
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int kb = (int)(u / ncc), cc = (int)(u - (int64_t)kb * ncc);
+    const bool shared = kb >= p.tiles128[E];
+    int e = E;
+    if (!shared) {
+      int lo = 0, hi = E;  // largest e with tiles128[e] <= kb
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.tiles128[mid] <= kb) lo = mid; else hi = mid;
+      }
+      e = lo;
+    }
+    const int cols = shared ? p.cols_s : p.cols_r;
+    if (cc * kTbCols >= cols) continue;  // uniform across the workgroup
+    const int kl = kb - p.tiles128[e];   // block index inside the segment
+    const int nrows = shared ? T : p.kept[e];
+    const int64_t row0 = shared ? 0 : p.offsets[e];
+    const int c0 = cc * kTbCols + 8 * cch;
+    const bool col_ok = c0 < cols;  // cols is a multiple of 64: a chunk is all in or all out
+    // source of segment row lr (nullptr: a zero row past the segment's end)
+    auto row_ptr = [&](int lr, float& mul) -> const uint16_t* {
+      mul = 1.0f;
+      if (lr >= nrows) return nullptr;
+      if (shared) return SRC == TQ_ROWS ? p.src + p.rows_cap_max * p.cols_r + (int64_t)lr * cols : p.src + (int64_t)lr * cols;
+      const int64_t row = row0 + lr;
+      if (SRC == TQ_ROWS) return p.src + row * cols;
+      const int a = p.row_src[row];
+      if (SRC == TQ_DY) mul = p.router_w[a];
+      return p.src + (int64_t)(a / p.k) * cols;
+    };
+    uint4 va[4], vb[4];
+    float ma[4], mb[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int j = it * 16 + wave * 4 + jq;  // row pair
+      const uint16_t* s0 = row_ptr(kl * kTbRows + 2 * j, ma[it]);
+      const uint16_t* s1 = row_ptr(kl * kTbRows + 2 * j + 1, mb[it]);
+      va[it] = (s0 && col_ok) ? *reinterpret_cast<const uint4*>(s0 + c0) : make_uint4(0, 0, 0, 0);
+      vb[it] = (s1 && col_ok) ? *reinterpret_cast<const uint4*>(s1 + c0) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int j = it * 16 + wave * 4 + jq;
+      const uint32_t a[4] = {va[it].x, va[it].y, va[it].z, va[it].w};
+      const uint32_t b[4] = {vb[it].x, vb[it].y, vb[it].z, vb[it].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {  // columns 8 cch + 2q and 8 cch + 2q + 1
+        uint32_t a0 = a[q] & 0xFFFFu, a1 = a[q] >> 16, b0 = b[q] & 0xFFFFu, b1 = b[q] >> 16;
+        if (SRC == TQ_DY) {  // router weight times grad_out, rounded to bf16 (nearest even)
+          a0 = f32_to_bf16(ma[it] * bf16_to_f32((uint16_t)a0));
+          a1 = f32_to_bf16(ma[it] * bf16_to_f32((uint16_t)a1));
+          b0 = f32_to_bf16(mb[it] * bf16_to_f32((uint16_t)b0));
+          b1 = f32_to_bf16(mb[it] * bf16_to_f32((uint16_t)b1));
+        }
+        tile[8 * cch + 2 * q][j] = a0 | (b0 << 16);
+        tile[8 * cch + 2 * q + 1][j] = a1 | (b1 << 16);
+      }
+    }
+    __syncthreads();
+    const int64_t Kp = 128 * (int64_t)(shared ? nkb - p.tiles128[E] : p.tiles128[e + 1] - p.tiles128[e]);
+    const int64_t kofs = shared ? 0 : 128 * (int64_t)p.tiles128[e];
+    uint16_t* dst = reinterpret_cast<uint16_t*>(p.dst) + (shared ? p.kr_cap * p.cols_r : kofs * cols);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int cl = it * 16 + (threadIdx.x >> 4);  // output row (source column) within the tile
+      const int cg = cc * kTbCols + cl;
+      const uint32_t* src = &tile[cl][4 * m];
+      if (cg < cols)
+        *reinterpret_cast<uint4*>(dst + (int64_t)cg * Kp + (int64_t)kl * kTbRows + 8 * m) =
+            make_uint4(src[0], src[1], src[2], src[3]);
+    }
     __syncthreads();
   }
 }
@@ -458,18 +539,18 @@ hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* 
   p.dst_scale = dst_scale;
   if (out_bf16) {
     switch (src_kind) {
-      case TQ_X: quant_t_rows<TQ_X, true><<<grid, 256, 0, s>>>(p); break;
-      case TQ_DY: quant_t_rows<TQ_DY, true><<<grid, 256, 0, s>>>(p); break;
-      case TQ_ROWS: quant_t_rows<TQ_ROWS, true><<<grid, 256, 0, s>>>(p); break;
+      case TQ_X: transpose_rows_bf16<TQ_X><<<grid, 256, 0, s>>>(p); break;
+      case TQ_DY: transpose_rows_bf16<TQ_DY><<<grid, 256, 0, s>>>(p); break;
+      case TQ_ROWS: transpose_rows_bf16<TQ_ROWS><<<grid, 256, 0, s>>>(p); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (src_kind) {
-      case TQ_X: quant_t_rows<TQ_X, false><<<grid, 256, 0, s>>>(p); break;
-      case TQ_DY: quant_t_rows<TQ_DY, false><<<grid, 256, 0, s>>>(p); break;
-      case TQ_ROWS: quant_t_rows<TQ_ROWS, false><<<grid, 256, 0, s>>>(p); break;
-      case TQ_ROWS32: quant_t_rows<TQ_ROWS32, false><<<grid, 256, 0, s>>>(p); break;
-      default: quant_t_rows<TQ_MX, false><<<grid, 256, 0, s>>>(p); break;
+      case TQ_X: quant_t_rows<TQ_X><<<grid, 256, 0, s>>>(p); break;
+      case TQ_DY: quant_t_rows<TQ_DY><<<grid, 256, 0, s>>>(p); break;
+      case TQ_ROWS: quant_t_rows<TQ_ROWS><<<grid, 256, 0, s>>>(p); break;
+      case TQ_ROWS32: quant_t_rows<TQ_ROWS32><<<grid, 256, 0, s>>>(p); break;
+      default: quant_t_rows<TQ_MX><<<grid, 256, 0, s>>>(p); break;
     }
   }
   return hipGetLastError();
