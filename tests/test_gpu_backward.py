@@ -46,6 +46,7 @@ SMALL = [
     ("no_shared", 200, 384, 320, 3, 2, 0, 1.0, False),
     ("many_experts", 513, 128, 64, 40, 4, 64, 1.0, True),
     ("deep", 130, 1024, 256, 4, 2, 512, 0.6, False),
+    ("deep_experts", 1100, 512, 192, 2, 2, 64, 1.0, False),  # grouped tile order
 ]
 
 

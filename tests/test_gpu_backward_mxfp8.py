@@ -62,6 +62,7 @@ SMALL = [
     ("no_shared", 200, 384, 256, 3, 2, 0, 1.0, False),
     ("many_experts", 513, 128, 128, 40, 4, 128, 1.0, True),
     ("deep", 130, 1024, 256, 4, 2, 512, 0.6, False),
+    ("deep_experts", 1100, 512, 256, 2, 2, 128, 1.0, False),  # grouped tile order
 ]
 
 

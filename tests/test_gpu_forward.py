@@ -49,6 +49,9 @@ SMALL = [
     ("many_experts", 513, 128, 64, 40, 4, 64, 1.0, True),
     ("one_expert", 260, 256, 128, 1, 1, 0, 1.0, False),
     ("deep_k", 130, 1024, 256, 4, 2, 512, 0.6, False),
+    # ~1100 rows per expert: 5 M tiles each, so the tile lists run in the
+    # grouped order (4 M tiles x all N tiles)
+    ("deep_experts", 1100, 512, 192, 2, 2, 64, 1.0, False),
 ]
 
 

@@ -55,6 +55,7 @@ SMALL = [
     ("drops_wide", 260, 384, 384, 4, 2, 0, 0.4),
     ("many_experts", 513, 128, 128, 40, 4, 128, 1.0),
     ("deep_k", 130, 1024, 256, 4, 2, 512, 1.0),
+    ("deep_experts", 1100, 512, 256, 2, 2, 128, 1.0),  # grouped tile order
 ]
 
 
