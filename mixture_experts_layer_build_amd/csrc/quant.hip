@@ -211,35 +211,42 @@ __device__ __forceinline__ void tq_store(const float (*tile)[kTqLd], uint8_t* ou
   scale_row[b] = (uint8_t)(X + 127);
 }
 
-__device__ __forceinline__ void bf16x32_to_tile(float (*tile)[kTqLd], int r, int half, const uint16_t* src, float mul) {
-  // src: 32 consecutive bf16 values (64 bytes, 16-byte aligned), or nullptr for a zero row
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint4 raw = src ? *reinterpret_cast<const uint4*>(src + 8 * q) : make_uint4(0, 0, 0, 0);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      tile[r][32 * half + 8 * q + 2 * j] = mul * u2f(w[j] << 16);
-      tile[r][32 * half + 8 * q + 2 * j + 1] = mul * u2f(w[j] & 0xFFFF0000u);
-    }
-  }
-}
-
 // Weights: src [B][R][C] bf16 -> dst codes [B][C][R], scales [B][C][R/32]
-// (R % 128 == 0, C % 64 == 0).
+// (R % 128 == 0, C % 64 == 0). The next unit's rows are loaded into
+// registers while the current unit is quantized and stored.
 __global__ void __launch_bounds__(256) quant_t_matrix(const uint16_t* __restrict__ src, int64_t B, int64_t R, int64_t C,
                                                       uint8_t* __restrict__ dst, uint8_t* __restrict__ dst_scale) {
   __shared__ float tile[kTqRows][kTqLd];
   const int64_t nkb = R / kTqRows, ncc = C / kTqCols;
   const int64_t units = B * nkb * ncc;
   const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
-  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+  auto fetch = [&](int64_t u, uint4 (&raw)[4]) {
     const int64_t b = u / (nkb * ncc);
     const int64_t rem = u - b * nkb * ncc;
     const int64_t kb = rem / ncc, cc = rem - kb * ncc;
     const uint16_t* s = src + b * R * C + (kb * kTqRows + r) * C + cc * kTqCols + 32 * half;
-    bf16x32_to_tile(tile, r, half, s, 1.0f);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) raw[q] = *reinterpret_cast<const uint4*>(s + 8 * q);
+  };
+  uint4 raw[4];
+  int64_t u = blockIdx.x;
+  if (u < units) fetch(u, raw);
+  for (; u < units; u += gridDim.x) {
+    float* trow = &tile[r][32 * half];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        trow[8 * q + 2 * j] = u2f(w[j] << 16);
+        trow[8 * q + 2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
+      }
+    }
     __syncthreads();
+    if (u + gridDim.x < units) fetch(u + gridDim.x, raw);
+    const int64_t b = u / (nkb * ncc);
+    const int64_t rem = u - b * nkb * ncc;
+    const int64_t kb = rem / ncc, cc = rem - kb * ncc;
     const int64_t c = cc * kTqCols + (threadIdx.x >> 2);
     tq_store(tile, dst + b * C * R + c * R + kb * kTqRows, dst_scale + b * C * (R / 32) + c * (R / 32) + kb * 4);
     __syncthreads();
@@ -285,11 +292,19 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
   const int ncc = (max(p.cols_r, p.cols_s) + kTqCols - 1) / kTqCols;
   const int64_t units = (int64_t)nkb * ncc;
   const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
-  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
-    const int kb = (int)(u / ncc), cc = (int)(u - (int64_t)kb * ncc);
-    const bool shared = kb >= p.tiles128[E];
+  // A unit (128-row block x 64 columns): its expert (E = the shared
+  // expert), column chunk and block inside the segment; live is false for a
+  // chunk past the expert's columns (uniform across the workgroup).
+  struct Unit {
+    int e, cc, kl, cols;
+    bool live;
+  };
+  auto place = [&](int64_t u) {
+    Unit w;
+    const int kb = (int)(u / ncc);
+    w.cc = (int)(u - (int64_t)kb * ncc);
     int e = E;
-    if (!shared) {
+    if (kb < p.tiles128[E]) {
       int lo = 0, hi = E;  // largest e with tiles128[e] <= kb
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -297,74 +312,107 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
       }
       e = lo;
     }
-    const int cols = shared ? p.cols_s : p.cols_r;
-    if (cc * kTqCols >= cols) continue;  // uniform across the workgroup
-    const int kl = kb - p.tiles128[e];    // block index inside the segment
-    const int lr = kl * kTqRows + r;      // row inside the segment
-    const int c0 = cc * kTqCols + 32 * half;
+    w.e = e;
+    w.cols = e == E ? p.cols_s : p.cols_r;
+    w.live = w.cc * kTqCols < w.cols;
+    w.kl = kb - p.tiles128[e];
+    return w;
+  };
+  // The thread's 32 source values of its row (row r of the block, columns
+  // 32 * half ..), held as loaded so that the next unit's loads are in
+  // flight while the current unit is quantized and stored.
+  constexpr int NV = SRC == TQ_ROWS32 ? 8 : SRC == TQ_MX ? 2 : 4;  // 16-byte loads
+  uint4 raw[NV];
+  float mul = 1.0f;
+  int X = 0;
+  bool have = false;
+  auto fetch = [&](const Unit& w) {
+    have = false;
+    mul = 1.0f;
+    if (!w.live) return;
+    const bool shared = w.e == E;
+    const int lr = w.kl * kTqRows + r;  // row inside the segment
+    const int c0 = w.cc * kTqCols + 32 * half;
+    const int nrows = shared ? T : p.kept[w.e];
+    if (lr >= nrows) return;  // zero row past the segment's end
+    const int64_t row = shared ? lr : p.offsets[w.e] + (int64_t)lr;
     if constexpr (SRC == TQ_ROWS32) {
-      const float* s = nullptr;
-      if (shared) {
-        if (lr < T) s = p.src32 + p.rows_cap_max * p.cols_r + (int64_t)lr * cols + c0;
-      } else if (lr < p.kept[e]) {
-        s = p.src32 + (p.offsets[e] + (int64_t)lr) * cols + c0;
-      }
-      float* trow = &tile[r][32 * half];
+      const float* s = p.src32 + (shared ? p.rows_cap_max * p.cols_r : 0) + row * w.cols + c0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float4 v = s ? *reinterpret_cast<const float4*>(s + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
-        trow[4 * q] = v.x;
-        trow[4 * q + 1] = v.y;
-        trow[4 * q + 2] = v.z;
-        trow[4 * q + 3] = v.w;
-      }
+      for (int q = 0; q < NV; ++q) raw[q] = *reinterpret_cast<const uint4*>(s + 4 * q);
     } else if constexpr (SRC == TQ_MX) {
-      int64_t ro = -1;
-      if (shared) {
-        if (lr < T) ro = lr;
-      } else if (lr < p.kept[e]) {
-        ro = p.offsets[e] + lr;
-      }
-      float* trow = &tile[r][32 * half];
-      if (ro >= 0) {
-        const int64_t code0 = shared ? p.rows_cap_max * p.cols_r + ro * cols : ro * cols;
-        const int64_t sc0 = shared ? p.rows_cap_max * (p.cols_r / 32) + ro * (cols / 32) : ro * (cols / 32);
-        const int X = (int)p.src_scale[sc0 + c0 / 32] - 127;
-        const uint4 q0 = *reinterpret_cast<const uint4*>(p.src_codes + code0 + c0);
-        const uint4 q1 = *reinterpret_cast<const uint4*>(p.src_codes + code0 + c0 + 16);
-        const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-        for (int i = 0; i < 32; ++i) trow[i] = e4m3_decode_scaled(w[i >> 2] >> (8 * (i & 3)), X);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) trow[i] = 0.f;
-      }
+      const int64_t code0 = shared ? p.rows_cap_max * p.cols_r + row * w.cols : row * w.cols;
+      const int64_t sc0 = shared ? p.rows_cap_max * (p.cols_r / 32) + row * (w.cols / 32) : row * (w.cols / 32);
+      X = (int)p.src_scale[sc0 + c0 / 32] - 127;
+      raw[0] = *reinterpret_cast<const uint4*>(p.src_codes + code0 + c0);
+      raw[1] = *reinterpret_cast<const uint4*>(p.src_codes + code0 + c0 + 16);
     } else {
-      const uint16_t* s = nullptr;
-      float mul = 1.0f;
+      const uint16_t* s;
       if (shared) {
-        if (lr < T) s = SRC == TQ_ROWS ? p.src + p.rows_cap_max * p.cols_r + (int64_t)lr * cols + c0
-                                       : p.src + (int64_t)lr * cols + c0;
-      } else if (lr < p.kept[e]) {
-        const int64_t row = p.offsets[e] + lr;
-        if (SRC == TQ_ROWS) {
-          s = p.src + row * cols + c0;
+        s = SRC == TQ_ROWS ? p.src + p.rows_cap_max * p.cols_r + row * w.cols + c0 : p.src + row * w.cols + c0;
+      } else if (SRC == TQ_ROWS) {
+        s = p.src + row * w.cols + c0;
+      } else {
+        const int a = p.row_src[row];
+        s = p.src + (int64_t)(a / p.k) * w.cols + c0;
+        if (SRC == TQ_DY) mul = p.router_w[a];
+      }
+#pragma unroll
+      for (int q = 0; q < NV; ++q) raw[q] = *reinterpret_cast<const uint4*>(s + 8 * q);
+    }
+    have = true;
+  };
+  // raw values -> fp32 in the LDS tile (zeros for a row past the segment)
+  auto stage = [&]() {
+    float* trow = &tile[r][32 * half];
+    if (!have) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) trow[i] = 0.f;
+      return;
+    }
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (SRC == TQ_ROWS32) {
+          trow[4 * q + j] = u2f(w[j]);
+        } else if constexpr (SRC == TQ_MX) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) trow[16 * q + 4 * j + b] = e4m3_decode_scaled(w[j] >> (8 * b), X);
         } else {
-          const int a = p.row_src[row];
-          s = p.src + (int64_t)(a / p.k) * cols + c0;
-          if (SRC == TQ_DY) mul = p.router_w[a];
+          trow[8 * q + 2 * j] = mul * u2f(w[j] << 16);
+          trow[8 * q + 2 * j + 1] = mul * u2f(w[j] & 0xFFFF0000u);
         }
       }
-      bf16x32_to_tile(tile, r, half, s, mul);
+    }
+  };
+  int64_t u = blockIdx.x;
+  Unit cur{};
+  if (u < units) {
+    cur = place(u);
+    fetch(cur);
+  }
+  for (; u < units; u += gridDim.x) {
+    if (cur.live) stage();
+    __syncthreads();
+    Unit nxt{};
+    if (u + gridDim.x < units) {
+      nxt = place(u + gridDim.x);
+      fetch(nxt);
+    }
+    if (cur.live) {
+      const bool shared = cur.e == E;
+      const int64_t Kp = 128 * (int64_t)(shared ? nkb - p.tiles128[E] : p.tiles128[cur.e + 1] - p.tiles128[cur.e]);
+      const int64_t kofs = shared ? 0 : 128 * (int64_t)p.tiles128[cur.e];
+      const int64_t base = shared ? p.kr_cap * p.cols_r : kofs * cur.cols;
+      const int64_t sbase = shared ? p.kr_cap / 32 * p.cols_r : kofs / 32 * cur.cols;
+      const int64_t c = cur.cc * kTqCols + (threadIdx.x >> 2);
+      tq_store(tile, p.dst + base + c * Kp + (int64_t)cur.kl * kTqRows,
+               p.dst_scale + sbase + c * (Kp / 32) + cur.kl * 4);
     }
     __syncthreads();
-    const int64_t Kp = 128 * (int64_t)(shared ? nkb - p.tiles128[E] : p.tiles128[e + 1] - p.tiles128[e]);
-    const int64_t kofs = shared ? 0 : 128 * (int64_t)p.tiles128[e];
-    const int64_t base = shared ? p.kr_cap * p.cols_r : kofs * cols;
-    const int64_t sbase = shared ? p.kr_cap / 32 * p.cols_r : kofs / 32 * cols;
-    const int64_t c = cc * kTqCols + (threadIdx.x >> 2);
-    tq_store(tile, p.dst + base + c * Kp + (int64_t)kl * kTqRows, p.dst_scale + sbase + c * (Kp / 32) + kl * 4);
-    __syncthreads();
+    cur = nxt;
   }
 }
 
