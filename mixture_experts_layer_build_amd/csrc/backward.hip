@@ -27,6 +27,7 @@
 //   dx        : fixed-order gather-sum of dA rows back to token order
 //   bwd_dw    : TN grouped GEMM, the three weight gradients per expert
 #include "device_common.h"
+#include "combine.h"
 #include "gemm_nt.h"
 #include "mok_internal.h"
 
@@ -81,47 +82,6 @@ __global__ void __launch_bounds__(256) reduce_dw(const int32_t* __restrict__ hdr
   }
 }
 
-// dx[t] = bf16(sum_j dA[slot_row[t, j]] + dA_shared[t]), fp32, slot order.
-__global__ void __launch_bounds__(256) gather_sum_rows(const int32_t* __restrict__ hdr, const int32_t* __restrict__ slot_row,
-                                                       const uint16_t* __restrict__ y, const uint16_t* __restrict__ y_shared,
-                                                       uint16_t* __restrict__ out, int H, int k) {
-  const int T = hdr[HDR_T];
-  const int nchunk = H / 8;
-  for (int t = blockIdx.x; t < T; t += gridDim.x) {
-    const int32_t* sl = slot_row + (int64_t)t * k;
-    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
-      float acc[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const int row = sl[j];
-        if (row < 0) continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)row * H + c * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += u2f(w[q] << 16);
-          acc[2 * q + 1] += u2f(w[q] & 0xFFFF0000u);
-        }
-      }
-      if (y_shared) {
-        const uint4 v = *reinterpret_cast<const uint4*>(y_shared + (int64_t)t * H + c * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += u2f(w[q] << 16);
-          acc[2 * q + 1] += u2f(w[q] & 0xFFFF0000u);
-        }
-      }
-      uint4 o;
-      o.x = pack_bf16x2(acc[0], acc[1]);
-      o.y = pack_bf16x2(acc[2], acc[3]);
-      o.z = pack_bf16x2(acc[4], acc[5]);
-      o.w = pack_bf16x2(acc[6], acc[7]);
-      *reinterpret_cast<uint4*>(out + (int64_t)t * H + c * 8) = o;
-    }
-  }
-}
 
 hipError_t transpose(const void* in, void* out, int nb, int R, int C, hipStream_t s) {
   if (nb == 0) return hipSuccess;
@@ -243,8 +203,8 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
     LaunchTimer tm(ws, MOK_K_BWD_DX_SUM, s);
     const int cgrid = (int)std::min<int64_t>(c.max_tokens, (int64_t)ws->num_cus * 8);
     const uint16_t* y = (const uint16_t*)ws->ybuf;
-    gather_sum_rows<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, Is > 0 ? y + rcm * H : nullptr,
-                                          (uint16_t*)g->dx, H, k);
+    sum_slot_rows<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, Is > 0 ? y + rcm * H : nullptr,
+                                        (uint16_t*)g->dx, H, k, 0, 0);
     MOK_HIP_TRY(hipGetLastError());
   }
   {
@@ -357,8 +317,8 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
     LaunchTimer tm(ws, MOK_K_BWD_DX_SUM, s);
     const int cgrid = (int)std::min<int64_t>(c.max_tokens, (int64_t)ws->num_cus * 8);
     const uint16_t* y = (const uint16_t*)ws->ybuf;
-    gather_sum_rows<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, Is > 0 ? y + rcm * H : nullptr,
-                                          (uint16_t*)g->dx, H, k);
+    sum_slot_rows<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, Is > 0 ? y + rcm * H : nullptr,
+                                        (uint16_t*)g->dx, H, k, 0, 0);
     MOK_HIP_TRY(hipGetLastError());
   }
   {

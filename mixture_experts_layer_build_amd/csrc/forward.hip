@@ -20,58 +20,11 @@
 //   combine : out[t] = bf16(sum over j in slot order of y[slot_row[t, j]]
 //             + y_shared[t]), fp32 accumulation, no atomics.
 #include "device_common.h"
+#include "combine.h"
 #include "gemm_nt.h"
 #include "mok_internal.h"
 
 namespace mok {
-namespace {
-
-// out[t] = bf16(sum_j y[slot_row[t*k + j]] (kept slots, slot order) + y_shared[t]),
-// for every token (mb == 0) or the tokens of minibatch mb_index.
-__global__ void __launch_bounds__(256) combine_bf16(const int32_t* __restrict__ hdr, const int32_t* __restrict__ slot_row,
-                                                    const uint16_t* __restrict__ y, const uint16_t* __restrict__ y_shared,
-                                                    uint16_t* __restrict__ out, int H, int k, int mb_index, int mb) {
-  const int T = hdr[HDR_T];
-  const int t0 = mb > 0 ? min(T, mb_index * mb) : 0;
-  const int t1 = mb > 0 ? min(T, t0 + mb) : T;
-  const int nchunk = H / 8;
-  for (int t = t0 + (int)blockIdx.x; t < t1; t += gridDim.x) {
-    const int32_t* sl = slot_row + (int64_t)t * k;
-    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
-      float acc[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const int row = sl[j];
-        if (row < 0) continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)row * H + c * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += u2f(w[q] << 16);
-          acc[2 * q + 1] += u2f(w[q] & 0xFFFF0000u);
-        }
-      }
-      if (y_shared) {
-        const uint4 v = *reinterpret_cast<const uint4*>(y_shared + (int64_t)t * H + c * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += u2f(w[q] << 16);
-          acc[2 * q + 1] += u2f(w[q] & 0xFFFF0000u);
-        }
-      }
-      uint4 o;
-      o.x = pack_bf16x2(acc[0], acc[1]);
-      o.y = pack_bf16x2(acc[2], acc[3]);
-      o.z = pack_bf16x2(acc[4], acc[5]);
-      o.w = pack_bf16x2(acc[6], acc[7]);
-      *reinterpret_cast<uint4*>(out + (int64_t)t * H + c * 8) = o;
-    }
-  }
-}
-
-}  // namespace
 
 static void fill_schedule(nt::Params& p, const mok_workspace* ws, const SchedView& v) {
   const mok_config& c = ws->cfg;
@@ -172,7 +125,7 @@ hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a
       MOK_HIP_TRY(hipGetLastError());
     }
     LaunchTimer tm(ws, MOK_K_COMBINE, s);
-    combine_bf16<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, ys, (uint16_t*)a.out, c.hidden, c.topk, 0, 0);
+    sum_slot_rows<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, ys, (uint16_t*)a.out, c.hidden, c.topk, 0, 0);
     MOK_HIP_TRY(hipGetLastError());
     return hipSuccess;
   }
@@ -204,7 +157,7 @@ hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a
     MOK_HIP_TRY(hipEventRecord(ws->mb_events[b], s));
     MOK_HIP_TRY(hipStreamWaitEvent(aux, ws->mb_events[b], 0));
     LaunchTimer tm(ws, MOK_K_COMBINE, aux);
-    combine_bf16<<<movers * 4, 256, 0, aux>>>(v.header, v.slot_row, y, ys, (uint16_t*)a.out, c.hidden, c.topk, b, mb);
+    sum_slot_rows<<<movers * 4, 256, 0, aux>>>(v.header, v.slot_row, y, ys, (uint16_t*)a.out, c.hidden, c.topk, b, mb);
     MOK_HIP_TRY(hipGetLastError());
   }
   MOK_HIP_TRY(hipEventRecord(ws->mb_events[n_mbq], aux));
