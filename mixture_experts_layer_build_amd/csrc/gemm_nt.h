@@ -237,7 +237,14 @@ grouped_gemm_nt(Params p) {
   const int nq = (gridDim.x % kNumXcd) == 0 ? kNumXcd : 1;
   const int xq = blockIdx.x % nq;
   const int slot = blockIdx.x / nq, slots = gridDim.x / nq;
-  const bool lpt = (MODE == GATE_UP || MODE == BWD_DH) && lds_tiles;
+  // experts with at least kGroupM M tiles on average
+  const bool deep = n_routed_mt >= kGroupM * E;
+  // longest-first lists: always for gate/up and dh; for down (not in a
+  // minibatch launch, whose rows are a minibatch's share) and dA when
+  // experts are deep, where the ragged tail tiles otherwise end the kernel
+  // unevenly (at shallow experts the natural order measured faster for them)
+  const bool lpt = lds_tiles && (MODE == GATE_UP || MODE == BWD_DH ||
+                                 (deep && (MODE == BWD_DX || (MODE == DOWN && p.mb == 0))));
   int TFr = 0, TF = 0, TTr = 0, TT = 0, f0 = 0, nf = 0, u0 = 0, qlen = 0, id0 = 0;
   if (lpt) {
     // counts of full and tail M tiles per expert (index E = shared expert),
@@ -342,7 +349,7 @@ grouped_gemm_nt(Params p) {
   // an XCD's round already spans whole experts and the natural order (N
   // fastest) measured faster; the grad-out GEMM keeps it too (slower
   // grouped at 32768 tokens). The weight gradients are always grouped.
-  const bool grp_order = MODE == BWD_DW || (MODE != BWD_DH && n_routed_mt >= kGroupM * E);
+  const bool grp_order = MODE == BWD_DW || (MODE != BWD_DH && deep);
   auto grouped = [&](int v, int n_m, int n_n, int& mi, int& ni) {
     if (!grp_order) {
       mi = v / n_n;
