@@ -80,6 +80,9 @@ def _stream() -> C.c_void_p:
     return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+_PLACEHOLDER: dict = {}
+
+
 def _ptr(t) -> C.c_void_p | None:
     if t is None:
         return None
@@ -87,6 +90,14 @@ def _ptr(t) -> C.c_void_p | None:
         raise ValueError("tensor must live on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
+    if t.numel() == 0:
+        # An empty batch: torch gives no storage (pointer 0), which the
+        # library rejects. The kernels read T = 0 from the schedule and never
+        # touch these buffers, so a small placeholder of the device stands in.
+        dev = t.device.index if t.device.index is not None else torch.cuda.current_device()
+        if dev not in _PLACEHOLDER:
+            _PLACEHOLDER[dev] = torch.zeros(64, dtype=torch.int32, device=t.device)
+        return C.c_void_p(_PLACEHOLDER[dev].data_ptr())
     return C.c_void_p(t.data_ptr())
 
 

@@ -1,0 +1,118 @@
+"""Edge cases of the whole path against the oracle: a batch smaller than the
+workspace's max_tokens (BF16 and MXFP8, forward and backward), an empty
+batch (no tokens: empty outputs, every weight gradient exactly zero), and
+router weights of zero (the output is the shared expert alone)."""
+import numpy as np
+import pytest
+
+from mokutil import TOL_BF16, TOL_MXFP8, assert_close_inf, f64, to_dev
+
+from oracle import moe as omoe
+from workloads import MoEShape, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import mixture_experts_layer_build_amd as mok  # noqa: E402
+
+
+def np64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def quantize_weights(wdev: dict) -> dict:
+    q = {}
+    for name, t in wdev.items():
+        codes, sc = mok.mxfp8_quantize(t.reshape(-1, t.shape[-1]), axis=1)
+        q[name] = codes.view(t.shape)
+        q[name + "_scale"] = sc
+    return q
+
+
+def run(c: MoEShape, inp: dict, T_max: int, mxfp8: bool):
+    d = to_dev(inp)
+    cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=T_max,
+                        shared_intermediate=c.I_s)
+    ws = mok.Workspace(cfg)
+    mode = mok.MOK_MODE_MXFP8 if mxfp8 else mok.MOK_MODE_BF16
+    sched = mok.build_schedule(ws, d["top_experts"])
+    ctx = torch.empty(mok.context_bytes(cfg, mode), dtype=torch.uint8, device="cuda")
+    w_fwd = quantize_weights(d["weights"]) if mxfp8 else d["weights"]
+    out = mok.forward(ws, sched, d["x"], d["router_weights"], w_fwd, mode=mode, context=ctx)
+    g = mok.backward(ws, sched, ctx, d["grad_out"], d["x"], d["router_weights"], d["weights"], mode=mode)
+    torch.cuda.synchronize()
+    return out, g
+
+
+@pytest.mark.parametrize("mxfp8", [False, True], ids=["bf16", "mxfp8"])
+def test_batch_smaller_than_max_tokens(mxfp8):
+    # 37 tokens in a workspace sized for 1000
+    c = MoEShape("small_batch", T=37, H=256, I=128, E=5, k=2, I_s=128, seed=41, w_std=0.05,
+                 mode="mxfp8" if mxfp8 else "bf16", passes="fwd+bwd")
+    inp = make_inputs(c)
+    out, g = run(c, inp, 1000, mxfp8)
+    args = (f64(inp["x"]), inp["top_experts"], inp["router_weights"], f64(inp["w_gate"]), f64(inp["w_up"]),
+            f64(inp["w_down"]), f64(inp["s_gate"]), f64(inp["s_up"]), f64(inp["s_down"]))
+    tol = TOL_MXFP8 if mxfp8 else TOL_BF16
+    ref_out = omoe.forward_mxfp8(*args) if mxfp8 else omoe.forward(*args)
+    assert_close_inf(np64(out), ref_out, tol, "out")
+    ref = omoe.backward_mxfp8(f64(inp["grad_out"]), *args) if mxfp8 else omoe.backward(f64(inp["grad_out"]), *args)
+    for gname, rname in [("dx", "dx"), ("d_router_weights", "d_router_weights"), ("d_routed_gate", "d_w_gate"),
+                         ("d_routed_up", "d_w_up"), ("d_routed_down", "d_w_down"), ("d_shared_gate", "d_s_gate"),
+                         ("d_shared_up", "d_s_up"), ("d_shared_down", "d_s_down")]:
+        assert_close_inf(np64(g[gname]), ref[rname], tol, gname)
+
+
+@pytest.mark.parametrize("mxfp8", [False, True], ids=["bf16", "mxfp8"])
+def test_empty_batch(mxfp8):
+    H, I, E, k, Is = 256, 128, 4, 2, 128
+    rng = np.random.default_rng(3)
+    dev = "cuda"
+    cfg = mok.MoKConfig(hidden=H, intermediate=I, num_experts=E, topk=k, max_tokens=64, shared_intermediate=Is)
+    ws = mok.Workspace(cfg)
+    mode = mok.MOK_MODE_MXFP8 if mxfp8 else mok.MOK_MODE_BF16
+    w = {"routed_gate": torch.from_numpy(rng.normal(0, 0.05, (E, I, H)).astype(np.float32)),
+         "routed_up": torch.from_numpy(rng.normal(0, 0.05, (E, I, H)).astype(np.float32)),
+         "routed_down": torch.from_numpy(rng.normal(0, 0.05, (E, H, I)).astype(np.float32)),
+         "shared_gate": torch.from_numpy(rng.normal(0, 0.05, (Is, H)).astype(np.float32)),
+         "shared_up": torch.from_numpy(rng.normal(0, 0.05, (Is, H)).astype(np.float32)),
+         "shared_down": torch.from_numpy(rng.normal(0, 0.05, (H, Is)).astype(np.float32))}
+    w = {n: t.to(torch.bfloat16).to(dev) for n, t in w.items()}
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+    top = torch.empty((0, k), dtype=torch.int64, device=dev)
+    rw = torch.empty((0, k), dtype=torch.float32, device=dev)
+    go = torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+    sched = mok.build_schedule(ws, top)
+    ctx = torch.empty(mok.context_bytes(cfg, mode), dtype=torch.uint8, device=dev)
+    out = mok.forward(ws, sched, x, rw, quantize_weights(w) if mxfp8 else w, mode=mode, context=ctx)
+    # gradient buffers start non-zero: the backward must write every element
+    grads = {"dx": torch.empty((0, H), dtype=torch.bfloat16, device=dev),
+             "d_router_weights": torch.empty((0, k), dtype=torch.float32, device=dev)}
+    for n, t in w.items():
+        grads["d_" + n] = torch.full_like(t, 7.0)
+    g = mok.backward(ws, sched, ctx, go, x, rw, w, mode=mode, grads=grads)
+    torch.cuda.synchronize()
+    assert out.shape == (0, H) and g["dx"].shape == (0, H) and g["d_router_weights"].shape == (0, k)
+    for n in w:
+        assert not torch.any(g["d_" + n] != 0), n
+
+
+def test_zero_router_weights_leave_the_shared_expert():
+    c = MoEShape("zero_w", T=300, H=256, I=128, E=6, k=3, I_s=128, seed=42, w_std=0.05)
+    inp = make_inputs(c)
+    inp["router_weights"] = np.zeros_like(inp["router_weights"])
+    d = to_dev(inp)
+    cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=c.T,
+                        shared_intermediate=c.I_s)
+    ws = mok.Workspace(cfg)
+    sched = mok.build_schedule(ws, d["top_experts"])
+    out = mok.forward(ws, sched, d["x"], d["router_weights"], d["weights"])
+    torch.cuda.synchronize()
+    ref = omoe.forward(f64(inp["x"]), inp["top_experts"], inp["router_weights"], f64(inp["w_gate"]),
+                       f64(inp["w_up"]), f64(inp["w_down"]), f64(inp["s_gate"]), f64(inp["s_up"]),
+                       f64(inp["s_down"]))
+    assert_close_inf(np64(out), ref, TOL_BF16, "out")
+    shared_only = omoe.forward(f64(inp["x"]), np.full_like(inp["top_experts"], -1), inp["router_weights"],
+                               f64(inp["w_gate"]), f64(inp["w_up"]), f64(inp["w_down"]), f64(inp["s_gate"]),
+                               f64(inp["s_up"]), f64(inp["s_down"]))
+    assert_close_inf(np64(out), shared_only, TOL_BF16, "shared only")
