@@ -29,11 +29,6 @@ typedef short i16x8v __attribute__((vector_size(16)));
 // with 64 banks, and 8 consecutive rows hit 8 distinct groups with 32.
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; }
 
-// The same for 64-byte rows (4 chunks): 16-byte reads of 16 consecutive rows
-// at one logical chunk hit 16 distinct bank groups with 64 banks, and 8
-// consecutive rows 8 distinct groups with 32.
-__device__ __forceinline__ int swz64(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
-
 // LDS byte address of a shared-memory object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -65,9 +60,8 @@ __device__ __forceinline__ void lds_dma16(i32x4v rs, uint32_t voff, uint32_t sof
                : "memory", "m0");
 }
 
-// 4 bytes per lane into LDS at m0 + 4 * lane. Used as an L2 prefetch: each
-// lane touches one cache line; the LDS bytes land in a scratch area nobody
-// reads.
+// 4 bytes per lane into LDS at m0 + 4 * lane (the MXFP8 block-scale dword
+// of one row per lane).
 __device__ __forceinline__ void lds_dma4(i32x4v rs, uint32_t voff, uint32_t soff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
                :
