@@ -242,7 +242,7 @@ def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sampl
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the all-to-all between GPUs is left out, "
+        print(json.dumps({"error": "this library runs on one GPU only: the all-to-all between GPUs is left out, "
                                    "so --gpus N with N > 1 is not supported"}))
         sys.exit(2)
     names = [n for n in CONFIGS] if a.all else [a.workload]
