@@ -636,11 +636,12 @@ grouped_gemm_nt(Params p) {
       constexpr int NI = decltype(ni_c)::value;
       const uint8_t* As = &L.stage[stage][0];
       const uint8_t* Bs = As + A_BYTES;
-      if constexpr (!FP8) {
+      if constexpr (!FP8 && MODE == BWD_DH) {
+        // (the dh epilogue leaves no registers for a second fragment set)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const int pc = ((2 * ks + lh) ^ sw) * 16;
-          bf16x8 fa[NI], fb[2];
+          bf16x8 fa[NI > 0 ? NI : 1], fb[2];
 #pragma unroll
           for (int i = 0; i < NI; ++i)
             fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + i * 32 + lr) * ROWB + pc);
@@ -651,6 +652,32 @@ grouped_gemm_nt(Params p) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        }
+      } else if constexpr (!FP8) {
+        // Fragments are double-buffered: sub-step ks + 1's LDS reads are
+        // issued before sub-step ks's MFMAs (the scheduling barriers keep
+        // that order), so the reads' latency overlaps the matrix work
+        // instead of stalling the wave between them.
+        bf16x8 fa[2][NI > 0 ? NI : 1], fb[2][2];
+        auto load_frags = [&](int ks, int buf) {
+          const int pc = ((2 * ks + lh) ^ sw) * 16;
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+            fa[buf][i] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + i * 32 + lr) * ROWB + pc);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) fb[buf][j] = *reinterpret_cast<const bf16x8*>(Bs + (b_row(j) + lr) * ROWB + pc);
+        };
+        load_frags(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          if (ks + 1 < 4) load_frags(ks + 1, (ks + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this sub-step's MFMAs
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       } else {
         // MFMA sub-step ks covers K bytes [64 ks, 64 ks + 64): lane bytes
