@@ -210,7 +210,7 @@ mok_status mok_workspace_destroy(mok_workspace* ws);
  * inverse, and per-minibatch sub-offsets. Deterministic: the same ids give
  * the same bytes ([R] "How MoK differs from a general MoE kernel library").
  * `schedule` is a device buffer of at least mok_schedule_bytes(cfg) bytes;
- * 0 <= T <= max_tokens. Runs 3 to 4 small kernels.
+ * 0 <= T <= max_tokens. Runs 2 small kernels (3 with more than one minibatch).
  */
 mok_status mok_build_schedule(mok_workspace* ws, const int64_t* top_experts, int64_t T,
                               void* schedule, size_t schedule_bytes, void* stream);
@@ -227,6 +227,9 @@ mok_status mok_build_schedule(mok_workspace* ws, const int64_t* top_experts, int
  * quantized along I before the down projection.
  * `context` (device, nullable, at least mok_context_bytes) receives the
  * activations mok_backward needs; pass NULL for inference.
+ * x, router_weights and out must be non-NULL even for an empty batch (the
+ * host cannot see T): with T = 0 they are never read or written, so any
+ * device address will do.
  */
 mok_status mok_forward(mok_workspace* ws, mok_mode mode, const void* schedule, size_t schedule_bytes,
                        const void* x, const float* router_weights, const mok_weights* weights,
@@ -242,7 +245,10 @@ mok_status mok_forward(mok_workspace* ws, mok_mode mode, const void* schedule, s
  * weight gradients' operands in 32-row blocks of each expert's rows), and
  * the context must come from an MXFP8 forward of the same schedule.
  * MXFP8 mode returns MOK_ERR_UNSUPPORTED unless H, I and I_s are multiples
- * of 128. Uses only the workspace's scratch (no allocation).
+ * of 128. Uses only the workspace's scratch (no allocation). Every weight
+ * gradient is written in full (zero for experts with no kept rows, and for
+ * all of them when T = 0); as in mok_forward, the token-sized pointers must
+ * be non-NULL even when T = 0.
  */
 mok_status mok_backward(mok_workspace* ws, mok_mode mode, const void* schedule, size_t schedule_bytes,
                         const void* context, size_t context_bytes, const void* grad_out, const void* x,
