@@ -299,7 +299,12 @@ typedef enum mok_kernel_id {
 } mok_kernel_id;
 
 const char* mok_kernel_name(int kernel_id);
+/* enable != 0: time every kernel; 0: none. */
 mok_status mok_workspace_set_timing(mok_workspace* ws, int enable);
+/* Time only the kernels whose bit (1 << mok_kernel_id) is set; 0 = none.
+ * Each timed launch records two events on its stream, a few microseconds
+ * each, so a measurement of the whole step times only what it needs. */
+mok_status mok_workspace_set_timing_mask(mok_workspace* ws, uint32_t kernel_mask);
 /* Waits for recorded events and returns, per kernel id, the summed
  * milliseconds and number of launches since the last reset; then resets. */
 mok_status mok_workspace_read_timing(mok_workspace* ws, float* total_ms, int64_t* launches, int n);

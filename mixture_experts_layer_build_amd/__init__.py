@@ -128,8 +128,19 @@ class Workspace:
             pass
 
     # per-kernel event timing (diagnostics)
-    def set_timing(self, on: bool) -> None:
-        _lib.check("mok_workspace_set_timing", lib().mok_workspace_set_timing(self.handle, int(on)))
+    def set_timing(self, on: bool, kernels=None) -> None:
+        """Time every kernel (on), none (off), or only the named ones
+        (kernels: names as mok_kernel_name gives them, e.g. "gate_up")."""
+        if kernels is None or not on:
+            _lib.check("mok_workspace_set_timing", lib().mok_workspace_set_timing(self.handle, int(on)))
+            return
+        ids = {lib().mok_kernel_name(i).decode(): i for i in range(_lib.KERNEL_COUNT)}
+        mask = 0
+        for name in kernels:
+            if name not in ids:
+                raise ValueError(f"unknown kernel name {name!r}")
+            mask |= 1 << ids[name]
+        _lib.check("mok_workspace_set_timing_mask", lib().mok_workspace_set_timing_mask(self.handle, mask))
 
     def read_timing(self) -> dict:
         n = _lib.KERNEL_COUNT

@@ -24,7 +24,7 @@ EXPORTS = (
     "mok_status_string", "mok_validate_config", "mok_schedule_bytes", "mok_schedule_layout_query",
     "mok_context_bytes", "mok_workspace_bytes", "mok_workspace_create", "mok_workspace_destroy",
     "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize", "mok_kernel_name",
-    "mok_workspace_set_timing", "mok_workspace_read_timing",
+    "mok_workspace_set_timing", "mok_workspace_set_timing_mask", "mok_workspace_read_timing",
 )
 
 HDR_FIELDS = ("T", "k", "E", "C", "P", "rows_cap", "n_mb", "minibatch", "dropped", "invalid",
@@ -98,6 +98,7 @@ def load() -> C.CDLL:
         "mok_mxfp8_quantize": (i32, [vp, i32, i64, i64, i64, i32, vp, i64, vp, vp]),
         "mok_kernel_name": (C.c_char_p, [i32]),
         "mok_workspace_set_timing": (i32, [vp, i32]),
+        "mok_workspace_set_timing_mask": (i32, [vp, C.c_uint32]),
         "mok_workspace_read_timing": (i32, [vp, C.POINTER(C.c_float), C.POINTER(i64), i32]),
     }
     for name, (res, args) in sig.items():

@@ -88,7 +88,7 @@ SchedView sched_view(void* base, const Layout& L) {
 }
 
 LaunchTimer::LaunchTimer(mok_workspace* w, int k, hipStream_t s) : ws(w), kernel(k), stream(s) {
-  if (!ws || !ws->timing) return;
+  if (!ws || k < 0 || k >= 32 || !((ws->timing_mask >> k) & 1u)) return;
   auto get = [&]() {
     hipEvent_t e = nullptr;
     if (!ws->event_pool.empty()) {
@@ -105,7 +105,7 @@ LaunchTimer::LaunchTimer(mok_workspace* w, int k, hipStream_t s) : ws(w), kernel
 }
 
 LaunchTimer::~LaunchTimer() {
-  if (!ws || !ws->timing || !a || !b) return;
+  if (!ws || !a || !b) return;
   (void)hipEventRecord(b, stream);
   ws->launches.push_back(TimedLaunch{kernel, a, b});
 }
@@ -578,7 +578,15 @@ extern "C" const char* mok_kernel_name(int id) {
 
 extern "C" mok_status mok_workspace_set_timing(mok_workspace* ws, int enable) {
   if (!ws) return MOK_ERR_INVALID_ARGUMENT;
-  ws->timing = enable != 0;
+  ws->timing_mask = enable != 0 ? (1u << MOK_K_COUNT) - 1u : 0u;
+  return MOK_OK;
+}
+
+static_assert(MOK_K_COUNT <= 32, "one mask bit per kernel id");
+
+extern "C" mok_status mok_workspace_set_timing_mask(mok_workspace* ws, uint32_t kernel_mask) {
+  if (!ws) return MOK_ERR_INVALID_ARGUMENT;
+  ws->timing_mask = kernel_mask & ((1u << MOK_K_COUNT) - 1u);
   return MOK_OK;
 }
 

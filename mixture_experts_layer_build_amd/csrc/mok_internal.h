@@ -144,7 +144,7 @@ struct mok_workspace {
   hipStream_t aux_stream = nullptr;
   std::vector<hipEvent_t> mb_events;  // one per minibatch (down done), then the join
   // timing
-  bool timing = false;
+  uint32_t timing_mask = 0;  // bit k: time launches of kernel id k
   std::vector<mok::TimedLaunch> launches;
   std::vector<hipEvent_t> event_pool;
 };
