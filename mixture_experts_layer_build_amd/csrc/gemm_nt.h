@@ -364,7 +364,17 @@ grouped_gemm_nt(Params p) {
     ni = r / gm;
   };
 
-  for (int q = slot; q < qlen; q += slots) {
+  // Gate/up's and dh's lists are longest first and end with their cheapest
+  // tiles, so after the complete rounds the last slots are the least loaded
+  // (they took tail tiles earliest): the last, partial round goes to them,
+  // slot slots - 1 first. BF16 only: in MXFP8 the extra index arithmetic
+  // cost more than the balance gained (gate/up measured slower), and other
+  // modes keep plain round-robin.
+  constexpr bool kRevLast = !FP8 && (MODE == GATE_UP || MODE == BWD_DH);
+  const int q_base = kRevLast ? qlen / slots * slots : 0;  // first position of the partial round
+  const int q_stop = kRevLast && lpt ? q_base + (slot >= slots - (qlen - q_base) ? slots : 0) : qlen;
+  for (int q0 = slot; q0 < q_stop; q0 += slots) {
+    const int q = (kRevLast && lpt && q0 >= q_base) ? q_base + slots - 1 - slot : q0;
     // ---- decode the tile ----
     Tile t;
     const int id = id0 + q;  // natural-order id (BWD_DW, or more experts than the LDS tables hold)
