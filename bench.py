@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="oracle chunk size; 0 = automatic")
     ap.add_argument("--all", action="store_true", help="one line per workload (diagnostics)")
+    ap.add_argument("--autograd", action="store_true",
+                    help="run the step through the torch.autograd layer (forward, then backward from "
+                         "grad_out for the training workloads) instead of the direct library calls")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain device-to-device copy of MIB MiB (a "
                          "known-size reference for the HBM byte counters of a profiler run)")
@@ -153,7 +156,7 @@ def copy_calibration(mib: int) -> None:
 
 
 def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sample_tokens: int,
-        minibatch: int = 0, movers: int = 0) -> dict:
+        minibatch: int = 0, movers: int = 0, use_autograd: bool = False) -> dict:
     import torch
     import mixture_experts_layer_build_amd as mok
 
@@ -162,7 +165,9 @@ def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sampl
     cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=c.T,
                         shared_intermediate=c.I_s, capacity_multiplier=mult, expert_pad=c.expert_pad,
                         minibatch_size=minibatch, num_mover_wgs=movers)
-    ws = mok.Workspace(cfg)
+    # the autograd layer takes its workspace from the per-config cache; the
+    # direct calls use one of their own
+    ws = mok.get_workspace(cfg) if use_autograd else mok.Workspace(cfg)
     mode = mok.MOK_MODE_MXFP8 if c.mode == "mxfp8" else mok.MOK_MODE_BF16
     training = c.passes != "fwd"
     ctx = torch.empty(mok.context_bytes(cfg, mode), dtype=torch.uint8, device="cuda") if training else None
@@ -187,6 +192,26 @@ def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sampl
         if training:
             grads = mok.backward(ws, sched, ctx, d["g"], d["x"], d["w"],
                                  bf16_weights if mode == mok.MOK_MODE_MXFP8 else weights, mode=mode, grads=grads)
+
+    if use_autograd:
+        from mixture_experts_layer_build_amd.autograd import MoKRuntime, moe_layer
+        rt = MoKRuntime(cfg, mode)
+        names = ("shared_gate", "shared_up", "shared_down", "routed_gate", "routed_up", "routed_down")
+        leaves = [d["x"], d["w"]] + [d["weights"].get(n) for n in names]
+        for t in leaves:
+            if t is not None:
+                t.requires_grad_(training)
+
+        def step():  # noqa: F811
+            # gradients start from None each step, as after an optimizer's
+            # zero_grad(set_to_none=True); the weights do not change, so in
+            # MXFP8 their quantized copies are reused
+            for t in leaves:
+                if t is not None:
+                    t.grad = None
+            y = moe_layer(rt, d["x"], d["w"], d["top"], *[d["weights"].get(n) for n in names])
+            if training:
+                y.backward(d["g"])
 
     for _ in range(warmup):
         step()
@@ -213,6 +238,8 @@ def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sampl
     breakdown = ws.read_timing()
     ws.set_timing(False)
 
+    if use_autograd:
+        mok.build_schedule(ws, d["top"], sched)
     fields = mok.schedule_fields(ws, sched)
     R_kept = kept_assignments(fields)
     fwd_flops = c.fwd_flops(kept_assignments=R_kept)
@@ -234,6 +261,7 @@ def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sampl
                    "topk": c.k, "shared_intermediate": c.I_s, "capacity_multiplier": mult,
                    "expert_pad": c.expert_pad, "passes": c.passes, "kept_assignments": R_kept,
                    "minibatch_size": minibatch, "num_mover_wgs": movers,
+                   "api": "torch.autograd layer" if use_autograd else "direct library calls",
                    "parallelism": "single GPU (one GPU's share; no all-to-all)"},
         "tflops": round(flops / (dt / steps) / 1e12, 2),
         "frac_of_peak_layer": round(flops / (dt / steps) / 1e12 / peak, 4),
@@ -263,7 +291,7 @@ def main():
         c = CONFIGS[n]
         mult = c.capacity_multiplier if a.mult is None else a.mult
         line = run(c, a.steps, a.warmup, mult, not a.no_cpu_baseline and not a.all, a.cpu_sample_tokens,
-                   a.minibatch, a.movers)
+                   a.minibatch, a.movers, a.autograd)
         print(json.dumps(line), flush=True)
     if a.copy_calibration:
         copy_calibration(a.copy_calibration)
