@@ -279,9 +279,9 @@ mok_status mok_mxfp8_quantize(const void* src, int src_is_fp32, int64_t rows, in
 /* Per-kernel event timing inside a workspace: when enabled, every launch
  * the workspace makes is bracketed by HIP events on the launch stream. */
 typedef enum mok_kernel_id {
-  MOK_K_SCHED_COUNT = 0, /* reserved: the count pass runs inside the scan kernel */
-  MOK_K_SCHED_SCAN,
-  MOK_K_SCHED_SCATTER,
+  MOK_K_SCHED_COUNT = 0, /* per-chunk expert histograms */
+  MOK_K_SCHED_SCAN,      /* reserved: the scans run inside the scatter kernel */
+  MOK_K_SCHED_SCATTER,   /* scans, ranks and permutation */
   MOK_K_SCHED_MINIBATCH,
   MOK_K_QUANT_X,
   MOK_K_GATE_UP,

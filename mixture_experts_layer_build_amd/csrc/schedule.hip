@@ -13,15 +13,19 @@
 // a = t*k + j are kept, later ones dropped; rows of an expert are in
 // ascending a; segments are padded to P rows.
 //
-// Two launches, each a streaming pass (no atomics on global memory, so the
-// bytes are identical from run to run):
-//   1. count+scan: one workgroup. All threads count the assignments into
-//      per-chunk histograms in LDS (LDS atomics: counts do not depend on
-//      order), then per-expert exclusive scans over chunks (chunk bases),
-//      counts, kept, padded offsets, tile prefix sums, header, padding rows.
-//   2. scatter: one wave per chunk: stable rank of each assignment inside its
-//      expert from a wave ballot match plus the chunk base, then the
-//      permutation (row_src) and its inverse (slot_row).
+// Two launches (no atomics on global memory, so the bytes are identical from
+// run to run):
+//   1. count: workgroup b counts the assignments of chunks [16 b, 16 b + 16)
+//      into per-chunk expert histograms in LDS (LDS atomics: counts do not
+//      depend on the order of the adds) and stores them.
+//   2. scan + scatter: every workgroup reads the whole chunk x expert table,
+//      derives per-expert totals, kept counts, padded offsets and the rank
+//      base of each of its 16 chunks itself (no grid-wide wait), then one
+//      wave per chunk ranks each assignment inside its expert from a wave
+//      ballot match plus that base and writes the permutation (row_src) and
+//      its inverse (slot_row). Workgroup 0 also writes counts, kept, offsets,
+//      tile prefix sums and the header; the padding rows are split over all
+//      workgroups.
 // (3. minibatch sub-offsets: binary search per (minibatch, expert); only
 //     when the schedule has more than one minibatch.)
 #include "device_common.h"
@@ -30,9 +34,12 @@
 namespace mok {
 namespace {
 
-constexpr int kWaves = 4;        // waves per workgroup in the scatter kernel
+constexpr int kWaves = 16;       // waves per workgroup in both passes
+constexpr int kThreads = kWaves * 64;
+constexpr int kCountChunks = 16; // chunks per workgroup in the count pass
+constexpr int kScatterChunks = 4;  // chunks per workgroup in the scatter pass: one wave each, one per SIMD
 constexpr int kMaxE = 1024;      // the largest expert count a workspace accepts
-constexpr int kCountBatch = 16;  // loads in flight per thread while counting
+constexpr int kCountBatch = 8;   // loads in flight per thread while counting
 constexpr int kScatterBatch = 8; // 64-assignment rounds loaded ahead per wave (divides iters)
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -64,84 +71,109 @@ struct SchedParams {
   int hash;
   int shared_rows;    // T if the shared expert exists, else 0
   SchedView v;
-  int32_t* chunk_hist;  // [n_chunks][E] chunk bases for the scatter
+  int32_t* chunk_hist;  // [n_chunks][E] per-chunk expert counts
 };
 
-// One workgroup of 1024 threads.
-__global__ void __launch_bounds__(1024) sched_count_scan(SchedParams p) {
-  extern __shared__ int32_t lds[];  // [n_chunks * E] per-chunk histograms, then chunk bases
-  __shared__ int32_t s_wtot[kNumTileBMs + 3][16];  // per-wave totals: scans, invalid, dropped
-  __shared__ int32_t s_tot[kNumTileBMs + 3];
-  __shared__ int32_t s_part[1024];  // chunk-run totals of the per-expert scan
-  __shared__ int32_t s_cnt[kMaxE];
-  __shared__ int32_t s_kept[kMaxE];
-  __shared__ int32_t s_off[kMaxE + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = p.E, NC = p.n_chunks;
-  int32_t* h = lds;
-  for (int i = tid; i < NC * E; i += 1024) h[i] = 0;
+// Pass 1. Workgroup b: histograms of chunks [kCountChunks b, kCountChunks (b + 1)).
+__global__ void __launch_bounds__(kThreads) sched_count(SchedParams p) {
+  extern __shared__ int32_t lds[];  // [kCountChunks][E]
+  const int tid = threadIdx.x, E = p.E;
+  const int c0 = blockIdx.x * kCountChunks;
+  const int nc = min(kCountChunks, p.n_chunks - c0);
+  for (int i = tid; i < nc * E; i += kThreads) lds[i] = 0;
   __syncthreads();
-  // count: thread tid takes assignments tid + 1024 j, kCountBatch loads ahead
-  int invalid = 0;
-  for (int64_t a0 = tid; a0 < p.n; a0 += (int64_t)1024 * kCountBatch) {
+  const int64_t a_lo = (int64_t)c0 << p.chunk_shift;
+  const int64_t a_hi = min(p.n, (int64_t)(c0 + nc) << p.chunk_shift);
+  for (int64_t a0 = a_lo + tid; a0 < a_hi; a0 += (int64_t)kThreads * kCountBatch) {
     int64_t ev[kCountBatch];
 #pragma unroll
     for (int u = 0; u < kCountBatch; ++u) {
-      const int64_t a = a0 + (int64_t)1024 * u;
-      ev[u] = a < p.n ? p.top[a] : 0;
+      const int64_t a = a0 + (int64_t)kThreads * u;
+      ev[u] = a < a_hi ? p.top[a] : -1;
     }
 #pragma unroll
     for (int u = 0; u < kCountBatch; ++u) {
-      const int64_t a = a0 + (int64_t)1024 * u;
-      if (a < p.n) {
-        if (ev[u] >= 0 && ev[u] < E)
-          atomicAdd(&h[(int)(a >> p.chunk_shift) * E + (int)ev[u]], 1);
-        else
-          ++invalid;
-      }
+      const int64_t a = a0 + (int64_t)kThreads * u;
+      if (a < a_hi && ev[u] >= 0 && ev[u] < E) atomicAdd(&lds[(int)((a - a_lo) >> p.chunk_shift) * E + (int)ev[u]], 1);
     }
   }
-  // per-expert exclusive scan over chunks (in LDS): G = p.scan_group runs of
-  // contiguous chunks per expert, run q of expert e on thread q * E + e (so a
-  // wave's lanes read consecutive experts of one chunk: no bank conflicts);
-  // the run totals, summed in order, give each run its base.
   __syncthreads();
+  for (int i = tid; i < nc * E; i += kThreads) p.chunk_hist[(int64_t)c0 * E + i] = lds[i];
+}
+
+// Pass 2. Workgroup b: the scans (every workgroup, all its waves), then the
+// scatter of chunks [kScatterChunks b, kScatterChunks (b + 1)), wave w < kScatterChunks
+// taking chunk kScatterChunks b + w (one scatter wave per SIMD).
+__global__ void __launch_bounds__(kThreads) sched_scan_scatter(SchedParams p, int nbits) {
+  extern __shared__ int32_t lds[];  // [E] segment offsets, then [kScatterChunks][E] running rank per expert
+  __shared__ int32_t s_part[kThreads];  // per chunk run: all chunks
+  __shared__ int32_t s_pre[kThreads];   // per chunk run: chunks before this workgroup's first
+  __shared__ int32_t s_cnt[kMaxE];
+  __shared__ int32_t s_base[kMaxE];
+  __shared__ int32_t s_wtot[kNumTileBMs + 3][kWaves];  // per-wave totals: scans, counts, dropped
+  __shared__ int32_t s_tot[kNumTileBMs + 3];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = p.E, NC = p.n_chunks;
+  const int c_first = blockIdx.x * kScatterChunks;
+  int32_t* offs = lds;
+  int32_t* run_all = lds + E;
+  // this workgroup's own chunk counts of expert tid (E <= kThreads), loaded
+  // first so that their latency overlaps the scan's loads
+  int own[kScatterChunks];
+#pragma unroll
+  for (int w = 0; w < kScatterChunks; ++w)
+    own[w] = (tid < E && c_first + w < NC) ? p.chunk_hist[(int64_t)(c_first + w) * E + tid] : 0;
+  // per-expert totals over all chunks and over the chunks before c_first:
+  // G = p.scan_group runs of contiguous chunks per expert, run q of expert e
+  // on thread q * E + e (a wave's lanes read consecutive experts of a chunk)
   {
+    constexpr int kB = 8;  // loads in flight per thread
     const int G = p.scan_group, part = tid / E, ge = tid - part * E;
-    const bool act = part < G;
     const int per = (NC + G - 1) / G;
-    const int c0 = min(NC, part * per), c1 = min(NC, c0 + per);
-    int run = 0;
-    if (act)
-      for (int c = c0; c < c1; ++c) run += h[c * E + ge];
-    s_part[tid] = run;
-    __syncthreads();
-    if (act) {
-      int base = 0;
-      for (int q = 0; q < part; ++q) base += s_part[q * E + ge];
-      if (part == G - 1) s_cnt[ge] = base + run;
-      for (int c = c0; c < c1; ++c) {
-        const int v = h[c * E + ge];
-        h[c * E + ge] = base;
-        base += v;
+    const int r0 = min(NC, part * per), r1 = part < G ? min(NC, r0 + per) : r0;
+    int tot = 0, pre = 0;
+    for (int c = r0; c < r1; c += kB) {
+      int v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) v[u] = c + u < r1 ? p.chunk_hist[(int64_t)(c + u) * E + ge] : 0;
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        tot += v[u];
+        pre += c + u < c_first ? v[u] : 0;
       }
+    }
+    s_part[tid] = tot;
+    s_pre[tid] = pre;
+    __syncthreads();
+    for (int e = tid; e < E; e += kThreads) {
+      int t = 0, b = 0;
+      for (int q = 0; q < G; ++q) {
+        t += s_part[q * E + e];
+        b += s_pre[q * E + e];
+      }
+      s_cnt[e] = t;
+      s_base[e] = b;
     }
   }
   __syncthreads();
-  // totals and kept, one expert per thread (E <= 1024)
-  const int e = tid;
-  int kept = 0, dropped = 0;
-  if (e < E) {
-    const int run = s_cnt[e];
-    kept = run < p.C ? run : p.C;
-    p.v.counts[e] = run;
-    p.v.kept[e] = kept;
-    s_kept[e] = kept;
-    dropped = run - kept;
+  // running rank of each expert at the start of each of this workgroup's chunks
+  if (tid < E) {
+    int acc = s_base[tid];
+#pragma unroll
+    for (int w = 0; w < kScatterChunks; ++w) {
+      run_all[w * E + tid] = acc;
+      acc += own[w];
+    }
   }
-  // exclusive scans over experts: padded rows, then tiles for each BM; plus
-  // the invalid and dropped totals. Wave scans, then one pass over the 16
-  // wave totals.
+  // kept, padded rows and tile counts per expert (one expert per thread,
+  // E <= 1024), exclusive scans over experts: wave scans, then one pass over
+  // the wave totals
+  const int e = tid;
+  int cnt = 0, kept = 0;
+  if (e < E) {
+    cnt = s_cnt[e];
+    kept = cnt < p.C ? cnt : p.C;
+  }
   const int padded = (kept + p.P - 1) / p.P * p.P;
   int val[1 + kNumTileBMs], incl[1 + kNumTileBMs];
 #pragma unroll
@@ -149,15 +181,15 @@ __global__ void __launch_bounds__(1024) sched_count_scan(SchedParams p) {
     val[q] = q == 0 ? padded : (padded + kTileBM[q - 1] - 1) / kTileBM[q - 1];
     incl[q] = wave_inclusive_scan(val[q], lane);
   }
-  const int inv_w = wave_sum(invalid), drop_w = wave_sum(dropped);
+  const int cnt_w = wave_sum(cnt), drop_w = wave_sum(cnt - kept);
   if (lane == 63) {
 #pragma unroll
     for (int q = 0; q < 1 + kNumTileBMs; ++q) s_wtot[q][wave] = incl[q];
-    s_wtot[1 + kNumTileBMs][wave] = inv_w;
+    s_wtot[1 + kNumTileBMs][wave] = cnt_w;
     s_wtot[2 + kNumTileBMs][wave] = drop_w;
   }
   __syncthreads();
-  for (int i = tid; i < NC * E; i += 1024) p.chunk_hist[i] = h[i];  // chunk bases for the scatter pass
+  const bool writer = blockIdx.x == 0;
 #pragma unroll
   for (int q = 0; q < 1 + kNumTileBMs; ++q) {
     int before = 0;
@@ -165,9 +197,9 @@ __global__ void __launch_bounds__(1024) sched_count_scan(SchedParams p) {
     const int excl = before + incl[q] - val[q];
     if (e < E) {
       if (q == 0) {
-        p.v.offsets[e] = excl;
-        s_off[e] = excl;
-      } else {
+        offs[e] = excl;
+        if (writer) p.v.offsets[e] = excl;
+      } else if (writer) {
         p.v.tiles[(q - 1) * (E + 2) + e] = excl;
       }
     }
@@ -176,61 +208,56 @@ __global__ void __launch_bounds__(1024) sched_count_scan(SchedParams p) {
 #pragma unroll
     for (int q = 0; q < 3 + kNumTileBMs; ++q) {
       int tot = 0;
-      for (int w = 0; w < 16; ++w) tot += s_wtot[q][w];
+      for (int w = 0; w < kWaves; ++w) tot += s_wtot[q][w];
       s_tot[q] = tot;
     }
   }
   __syncthreads();
-  const int invalid_total = s_tot[1 + kNumTileBMs], dropped_total = s_tot[2 + kNumTileBMs];
   const int total_rows = s_tot[0];
-  if (tid == 0) {
-    s_off[E] = total_rows;
-    p.v.offsets[E] = total_rows;
-    for (int q = 0; q < kNumTileBMs; ++q) {
-      const int bm = kTileBM[q];
-      p.v.tiles[q * (E + 2) + E] = s_tot[q + 1];
-      p.v.tiles[q * (E + 2) + E + 1] = s_tot[q + 1] + (p.shared_rows + bm - 1) / bm;
+  if (writer) {
+    if (e < E) {
+      p.v.counts[e] = cnt;
+      p.v.kept[e] = kept;
+      if (p.n_mb == 1) {  // single-minibatch sub-offsets: [offsets, offsets + kept]
+        p.v.mb_offsets[e] = offs[e];
+        p.v.mb_offsets[E + e] = offs[e] + kept;
+      }
     }
-    int32_t* hd = p.v.header;
-    hd[HDR_T] = p.T;
-    hd[HDR_K] = p.k;
-    hd[HDR_E] = E;
-    hd[HDR_C] = p.C;
-    hd[HDR_P] = p.P;
-    hd[HDR_ROWS_CAP] = p.rows_cap;
-    hd[HDR_NMB] = p.n_mb;
-    hd[HDR_MB] = p.mb;
-    hd[HDR_DROPPED] = dropped_total;
-    hd[HDR_INVALID] = invalid_total;
-    hd[HDR_ROWS_TOTAL] = total_rows;
-    hd[HDR_HASH] = p.hash;
-    for (int i = HDR_HASH + 1; i < HDR_INTS; ++i) hd[i] = 0;
+    if (tid == 0) {
+      p.v.offsets[E] = total_rows;
+      for (int q = 0; q < kNumTileBMs; ++q) {
+        const int bm = kTileBM[q];
+        p.v.tiles[q * (E + 2) + E] = s_tot[q + 1];
+        p.v.tiles[q * (E + 2) + E + 1] = s_tot[q + 1] + (p.shared_rows + bm - 1) / bm;
+      }
+      int32_t* hd = p.v.header;
+      hd[HDR_T] = p.T;
+      hd[HDR_K] = p.k;
+      hd[HDR_E] = E;
+      hd[HDR_C] = p.C;
+      hd[HDR_P] = p.P;
+      hd[HDR_ROWS_CAP] = p.rows_cap;
+      hd[HDR_NMB] = p.n_mb;
+      hd[HDR_MB] = p.mb;
+      hd[HDR_DROPPED] = s_tot[2 + kNumTileBMs];
+      hd[HDR_INVALID] = (int)(p.n - s_tot[1 + kNumTileBMs]);  // assignments no expert counted
+      hd[HDR_ROWS_TOTAL] = total_rows;
+      hd[HDR_HASH] = p.hash;
+      for (int i = HDR_HASH + 1; i < HDR_INTS; ++i) hd[i] = 0;
+    }
   }
-  __syncthreads();
-  // padding rows of every segment, and unused rows up to rows_cap(T), get -1
-  if (e < E) {
-    const int lo = s_off[e] + s_kept[e], hi = s_off[e + 1];
-    for (int r = lo; r < hi; ++r) p.v.row_src[r] = -1;
+  // padding rows of every segment (experts split over the workgroups), and
+  // unused rows up to rows_cap(T), get -1
+  if (e < E && e % gridDim.x == blockIdx.x) {
+    const int hi = e + 1 < E ? offs[e + 1] : total_rows;
+    for (int r = offs[e] + kept; r < hi; ++r) p.v.row_src[r] = -1;
   }
-  for (int r = total_rows + tid; r < p.rows_cap; r += 1024) p.v.row_src[r] = -1;
-  // single-minibatch sub-offsets: [offsets, offsets + kept]
-  if (p.n_mb == 1 && e < E) {
-    p.v.mb_offsets[e] = s_off[e];
-    p.v.mb_offsets[E + e] = s_off[e] + s_kept[e];
-  }
-}
-
-__global__ void __launch_bounds__(256) sched_scatter(SchedParams p, int nbits) {
-  extern __shared__ int32_t lds[];  // [E] segment offsets, then [kWaves][E] running rank per expert
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int chunk = blockIdx.x * kWaves + wave;
-  int32_t* offs = lds;
-  int32_t* run = lds + p.E + wave * p.E;
-  for (int e = threadIdx.x; e < p.E; e += 256) offs[e] = p.v.offsets[e];
-  if (chunk < p.n_chunks)
-    for (int e = lane; e < p.E; e += 64) run[e] = p.chunk_hist[(int64_t)chunk * p.E + e];
-  __syncthreads();
-  if (chunk >= p.n_chunks) return;  // whole waves exit together; no block barrier below
+  for (int r = total_rows + blockIdx.x * kThreads + tid; r < p.rows_cap; r += gridDim.x * kThreads)
+    p.v.row_src[r] = -1;
+  // scatter: wave w ranks chunk c_first + w
+  const int chunk = c_first + wave;
+  if (wave >= kScatterChunks || chunk >= NC) return;  // whole waves exit; no barrier below
+  int32_t* run = run_all + wave * E;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int64_t base = (int64_t)chunk * p.iters * 64;
   for (int it0 = 0; it0 < p.iters; it0 += kScatterBatch) {
@@ -244,27 +271,27 @@ __global__ void __launch_bounds__(256) sched_scatter(SchedParams p, int nbits) {
 #pragma unroll
     for (int u = 0; u < kScatterBatch; ++u) {
       const int64_t a = base + (int64_t)(it0 + u) * 64 + lane;
-      const int e = ev[u];
-      const bool valid = e >= 0;
+      const int ex = ev[u];
+      const bool valid = ex >= 0;
       // lanes holding the same expert id: intersect ballots bit by bit
       uint64_t same = ballot64(valid);
       for (int b = 0; b < nbits; ++b) {
-        const bool bit = valid && ((e >> b) & 1);
+        const bool bit = valid && ((ex >> b) & 1);
         const uint64_t m = ballot64(bit);
         same &= bit ? m : ~m;
       }
       int q = 0;
-      if (valid) q = run[e] + __popcll(same & lt_mask);
+      if (valid) q = run[ex] + __popcll(same & lt_mask);
       __builtin_amdgcn_wave_barrier();
       // the highest lane of each group advances that expert's running count
       const bool last = valid && ((same >> lane) == 1ull);
-      if (last) run[e] = q + 1;
+      if (last) run[ex] = q + 1;
       __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_wave_barrier();
       if (a < p.n) {
         int slot = -1;
         if (valid && q < p.C) {
-          const int row = offs[e] + q;
+          const int row = offs[ex] + q;
           p.v.row_src[row] = (int32_t)a;
           slot = row;
         }
@@ -311,10 +338,11 @@ hipError_t launch_schedule(mok_workspace* ws, const int64_t* top, int64_t T, voi
   p.shared_rows = c.shared_intermediate > 0 ? (int)T : 0;
   p.v = sched_view(sched, ws->layout);
   p.chunk_hist = ws->chunk_hist;
-  // chunk size: keep n_chunks * E within the count+scan kernel's LDS budget
-  const int64_t lds_ints = 24 * 1024;
+  // chunk size: n_chunks * E within the workspace's chunk table (and each
+  // scan thread's share of it small)
+  const int64_t table_ints = 24 * 1024;
   int iters = kScatterBatch;
-  while ((p.n + iters * 64 - 1) / (iters * 64) * (int64_t)p.E > lds_ints) iters *= 2;
+  while ((p.n + iters * 64 - 1) / (iters * 64) * (int64_t)p.E > table_ints) iters *= 2;
   p.iters = iters;
   p.chunk_shift = 6;
   while ((1 << p.chunk_shift) < iters * 64) ++p.chunk_shift;
@@ -325,15 +353,18 @@ hipError_t launch_schedule(mok_workspace* ws, const int64_t* top, int64_t T, voi
   while (p.scan_group < 64 && p.scan_group * 2 * p.E <= 1024) p.scan_group *= 2;
   int nbits = 0;
   while ((1 << nbits) < p.E) ++nbits;
-  {
-    LaunchTimer t(ws, MOK_K_SCHED_SCAN, s);
-    sched_count_scan<<<1, 1024, (size_t)p.n_chunks * p.E * sizeof(int32_t), s>>>(p);
+  const int count_groups = (p.n_chunks + kCountChunks - 1) / kCountChunks;
+  const int scatter_groups = (p.n_chunks + kScatterChunks - 1) / kScatterChunks;
+  if (count_groups > 0) {
+    LaunchTimer t(ws, MOK_K_SCHED_COUNT, s);
+    sched_count<<<count_groups, kThreads, (size_t)kCountChunks * p.E * sizeof(int32_t), s>>>(p);
     MOK_HIP_TRY(hipGetLastError());
   }
-  if (p.n_chunks > 0) {
+  {
+    // at least one workgroup: an empty batch still gets its header
     LaunchTimer t(ws, MOK_K_SCHED_SCATTER, s);
-    const int grid_w = (p.n_chunks + kWaves - 1) / kWaves;
-    sched_scatter<<<grid_w, 256, (size_t)(kWaves + 1) * p.E * sizeof(int32_t), s>>>(p, nbits);
+    sched_scan_scatter<<<scatter_groups > 0 ? scatter_groups : 1, kThreads,
+                         (size_t)(kScatterChunks + 1) * p.E * sizeof(int32_t), s>>>(p, nbits);
     MOK_HIP_TRY(hipGetLastError());
   }
   if (p.n_mb > 1) {
