@@ -46,6 +46,12 @@ constexpr int kMaxLdsE = 256;  // schedules with more experts search the tile ta
 constexpr int kGroupM = 4;  // BWD_DW tile order: 4 M tiles per group
 constexpr int kDwPartsPerNTile = 4;  // partial router-weight gradients per N tile (one per wave column)
 constexpr uint32_t kOff = 0x80000000u;  // offset past every resource: loads return 0
+// Short tiles (at most SHORT_ROWS valid rows: an expert's ragged last tile)
+// run their K loop on a ring of three compact stages, A SHORT_ROWS rows then
+// B BN rows each, so that two steps are in flight instead of one.
+constexpr int SHORT_ROWS = 64;
+constexpr int SHORT_SLOT = (SHORT_ROWS + BN) * ROWB;  // 40 KiB
+static_assert(3 * SHORT_SLOT <= NSTAGE * (A_BYTES + B_BYTES), "three short stages fit the two full ones");
 
 enum Mode : int {
   GATE_UP = 0,  // A = tokens of x, B = gate | up rows, epilogue h = silu(g) * u
@@ -642,10 +648,8 @@ grouped_gemm_nt(Params p) {
     // NI = live 32-row blocks (compile time, so that a ragged tile's wave
     // runs only its valid blocks' LDS reads and MFMAs without a per-block
     // branch in the unrolled step)
-    auto compute = [&](auto ni_c, int stage) {
+    auto compute = [&](auto ni_c, int stage, const uint8_t* As, const uint8_t* Bs) {
       constexpr int NI = decltype(ni_c)::value;
-      const uint8_t* As = &L.stage[stage][0];
-      const uint8_t* Bs = As + A_BYTES;
       if constexpr (!FP8 && MODE == BWD_DH) {
         // (the dh epilogue leaves no registers for a second fragment set)
 #pragma unroll
@@ -735,16 +739,63 @@ grouped_gemm_nt(Params p) {
         wait_vmcnt<0>();
         __syncthreads();  // every wave's loads of step kt landed; step kt-1's stage is free
         if (kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
-        if constexpr (decltype(ni_c)::value > 0) compute(ni_c, kt & 1);
+        if constexpr (decltype(ni_c)::value > 0) {
+          const uint8_t* As = &L.stage[kt & 1][0];
+          compute(ni_c, kt & 1, As, As + A_BYTES);
+        }
+      }
+    };
+    // Short tiles: three compact stages, steps kt+1 and kt+2 in flight while
+    // kt is consumed. Each wave loads 8 of the SHORT_ROWS A rows and its 32 B
+    // rows (5 instructions a step), so "step kt landed" is vmcnt <= 5 while
+    // step kt+1's loads are outstanding.
+    constexpr bool kShortRing = !FP8 && MODE == GATE_UP;
+    auto k_loop_short = [&](auto ni_c) {
+      const int arow = 8 * wave + dr;
+      const int asrc = L.row_src[arow];
+      const uint32_t a_off_s = asrc >= 0 ? (uint32_t)asrc * a_row_bytes + 16u * (uint32_t)(dp ^ swz(arow)) : kOff;
+      auto issue_s = [&](int slot, int kstep) {
+        const uint32_t kb = (uint32_t)(kstep * KS) * ES;
+        const uint32_t sbase = lds0 + (uint32_t)slot * SHORT_SLOT;
+        lds_dma16(rs_a, a_off_s, kb, sbase + (uint32_t)(8 * wave) * ROWB);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          lds_dma16(rs_b, b_off[i], kb, sbase + SHORT_ROWS * ROWB + (uint32_t)(32 * wave + 8 * i) * ROWB);
+      };
+      wait_vmcnt<0>();  // stores of the previous tile's epilogue are older than these loads
+      if (nk > 0) issue_s(0, 0);
+      if (nk > 1) issue_s(1, 1);
+      int slot = 0;
+      for (int kt = 0; kt < nk; ++kt) {
+        if (kt + 1 < nk)
+          wait_vmcnt<5>();
+        else
+          wait_vmcnt<0>();
+        __syncthreads();  // every wave's loads of step kt landed; step kt-1's stage is free
+        if (kt + 2 < nk) issue_s(slot == 0 ? 2 : slot - 1, kt + 2);
+        if constexpr (decltype(ni_c)::value > 0) {
+          const uint8_t* As = &L.stage[0][0] + slot * SHORT_SLOT;
+          compute(ni_c, 0, As, As + SHORT_ROWS * ROWB);
+        }
+        slot = slot == 2 ? 0 : slot + 1;
       }
     };
     // every wave runs the same loads and barriers; only its MFMA blocks differ
-    switch (live_blocks) {
-      case 4: k_loop(std::integral_constant<int, 4>{}); break;
-      case 3: k_loop(std::integral_constant<int, 3>{}); break;
-      case 2: k_loop(std::integral_constant<int, 2>{}); break;
-      case 1: k_loop(std::integral_constant<int, 1>{}); break;
-      default: k_loop(std::integral_constant<int, 0>{}); break;
+    if (kShortRing && rows_here <= SHORT_ROWS) {
+      // wave rows 0-127 hold at most 2 live blocks, rows 128-255 none
+      switch (live_blocks) {
+        case 2: k_loop_short(std::integral_constant<int, 2>{}); break;
+        case 1: k_loop_short(std::integral_constant<int, 1>{}); break;
+        default: k_loop_short(std::integral_constant<int, 0>{}); break;
+      }
+    } else {
+      switch (live_blocks) {
+        case 4: k_loop(std::integral_constant<int, 4>{}); break;
+        case 3: k_loop(std::integral_constant<int, 3>{}); break;
+        case 2: k_loop(std::integral_constant<int, 2>{}); break;
+        case 1: k_loop(std::integral_constant<int, 1>{}); break;
+        default: k_loop(std::integral_constant<int, 0>{}); break;
+      }
     }
 
     // ---- epilogue ----
