@@ -48,10 +48,13 @@ constexpr int kDwPartsPerNTile = 4;  // partial router-weight gradients per N ti
 constexpr uint32_t kOff = 0x80000000u;  // offset past every resource: loads return 0
 // Short tiles (at most SHORT_ROWS valid rows: an expert's ragged last tile)
 // run their K loop on a ring of three compact stages, A SHORT_ROWS rows then
-// B BN rows each, so that two steps are in flight instead of one.
+// B BN rows each (and their MXFP8 scale dwords), so that two steps are in
+// flight instead of one.
 constexpr int SHORT_ROWS = 64;
 constexpr int SHORT_SLOT = (SHORT_ROWS + BN) * ROWB;  // 40 KiB
+constexpr int SHORT_SSLOT = (SHORT_ROWS + BN) * 4;    // 1280 bytes of scales
 static_assert(3 * SHORT_SLOT <= NSTAGE * (A_BYTES + B_BYTES), "three short stages fit the two full ones");
+static_assert(3 * SHORT_SSLOT <= NSTAGE * (SA_BYTES + SB_BYTES), "and their scales the two full ones'");
 
 enum Mode : int {
   GATE_UP = 0,  // A = tokens of x, B = gate | up rows, epilogue h = silu(g) * u
@@ -648,7 +651,8 @@ grouped_gemm_nt(Params p) {
     // NI = live 32-row blocks (compile time, so that a ragged tile's wave
     // runs only its valid blocks' LDS reads and MFMAs without a per-block
     // branch in the unrolled step)
-    auto compute = [&](auto ni_c, int stage, const uint8_t* As, const uint8_t* Bs) {
+    // As, Bs: the stage's A and B rows; Sa, Sb: their MXFP8 scale dwords
+    auto compute = [&](auto ni_c, const uint8_t* As, const uint8_t* Bs, const uint8_t* Sa, const uint8_t* Sb) {
       constexpr int NI = decltype(ni_c)::value;
       if constexpr (!FP8 && MODE == BWD_DH) {
         // (the dh epilogue leaves no registers for a second fragment set)
@@ -698,7 +702,6 @@ grouped_gemm_nt(Params p) {
         // 0-15 are chunk 4 ks + lh (block 2 ks), bytes 16-31 chunk
         // 4 ks + 2 + lh (block 2 ks + 1); the lane's scale operand is block
         // 2 ks + lh of its row (that byte of the row's scale dword).
-        const uint8_t* Ss = &L.scale[stage][0];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int p0 = ((4 * ks + lh) ^ sw) * 16, p1 = ((4 * ks + 2 + lh) ^ sw) * 16;
@@ -710,7 +713,7 @@ grouped_gemm_nt(Params p) {
             const i32x4 lo = *reinterpret_cast<const i32x4*>(As + row * ROWB + p0);
             const i32x4 hi = *reinterpret_cast<const i32x4*>(As + row * ROWB + p1);
             fa[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            sa[i] = Ss[row * 4 + 2 * ks + lh];
+            sa[i] = Sa[row * 4 + 2 * ks + lh];
           }
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
@@ -718,7 +721,7 @@ grouped_gemm_nt(Params p) {
             const i32x4 lo = *reinterpret_cast<const i32x4*>(Bs + row * ROWB + p0);
             const i32x4 hi = *reinterpret_cast<const i32x4*>(Bs + row * ROWB + p1);
             fb[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            sbv[j] = Ss[SA_BYTES + row * 4 + 2 * ks + lh];
+            sbv[j] = Sb[row * 4 + 2 * ks + lh];
           }
 #pragma unroll
           for (int i = 0; i < NI; ++i)
@@ -741,15 +744,18 @@ grouped_gemm_nt(Params p) {
         if (kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
         if constexpr (decltype(ni_c)::value > 0) {
           const uint8_t* As = &L.stage[kt & 1][0];
-          compute(ni_c, kt & 1, As, As + A_BYTES);
+          const uint8_t* Sa = &L.scale[kt & 1][0];
+          compute(ni_c, As, As + A_BYTES, Sa, Sa + SA_BYTES);
         }
       }
     };
     // Short tiles: three compact stages, steps kt+1 and kt+2 in flight while
     // kt is consumed. Each wave loads 8 of the SHORT_ROWS A rows and its 32 B
-    // rows (5 instructions a step), so "step kt landed" is vmcnt <= 5 while
-    // step kt+1's loads are outstanding.
-    constexpr bool kShortRing = !FP8 && MODE == GATE_UP;
+    // rows (5 instructions a step; in MXFP8 wave 0 adds the A rows' scale
+    // dwords and waves 4-7 the B rows'), so step kt has landed once at most 5
+    // of the wave's loads are outstanding: at least 5 of step kt+1's are
+    // younger.
+    constexpr bool kShortRing = MODE == GATE_UP;
     auto k_loop_short = [&](auto ni_c) {
       const int arow = 8 * wave + dr;
       const int asrc = L.row_src[arow];
@@ -761,6 +767,11 @@ grouped_gemm_nt(Params p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           lds_dma16(rs_b, b_off[i], kb, sbase + SHORT_ROWS * ROWB + (uint32_t)(32 * wave + 8 * i) * ROWB);
+        if (FP8 && (wave == 0 || wave >= 4)) {
+          const uint32_t ss = ldss0 + (uint32_t)slot * SHORT_SSLOT +
+                              (wave == 0 ? 0u : (uint32_t)(SHORT_ROWS + 64 * (wave - 4)) * 4u);
+          lds_dma4(rs_s, s_off, (uint32_t)(kstep * KS / 32), ss);
+        }
       };
       wait_vmcnt<0>();  // stores of the previous tile's epilogue are older than these loads
       if (nk > 0) issue_s(0, 0);
@@ -775,7 +786,8 @@ grouped_gemm_nt(Params p) {
         if (kt + 2 < nk) issue_s(slot == 0 ? 2 : slot - 1, kt + 2);
         if constexpr (decltype(ni_c)::value > 0) {
           const uint8_t* As = &L.stage[0][0] + slot * SHORT_SLOT;
-          compute(ni_c, 0, As, As + SHORT_ROWS * ROWB);
+          const uint8_t* Sa = &L.scale[0][0] + slot * SHORT_SSLOT;
+          compute(ni_c, As, As + SHORT_ROWS * ROWB, Sa, Sa + SHORT_ROWS * 4);
         }
         slot = slot == 2 ? 0 : slot + 1;
       }
