@@ -100,7 +100,9 @@ def _run_forward(runtime: MoKRuntime, keep: bool, x, router_weights, top_experts
     is allocated and filled only when ``keep``. Returns (out, schedule,
     context or None, weights by name)."""
     cfg = runtime.cfg
-    T = x.shape[0] if x.dim() == 2 else -1
+    if x is None or x.dim() != 2:
+        raise ValueError("x must be a [tokens, hidden] tensor")
+    T = x.shape[0]
     H, I, Is, E, k = cfg.hidden, cfg.intermediate, cfg.shared_intermediate, cfg.num_experts, cfg.topk
     _check("x", x, torch.bfloat16, (T, H))
     _check("router_weights", router_weights, torch.float32, (T, k))

@@ -50,6 +50,8 @@ def test_bad_arguments_are_rejected_before_the_device():
         moe_layer(rt, d["x"].float(), d["rw"], d["top"], d["sg"], d["su"], d["sd"], *w)
     with pytest.raises(ValueError, match="shape"):
         moe_layer(rt, d["x"], d["rw"][:, :1].contiguous(), d["top"], d["sg"], d["su"], d["sd"], *w)
+    with pytest.raises(ValueError, match=r"\[tokens, hidden\]"):
+        moe_layer(rt, d["x"].unsqueeze(0), d["rw"], d["top"], d["sg"], d["su"], d["sd"], *w)
     with pytest.raises(ValueError, match="int64"):
         moe_layer(rt, d["x"], d["rw"], d["top"].int(), d["sg"], d["su"], d["sd"], *w)
     with pytest.raises(ValueError, match="required"):
