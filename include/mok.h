@@ -268,8 +268,10 @@ mok_status mok_backward(mok_workspace* ws, mok_mode mode, const void* schedule, 
  * ld_dst % 8 == 0, ld_src % 8 == 0). Per block: X = clamp(floor(log2 amax)
  * - 8, -127, 127) (X = -127 for an all-zero block), scale byte X + 127,
  * element = round-to-nearest-even of v / 2^X on the E4M3 grid, saturating
- * at +-448, sign kept. Inputs must be finite. Bit-exact by construction
- * (integer arithmetic).
+ * at +-448, sign kept. Inputs must be finite. The codes are exact: the
+ * hardware scaled conversion gives the same bytes as the rule above.
+ * MOK_ERR_UNSUPPORTED for bf16 sources along axis 1 with more than 2^24 rows
+ * (one workgroup per row).
  */
 mok_status mok_mxfp8_quantize(const void* src, int src_is_fp32, int64_t rows, int64_t cols, int64_t ld_src,
                               int axis, uint8_t* dst, int64_t ld_dst, uint8_t* dst_scale, void* stream);

@@ -556,6 +556,7 @@ extern "C" mok_status mok_mxfp8_quantize(const void* src, int src_is_fp32, int64
   if (cols % 8 != 0 || ld_dst % 8 != 0 || ld_src % 8 != 0) return MOK_ERR_UNSUPPORTED;
   if (axis == 1 && cols % 32 != 0) return MOK_ERR_UNSUPPORTED;
   if (axis == 0 && rows % 32 != 0) return MOK_ERR_UNSUPPORTED;
+  if (axis == 1 && !src_is_fp32 && rows > ((int64_t)1 << 24)) return MOK_ERR_UNSUPPORTED;  // one workgroup per row
   if ((((uintptr_t)src) & 15) || (((uintptr_t)dst) & 7)) return MOK_ERR_UNSUPPORTED;
   if (axis == 0 && (((uintptr_t)dst_scale) & 7)) return MOK_ERR_UNSUPPORTED;
   return launch_quantize(src, src_is_fp32, rows, cols, ld_src, axis, dst, ld_dst, dst_scale, (hipStream_t)stream) ==

@@ -20,78 +20,63 @@
 namespace mok {
 namespace {
 
-// axis = 1, bf16 source: 4 lanes per 32-element block, 8 elements per lane.
-__global__ void __launch_bounds__(256) quant_axis1_bf16(const uint16_t* __restrict__ src, int64_t rows,
-                                                        int64_t cols, int64_t ld_src, uint8_t* __restrict__ dst,
-                                                        int64_t ld_dst, uint8_t* __restrict__ scale) {
-  const int64_t nblk_row = cols >> 5;
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t b = g >> 2;
-  const int part = (int)(g & 3);
-  const bool live = b < rows * nblk_row;
-  int64_t row = 0, blk = 0;
-  uint4 raw = make_uint4(0, 0, 0, 0);
-  if (live) {
-    row = b / nblk_row;
-    blk = b - row * nblk_row;
-    raw = *reinterpret_cast<const uint4*>(src + row * ld_src + blk * 32 + part * 8);
-  }
-  uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+// axis = 1, bf16 source: one workgroup per row, 4 lanes per 32-element
+// block, 8 elements (16 bytes) per lane, lanes on consecutive chunks, each
+// lane with up to 4 chunks' loads in flight. A row has nchunk = cols / 8
+// chunks, a multiple of 4, and the workgroup size is a multiple of 4, so the
+// 4 lanes of a block are always active together.
+__device__ __forceinline__ void quant_chunk_bf16(const uint4 raw, uint8_t* __restrict__ d, uint8_t* __restrict__ sc,
+                                                 int c) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t lo = (w[i] << 16) & 0x7FFFFFFFu, hi = w[i] & 0x7FFF0000u;
+    const uint32_t lo = (w[i] << 16) & 0x7FFFFFFFu, hi = w[i] & 0x7FFF0000u;
     amax = max(amax, max(lo, hi));
   }
   amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
   amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-  if (!live) return;
   const int X = mx_block_exponent(amax);
-  uint32_t c[2];
+  uint32_t q[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
-    c[h] = e4m3x4_encode_scaled(u2f(w[2 * h] << 16), u2f(w[2 * h] & 0xFFFF0000u), u2f(w[2 * h + 1] << 16),
+    q[h] = e4m3x4_encode_scaled(u2f(w[2 * h] << 16), u2f(w[2 * h] & 0xFFFF0000u), u2f(w[2 * h + 1] << 16),
                                 u2f(w[2 * h + 1] & 0xFFFF0000u), X);
-  *reinterpret_cast<uint2*>(dst + row * ld_dst + blk * 32 + part * 8) = make_uint2(c[0], c[1]);
-  if (part == 0) scale[row * nblk_row + blk] = (uint8_t)(X + 127);
+  *reinterpret_cast<uint2*>(d + (int64_t)c * 8) = make_uint2(q[0], q[1]);
+  if ((c & 3) == 0) sc[c >> 2] = (uint8_t)(X + 127);
 }
 
-// axis = 1, bf16 source with the row count read on the device (the
-// schedule header's token count), over a grid sized for max_rows.
+__device__ __forceinline__ void quant_row_bf16(const uint16_t* __restrict__ s, uint8_t* __restrict__ d,
+                                               uint8_t* __restrict__ sc, int nchunk) {
+  constexpr int kU = 4;
+  const int bd = blockDim.x;
+  for (int c0 = threadIdx.x; c0 < nchunk; c0 += kU * bd) {
+    uint4 raw[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      raw[u] = c0 + u * bd < nchunk ? *reinterpret_cast<const uint4*>(s + (int64_t)(c0 + u * bd) * 8)
+                                    : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (c0 + u * bd < nchunk) quant_chunk_bf16(raw[u], d, sc, c0 + u * bd);
+  }
+}
+
+__global__ void __launch_bounds__(256) quant_axis1_bf16(const uint16_t* __restrict__ src, int64_t cols,
+                                                        int64_t ld_src, uint8_t* __restrict__ dst, int64_t ld_dst,
+                                                        uint8_t* __restrict__ scale) {
+  const int64_t row = blockIdx.x;
+  quant_row_bf16(src + row * ld_src, dst + row * ld_dst, scale + row * (cols >> 5), (int)(cols >> 3));
+}
+
+// The same with the row count read on the device (the schedule header's
+// token count), over a grid sized for max_rows.
 __global__ void __launch_bounds__(256) quant_rows_dev_bf16(const uint16_t* __restrict__ src, const int32_t* __restrict__ hdr,
                                                            int64_t cols, uint8_t* __restrict__ dst,
                                                            uint8_t* __restrict__ scale) {
-  const int64_t rows = hdr[HDR_T];
-  const int64_t nblk_row = cols >> 5;
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t b = g >> 2;
-  const int part = (int)(g & 3);
-  const bool live = b < rows * nblk_row;
-  int64_t row = 0, blk = 0;
-  uint4 raw = make_uint4(0, 0, 0, 0);
-  if (live) {
-    row = b / nblk_row;
-    blk = b - row * nblk_row;
-    raw = *reinterpret_cast<const uint4*>(src + row * cols + blk * 32 + part * 8);
-  }
-  uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  uint32_t amax = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t lo = (w[i] << 16) & 0x7FFFFFFFu, hi = w[i] & 0x7FFF0000u;
-    amax = max(amax, max(lo, hi));
-  }
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-  if (!live) return;
-  const int X = mx_block_exponent(amax);
-  uint32_t c[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-    c[h] = e4m3x4_encode_scaled(u2f(w[2 * h] << 16), u2f(w[2 * h] & 0xFFFF0000u), u2f(w[2 * h + 1] << 16),
-                                u2f(w[2 * h + 1] & 0xFFFF0000u), X);
-  *reinterpret_cast<uint2*>(dst + row * cols + blk * 32 + part * 8) = make_uint2(c[0], c[1]);
-  if (part == 0) scale[row * nblk_row + blk] = (uint8_t)(X + 127);
+  const int64_t row = blockIdx.x;
+  if (row >= hdr[HDR_T]) return;
+  quant_row_bf16(src + row * cols, dst + row * cols, scale + row * (cols >> 5), (int)(cols >> 3));
 }
 
 // axis = 1, fp32 source: 8 lanes per block, 4 elements per lane.
@@ -614,12 +599,18 @@ hipError_t launch_quantize_rows_sched(const void* src, const int32_t* hdr, int64
   return hipGetLastError();
 }
 
+// threads per row-quantizer workgroup: a quarter of the row's 16-byte
+// chunks, rounded up to whole waves, at most 256
+static int row_threads(int64_t cols) {
+  const int64_t nchunk = cols >> 3;
+  return (int)std::min<int64_t>(256, std::max<int64_t>(64, (nchunk / 4 + 63) / 64 * 64));
+}
+
 hipError_t launch_quantize_rows_dev(const void* src, const int32_t* hdr, int64_t max_rows, int64_t cols, uint8_t* dst,
                                     uint8_t* dst_scale, hipStream_t s) {
-  const int64_t lanes = max_rows * (cols >> 5) * 4;
-  const int64_t grid = (lanes + 255) / 256;
-  if (grid == 0) return hipSuccess;
-  quant_rows_dev_bf16<<<dim3((unsigned)grid), dim3(256), 0, s>>>((const uint16_t*)src, hdr, cols, dst, dst_scale);
+  if (max_rows == 0 || cols == 0) return hipSuccess;
+  quant_rows_dev_bf16<<<dim3((unsigned)max_rows), dim3(row_threads(cols)), 0, s>>>((const uint16_t*)src, hdr, cols,
+                                                                                  dst, dst_scale);
   return hipGetLastError();
 }
 
@@ -634,8 +625,8 @@ hipError_t launch_quantize(const void* src, int src_is_fp32, int64_t rows, int64
       quant_axis1_f32<<<dim3((unsigned)grid), dim3(threads), 0, s>>>((const float*)src, rows, cols, ld_src, dst,
                                                                     ld_dst, dst_scale);
     else
-      quant_axis1_bf16<<<dim3((unsigned)grid), dim3(threads), 0, s>>>((const uint16_t*)src, rows, cols, ld_src,
-                                                                     dst, ld_dst, dst_scale);
+      quant_axis1_bf16<<<dim3((unsigned)rows), dim3(row_threads(cols)), 0, s>>>((const uint16_t*)src, cols, ld_src,
+                                                                               dst, ld_dst, dst_scale);
   } else {
     const int64_t lanes = (rows >> 5) * (cols / (src_is_fp32 ? 4 : 8));
     const int64_t grid = (lanes + threads - 1) / threads;
