@@ -479,7 +479,10 @@ grouped_gemm_nt(Params p) {
     const int live_blocks = min(4, max(0, (rows_here - wm * 128 + 31) / 32));
 
     // ---- row metadata, one thread per tile row ----
-    if (tid < BM) {
+    // Down's A rows are tile-local, so its loads do not need this table: its
+    // router weights are read while the first K step is in flight (below).
+    constexpr bool kLateMeta = MODE == DOWN;
+    if (!kLateMeta && tid < BM) {
       const int r = t.m0 + tid;
       int src = -1;
       float w = 0.f;
@@ -498,7 +501,7 @@ grouped_gemm_nt(Params p) {
       L.row_src[tid] = src;
       L.row_w[tid] = w;
     }
-    __syncthreads();
+    if constexpr (!kLateMeta) __syncthreads();
 
     // ---- operand resources and per-lane DMA offsets ----
     const bool a_by_token = MODE == GATE_UP || MODE == BWD_DH;
@@ -563,7 +566,7 @@ grouped_gemm_nt(Params p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 32 * wave + 8 * i + dr;
-      const int src = L.row_src[row];
+      const int src = kLateMeta ? (row < rows_here ? row : -1) : L.row_src[row];
       a_off[i] = src >= 0 ? (uint32_t)src * a_row_bytes + 16u * (uint32_t)(dp ^ swz(row)) : kOff;
     }
     const uint32_t b_row_bytes = (uint32_t)b_k * ES;
@@ -599,7 +602,7 @@ grouped_gemm_nt(Params p) {
         }
         rs_s = rsrc(sa_base, sa_bytes);
         rs_s2 = rsrc(MODE == BWD_DX ? sa_base2 : sa_base, sa_bytes);
-        const int src = L.row_src[64 * wave + lane];
+        const int src = kLateMeta ? (64 * wave + lane < rows_here ? 64 * wave + lane : -1) : L.row_src[64 * wave + lane];
         if (src >= 0) s_off = (uint32_t)src * kb;
       } else {
         const int lb = 64 * (wave - 4) + lane;
@@ -735,9 +738,33 @@ grouped_gemm_nt(Params p) {
 
     // ---- main loop: two stages, step kt+1 in flight while kt is consumed ----
     const int nk = K / KS;
+    // Down: the assignment of row m0 + tid is loaded ahead of the first
+    // step's loads (inline, so that the compiler's own wait for it cannot
+    // also cover them); its router weight then goes straight into the row
+    // table by LDS-DMA (zero past the segment), landing with the step.
     auto k_loop = [&](auto ni_c) {
-      wait_vmcnt<0>();  // stores of the previous tile's epilogue are older than these loads
-      if (nk > 0) issue(0, 0);
+      if constexpr (kLateMeta) {
+        const int r = t.m0 + tid;
+        const bool routed_row = tid < BM && r < t.m_end && !shared;
+        int a = 0;
+        if (routed_row) asm volatile("global_load_dword %0, %1, off" : "=v"(a) : "v"(p.row_src + r) : "memory");
+        if (nk > 0) issue(0, 0);
+        // the assignment is older than this wave's FP8 ? 9 : 8 loads of the step
+        if constexpr (FP8)
+          asm volatile("s_waitcnt vmcnt(9)" : "+v"(a) : : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(8)" : "+v"(a) : : "memory");
+        if (tid < BM) {
+          if (shared)
+            L.row_w[tid] = r < t.m_end ? 1.f : 0.f;
+          else
+            lds_dma4(rsrc(p.router_w, (uint32_t)T * p.k * 4u), routed_row ? (uint32_t)a * 4u : kOff, 0u,
+                     lds_addr(&L.row_w[64 * wave]));
+        }
+      } else {
+        wait_vmcnt<0>();  // stores of the previous tile's epilogue are older than these loads
+        if (nk > 0) issue(0, 0);
+      }
       for (int kt = 0; kt < nk; ++kt) {
         wait_vmcnt<0>();
         __syncthreads();  // every wave's loads of step kt landed; step kt-1's stage is free
