@@ -19,7 +19,7 @@ Formula (weights in the nn.Linear [out, in] layout, so y = W a):
   out[t] = sum_j w[t, j] * y_(t, j) + S_d (silu(S_g x_t) * (S_u x_t))
 with silu(z) = z * sigmoid(z). Dropped or invalid assignments contribute 0.
 
-Readings taken (listed in the design doc): SwiGLU is silu(gate) * up; the shared
+Readings taken where the pages leave a step open: SwiGLU is silu(gate) * up; the shared
 expert has weight 1 and is always on; router weights are used as given (the
 router is outside the layer, [R] §"Where MoK is the wrong tool"); the weight
 is applied to the expert output (equal to applying it to h by linearity).

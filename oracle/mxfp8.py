@@ -19,7 +19,7 @@ and scale formats taken here are the OCP Microscaling (MX) v1.0 ones:
     448 saturating to 448; the sign is kept (so -0 and negative values that
     round to zero give 0x80). Scale byte = X + 127.
 
-Readings taken (listed in the design doc): the OCP floor rule for X rather than a
+Readings taken where the pages leave a step open: the OCP floor rule for X rather than a
 round-up rule; saturation rather than NaN on overflow; sign-preserving zero.
 Non-finite inputs are outside the contract (asserted finite here).
 """

@@ -13,7 +13,7 @@ megakernel for NVL72 racks":
   * §"How MoK differs from a general MoE kernel library": the materialised
     plan is deterministic and replayable.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * With every expert on one GPU, the "destination" is an expert: the
     per-expert capacity is C = min(T, ceil(mult * T)) assignments, with
     mult the float32 value in the config evaluated in float64.
