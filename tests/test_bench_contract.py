@@ -1,5 +1,5 @@
-"""bench.py's output contract: one JSON line with the fields the benchmark
-driver reads (metric, value, unit, steps, warmup, ms_per_step, ...,
+"""bench.py's output contract: one JSON line with the fields a benchmark
+harness reads (metric, value, unit, steps, warmup, ms_per_step, ...,
 config.workload, roofline, cpu_baseline), and a clear refusal of more than
 one GPU."""
 import json
