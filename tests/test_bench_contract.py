@@ -41,3 +41,16 @@ def test_bench_json_line_contract():
     assert "traffic" in rf
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+
+
+@pytest.mark.gpu
+def test_bench_autograd_line():
+    # the same contract when the step runs through the torch.autograd layer
+    r = subprocess.run([sys.executable, "-u", BENCH, "--workload", "t8192_mxfp8_fwdbwd", "--steps", "2", "--warmup", "1",
+                        "--no-cpu-baseline", "--autograd"], capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    assert d["config"]["api"] == "torch.autograd layer" and d["config"]["passes"] == "fwd+bwd"
+    assert d["value"] > 0 and d["roofline"]["achieved"] > 0 and d["dtype"] == "mxfp8"
