@@ -246,6 +246,8 @@ enum TqSrc : int {
   TQ_ROWS32 = 4 // schedule-row-indexed fp32 rows (dG, dU of the MXFP8 backward)
 };
 
+constexpr int kMaxT128 = 1024 + 2;  // experts + 2 entries of a workspace's largest tile table
+
 struct TqParams {
   const int32_t* hdr;
   const int32_t* offsets;
@@ -271,9 +273,12 @@ struct TqParams {
 template <int SRC>
 __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
   __shared__ float tile[kTqRows][kTqLd];
+  __shared__ int32_t t128[kMaxT128];  // the per-expert 128-row tile prefix sums, searched per unit
   const int E = p.E;
   const int T = p.hdr[HDR_T];
-  const int nkb = p.tiles128[E + 1];
+  for (int i = threadIdx.x; i <= E + 1; i += blockDim.x) t128[i] = p.tiles128[i];
+  __syncthreads();
+  const int nkb = t128[E + 1];
   const int ncc = (max(p.cols_r, p.cols_s) + kTqCols - 1) / kTqCols;
   const int64_t units = (int64_t)nkb * ncc;
   const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
@@ -289,18 +294,18 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
     const int kb = (int)(u / ncc);
     w.cc = (int)(u - (int64_t)kb * ncc);
     int e = E;
-    if (kb < p.tiles128[E]) {
+    if (kb < t128[E]) {
       int lo = 0, hi = E;  // largest e with tiles128[e] <= kb
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (p.tiles128[mid] <= kb) lo = mid; else hi = mid;
+        if (t128[mid] <= kb) lo = mid; else hi = mid;
       }
       e = lo;
     }
     w.e = e;
     w.cols = e == E ? p.cols_s : p.cols_r;
     w.live = w.cc * kTqCols < w.cols;
-    w.kl = kb - p.tiles128[e];
+    w.kl = kb - t128[e];
     return w;
   };
   // The thread's 32 source values of its row (row r of the block, columns
@@ -388,8 +393,8 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
     }
     if (cur.live) {
       const bool shared = cur.e == E;
-      const int64_t Kp = 128 * (int64_t)(shared ? nkb - p.tiles128[E] : p.tiles128[cur.e + 1] - p.tiles128[cur.e]);
-      const int64_t kofs = shared ? 0 : 128 * (int64_t)p.tiles128[cur.e];
+      const int64_t Kp = 128 * (int64_t)(shared ? nkb - t128[E] : t128[cur.e + 1] - t128[cur.e]);
+      const int64_t kofs = shared ? 0 : 128 * (int64_t)t128[cur.e];
       const int64_t base = shared ? p.kr_cap * p.cols_r : kofs * cur.cols;
       const int64_t sbase = shared ? p.kr_cap / 32 * p.cols_r : kofs / 32 * cur.cols;
       const int64_t c = cur.cc * kTqCols + (threadIdx.x >> 2);
@@ -414,9 +419,12 @@ constexpr int kTbRows = 128, kTbCols = 128, kTbLd = kTbRows / 2 + 1;
 template <int SRC>
 __global__ void __launch_bounds__(256) transpose_rows_bf16(TqParams p) {
   __shared__ uint32_t tile[kTbCols][kTbLd];
+  __shared__ int32_t t128[kMaxT128];  // the per-expert 128-row tile prefix sums, searched per unit
   const int E = p.E;
   const int T = p.hdr[HDR_T];
-  const int nkb = p.tiles128[E + 1];
+  for (int i = threadIdx.x; i <= E + 1; i += blockDim.x) t128[i] = p.tiles128[i];
+  __syncthreads();
+  const int nkb = t128[E + 1];
   const int ncc = (max(p.cols_r, p.cols_s) + kTbCols - 1) / kTbCols;
   const int64_t units = (int64_t)nkb * ncc;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -424,19 +432,19 @@ __global__ void __launch_bounds__(256) transpose_rows_bf16(TqParams p) {
   const int m = threadIdx.x & 15;             // store phase: output rows' 8-element chunk
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
     const int kb = (int)(u / ncc), cc = (int)(u - (int64_t)kb * ncc);
-    const bool shared = kb >= p.tiles128[E];
+    const bool shared = kb >= t128[E];
     int e = E;
     if (!shared) {
       int lo = 0, hi = E;  // largest e with tiles128[e] <= kb
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (p.tiles128[mid] <= kb) lo = mid; else hi = mid;
+        if (t128[mid] <= kb) lo = mid; else hi = mid;
       }
       e = lo;
     }
     const int cols = shared ? p.cols_s : p.cols_r;
     if (cc * kTbCols >= cols) continue;  // uniform across the workgroup
-    const int kl = kb - p.tiles128[e];   // block index inside the segment
+    const int kl = kb - t128[e];   // block index inside the segment
     const int nrows = shared ? T : p.kept[e];
     const int64_t row0 = shared ? 0 : p.offsets[e];
     const int c0 = cc * kTbCols + 8 * cch;
@@ -481,8 +489,8 @@ __global__ void __launch_bounds__(256) transpose_rows_bf16(TqParams p) {
       }
     }
     __syncthreads();
-    const int64_t Kp = 128 * (int64_t)(shared ? nkb - p.tiles128[E] : p.tiles128[e + 1] - p.tiles128[e]);
-    const int64_t kofs = shared ? 0 : 128 * (int64_t)p.tiles128[e];
+    const int64_t Kp = 128 * (int64_t)(shared ? nkb - t128[E] : t128[e + 1] - t128[e]);
+    const int64_t kofs = shared ? 0 : 128 * (int64_t)t128[e];
     uint16_t* dst = reinterpret_cast<uint16_t*>(p.dst) + (shared ? p.kr_cap * p.cols_r : kofs * cols);
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
