@@ -15,7 +15,9 @@ What is specific to the wrapper:
   backwards;
 - in MXFP8 mode the quantized weights are reused until a parameter changes in
   place, and made again after;
-- an empty batch gives empty outputs and all-zero weight gradients."""
+- an empty batch gives empty outputs and all-zero weight gradients;
+- a training step (forward and backward) captured in one graph replays to
+  the eager step's bits."""
 import numpy as np
 import pytest
 
@@ -335,3 +337,49 @@ def test_experts_module_8192_tokens_mxfp8():
     same(m.routed_down_weights.grad, ref_g["d_routed_down"], "d_routed_down")
     for n in sw:
         same(sw[n].grad, ref_g["d_" + n], "d_" + n)
+
+
+def test_autograd_training_step_graph_replay():
+    # forward and backward captured in one graph (warm-up on a side stream
+    # first, as whole-network capture needs); every replay, with eager steps
+    # and synchronisations between replays, gives the eager step's bits
+    c = MoEShape("graph", T=300, H=256, I=256, E=5, k=3, I_s=128, seed=151, w_std=0.05, passes="fwd+bwd")
+    d = to_dev(make_inputs(c))
+    rt = MoKRuntime(shape_cfg(c))
+    L = leaves(d)
+    params = [L["x"], L["rw"]] + [L["w"][n] for n in NAMES]
+
+    def step():
+        for t in params:
+            t.grad = None
+        y = run_layer(rt, L)
+        y.backward(d["grad_out"])
+        return y
+
+    ref_y = step().detach().clone()
+    ref_g = {n: g.clone() for n, g in grads_of(L).items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    for t in params:
+        t.grad = None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y_static = run_layer(rt, L)
+        y_static.backward(d["grad_out"])
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        same(y_static, ref_y, f"replay {rep} out")
+        for n, gr in grads_of(L).items():
+            same(gr, ref_g[n], f"replay {rep} {n}")
+        # eager work between replays (its own gradients are set aside)
+        saved = [t.grad for t in params]
+        eager = run_layer(rt, leaves(d, grad=False))
+        torch.cuda.synchronize()
+        same(eager, ref_y, f"eager between replays {rep}")
+        for t, gr in zip(params, saved):
+            t.grad = gr
