@@ -116,3 +116,41 @@ def test_zero_router_weights_leave_the_shared_expert():
                                f64(inp["w_gate"]), f64(inp["w_up"]), f64(inp["w_down"]), f64(inp["s_gate"]),
                                f64(inp["s_up"]), f64(inp["s_down"]))
     assert_close_inf(np64(out), shared_only, TOL_BF16, "shared only")
+
+
+@pytest.mark.parametrize("mode", ["bf16", "mxfp8"])
+def test_more_experts_than_the_lds_tables_hold(mode):
+    # 300 experts: the grouped GEMM reads its tile tables from global memory
+    # (natural tile order) instead of LDS; forward (both modes) and the BF16
+    # backward against the oracle
+    c = MoEShape("e300", T=600, H=128, I=128, E=300, k=2, I_s=128, seed=161, w_std=0.05, passes="fwd+bwd",
+                 mode=mode)
+    inp = make_inputs(c)
+    d = to_dev(inp)
+    cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=c.T,
+                        shared_intermediate=c.I_s)
+    ws = mok.Workspace(cfg)
+    m = mok.MOK_MODE_MXFP8 if mode == "mxfp8" else mok.MOK_MODE_BF16
+    sched = mok.build_schedule(ws, d["top_experts"])
+    ctx = torch.empty(mok.context_bytes(cfg, m), dtype=torch.uint8, device="cuda")
+    w = d["weights"]
+    if mode == "mxfp8":
+        q = {}
+        for n, t in w.items():
+            codes, sc = mok.mxfp8_quantize(t.reshape(-1, t.shape[-1]), axis=1)
+            q[n], q[n + "_scale"] = codes.view(t.shape), sc
+        w = q
+    out = mok.forward(ws, sched, d["x"], d["router_weights"], w, mode=m, context=ctx)
+    torch.cuda.synchronize()
+    args = (f64(inp["x"]), inp["top_experts"], inp["router_weights"], f64(inp["w_gate"]), f64(inp["w_up"]),
+            f64(inp["w_down"]), f64(inp["s_gate"]), f64(inp["s_up"]), f64(inp["s_down"]))
+    ref = omoe.forward_mxfp8(*args) if mode == "mxfp8" else omoe.forward(*args)
+    assert_close_inf(np64(out), ref, TOL_MXFP8 if mode == "mxfp8" else TOL_BF16, f"e300 {mode} out")
+    if mode == "bf16":
+        g = mok.backward(ws, sched, ctx, d["grad_out"], d["x"], d["router_weights"], d["weights"])
+        torch.cuda.synchronize()
+        rg = omoe.backward(f64(inp["grad_out"]), *args)
+        for gname, rname in [("dx", "dx"), ("d_router_weights", "d_router_weights"), ("d_routed_gate", "d_w_gate"),
+                             ("d_routed_up", "d_w_up"), ("d_routed_down", "d_w_down"),
+                             ("d_shared_gate", "d_s_gate"), ("d_shared_up", "d_s_up"), ("d_shared_down", "d_s_down")]:
+            assert_close_inf(np64(g[gname]), rg[rname], TOL_BF16, f"e300 {gname}")
