@@ -121,8 +121,8 @@ def test_zero_router_weights_leave_the_shared_expert():
 @pytest.mark.parametrize("mode", ["bf16", "mxfp8"])
 def test_more_experts_than_the_lds_tables_hold(mode):
     # 300 experts: the grouped GEMM reads its tile tables from global memory
-    # (natural tile order) instead of LDS; forward (both modes) and the BF16
-    # backward against the oracle
+    # (natural tile order) instead of LDS; forward and backward in both
+    # modes against the oracle
     c = MoEShape("e300", T=600, H=128, I=128, E=300, k=2, I_s=128, seed=161, w_std=0.05, passes="fwd+bwd",
                  mode=mode)
     inp = make_inputs(c)
@@ -146,11 +146,14 @@ def test_more_experts_than_the_lds_tables_hold(mode):
             f64(inp["w_down"]), f64(inp["s_gate"]), f64(inp["s_up"]), f64(inp["s_down"]))
     ref = omoe.forward_mxfp8(*args) if mode == "mxfp8" else omoe.forward(*args)
     assert_close_inf(np64(out), ref, TOL_MXFP8 if mode == "mxfp8" else TOL_BF16, f"e300 {mode} out")
-    if mode == "bf16":
-        g = mok.backward(ws, sched, ctx, d["grad_out"], d["x"], d["router_weights"], d["weights"])
-        torch.cuda.synchronize()
+    g = mok.backward(ws, sched, ctx, d["grad_out"], d["x"], d["router_weights"], d["weights"], mode=m)
+    torch.cuda.synchronize()
+    if mode == "mxfp8":
+        rg = omoe.backward_mxfp8(f64(inp["grad_out"]), *args)
+    else:
         rg = omoe.backward(f64(inp["grad_out"]), *args)
-        for gname, rname in [("dx", "dx"), ("d_router_weights", "d_router_weights"), ("d_routed_gate", "d_w_gate"),
-                             ("d_routed_up", "d_w_up"), ("d_routed_down", "d_w_down"),
-                             ("d_shared_gate", "d_s_gate"), ("d_shared_up", "d_s_up"), ("d_shared_down", "d_s_down")]:
-            assert_close_inf(np64(g[gname]), rg[rname], TOL_BF16, f"e300 {gname}")
+    tol = TOL_MXFP8 if mode == "mxfp8" else TOL_BF16
+    for gname, rname in [("dx", "dx"), ("d_router_weights", "d_router_weights"), ("d_routed_gate", "d_w_gate"),
+                         ("d_routed_up", "d_w_up"), ("d_routed_down", "d_w_down"),
+                         ("d_shared_gate", "d_s_gate"), ("d_shared_up", "d_s_up"), ("d_shared_down", "d_s_down")]:
+        assert_close_inf(np64(g[gname]), rg[rname], tol, f"e300 {mode} {gname}")
