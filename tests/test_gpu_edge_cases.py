@@ -118,12 +118,14 @@ def test_zero_router_weights_leave_the_shared_expert():
     assert_close_inf(np64(out), shared_only, TOL_BF16, "shared only")
 
 
+@pytest.mark.parametrize("E", [300, 1024])
 @pytest.mark.parametrize("mode", ["bf16", "mxfp8"])
-def test_more_experts_than_the_lds_tables_hold(mode):
-    # 300 experts: the grouped GEMM reads its tile tables from global memory
+def test_more_experts_than_the_lds_tables_hold(mode, E):
+    # 300 and 1024 experts (the largest a workspace takes): the grouped GEMM
+    # reads its tile tables from global memory
     # (natural tile order) instead of LDS; forward and backward in both
     # modes against the oracle
-    c = MoEShape("e300", T=600, H=128, I=128, E=300, k=2, I_s=128, seed=161, w_std=0.05, passes="fwd+bwd",
+    c = MoEShape("many", T=2 * E, H=128, I=128, E=E, k=2, I_s=128, seed=161, w_std=0.05, passes="fwd+bwd",
                  mode=mode)
     inp = make_inputs(c)
     d = to_dev(inp)
@@ -145,7 +147,7 @@ def test_more_experts_than_the_lds_tables_hold(mode):
     args = (f64(inp["x"]), inp["top_experts"], inp["router_weights"], f64(inp["w_gate"]), f64(inp["w_up"]),
             f64(inp["w_down"]), f64(inp["s_gate"]), f64(inp["s_up"]), f64(inp["s_down"]))
     ref = omoe.forward_mxfp8(*args) if mode == "mxfp8" else omoe.forward(*args)
-    assert_close_inf(np64(out), ref, TOL_MXFP8 if mode == "mxfp8" else TOL_BF16, f"e300 {mode} out")
+    assert_close_inf(np64(out), ref, TOL_MXFP8 if mode == "mxfp8" else TOL_BF16, f"E={E} {mode} out")
     g = mok.backward(ws, sched, ctx, d["grad_out"], d["x"], d["router_weights"], d["weights"], mode=m)
     torch.cuda.synchronize()
     if mode == "mxfp8":
@@ -156,4 +158,4 @@ def test_more_experts_than_the_lds_tables_hold(mode):
     for gname, rname in [("dx", "dx"), ("d_router_weights", "d_router_weights"), ("d_routed_gate", "d_w_gate"),
                          ("d_routed_up", "d_w_up"), ("d_routed_down", "d_w_down"),
                          ("d_shared_gate", "d_s_gate"), ("d_shared_up", "d_s_up"), ("d_shared_down", "d_s_down")]:
-        assert_close_inf(np64(g[gname]), rg[rname], tol, f"e300 {mode} {gname}")
+        assert_close_inf(np64(g[gname]), rg[rname], tol, f"E={E} {mode} {gname}")
