@@ -175,10 +175,13 @@ __global__ void __launch_bounds__(kThreads) sched_scan_scatter(SchedParams p, in
     kept = cnt < p.C ? cnt : p.C;
   }
   const int padded = (kept + p.P - 1) / p.P * p.P;
+  // GEMM tiles cover the kept rows only: counted from the padded length, a
+  // pad that does not divide the tile height (P = 96: 250 kept rows, 288
+  // padded) would give a last tile with no valid row
   int val[1 + kNumTileBMs], incl[1 + kNumTileBMs];
 #pragma unroll
   for (int q = 0; q < 1 + kNumTileBMs; ++q) {
-    val[q] = q == 0 ? padded : (padded + kTileBM[q - 1] - 1) / kTileBM[q - 1];
+    val[q] = q == 0 ? padded : (kept + kTileBM[q - 1] - 1) / kTileBM[q - 1];
     incl[q] = wave_inclusive_scan(val[q], lane);
   }
   const int cnt_w = wave_sum(cnt), drop_w = wave_sum(cnt - kept);

@@ -50,6 +50,10 @@ def test_validate_config_contract():
     assert status(cfg(intermediate=96)) == _lib.MOK_ERR_UNSUPPORTED
     assert status(cfg(shared_intermediate=32)) == _lib.MOK_ERR_UNSUPPORTED
     assert status(cfg(expert_pad=48)) == _lib.MOK_ERR_UNSUPPORTED
+    # any positive multiple of 32 is a valid pad, also those that do not
+    # divide the GEMM tile height or exceed it
+    for pad in (32, 64, 96, 160, 192, 224, 288, 512):
+        assert status(cfg(expert_pad=pad)) == _lib.MOK_OK, pad
     assert status(cfg(num_experts=2048)) == _lib.MOK_ERR_UNSUPPORTED
     assert status(cfg(topk=0)) == _lib.MOK_ERR_INVALID_ARGUMENT
     assert status(cfg(max_tokens=0)) == _lib.MOK_ERR_INVALID_ARGUMENT

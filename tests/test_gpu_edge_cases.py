@@ -1,7 +1,9 @@
 """Edge cases of the whole path against the oracle: a batch smaller than the
 workspace's max_tokens (BF16 and MXFP8, forward and backward), an empty
-batch (no tokens: empty outputs, every weight gradient exactly zero), and
-router weights of zero (the output is the shared expert alone)."""
+batch (no tokens: empty outputs, every weight gradient exactly zero),
+router weights of zero (the output is the shared expert alone), and expert
+paddings that do not divide the 256-row GEMM tile (96, 160) or exceed it
+(512)."""
 import numpy as np
 import pytest
 
@@ -29,10 +31,10 @@ def quantize_weights(wdev: dict) -> dict:
     return q
 
 
-def run(c: MoEShape, inp: dict, T_max: int, mxfp8: bool):
+def run(c: MoEShape, inp: dict, T_max: int, mxfp8: bool, expert_pad: int = 32):
     d = to_dev(inp)
     cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=T_max,
-                        shared_intermediate=c.I_s)
+                        shared_intermediate=c.I_s, expert_pad=expert_pad)
     ws = mok.Workspace(cfg)
     mode = mok.MOK_MODE_MXFP8 if mxfp8 else mok.MOK_MODE_BF16
     sched = mok.build_schedule(ws, d["top_experts"])
@@ -159,3 +161,32 @@ def test_more_experts_than_the_lds_tables_hold(mode, E):
                          ("d_routed_up", "d_w_up"), ("d_routed_down", "d_w_down"),
                          ("d_shared_gate", "d_s_gate"), ("d_shared_up", "d_s_up"), ("d_shared_down", "d_s_down")]:
         assert_close_inf(np64(g[gname]), rg[rname], tol, f"E={E} {mode} {gname}")
+
+
+@pytest.mark.parametrize("pad", [96, 160, 512])
+@pytest.mark.parametrize("mxfp8", [False, True], ids=["bf16", "mxfp8"])
+def test_expert_pad_not_dividing_the_tile(mxfp8, pad):
+    # Expert 0 gets exactly 250 rows and expert 1 exactly 260: with P = 96
+    # their segments are padded to 288 rows, past one 256-row tile while the
+    # kept rows of expert 0 fit in one; P = 512 pads every segment past two
+    # tiles. Forward and backward against the oracle with the same padding.
+    T, H, I, E, k, Is = 640, 256, 128, 4, 2, 128
+    c = MoEShape("pad", T=T, H=H, I=I, E=E, k=k, I_s=Is, seed=97, w_std=0.05,
+                 mode="mxfp8" if mxfp8 else "bf16", passes="fwd+bwd")
+    inp = make_inputs(c)
+    top = np.empty((T, k), np.int64)
+    top[:, 0] = np.where(np.arange(T) < 250, 0, 2)
+    top[:, 1] = np.where(np.arange(T) < 260, 1, 3)
+    inp["top_experts"] = top
+    print(f"expert pad {pad} {'mxfp8' if mxfp8 else 'bf16'}", flush=True)
+    out, g = run(c, inp, T, mxfp8, expert_pad=pad)
+    args = (f64(inp["x"]), inp["top_experts"], inp["router_weights"], f64(inp["w_gate"]), f64(inp["w_up"]),
+            f64(inp["w_down"]), f64(inp["s_gate"]), f64(inp["s_up"]), f64(inp["s_down"]))
+    tol = TOL_MXFP8 if mxfp8 else TOL_BF16
+    ref_out = (omoe.forward_mxfp8 if mxfp8 else omoe.forward)(*args, expert_pad=pad)
+    assert_close_inf(np64(out), ref_out, tol, "out")
+    ref = (omoe.backward_mxfp8 if mxfp8 else omoe.backward)(f64(inp["grad_out"]), *args, expert_pad=pad)
+    for gname, rname in [("dx", "dx"), ("d_router_weights", "d_router_weights"), ("d_routed_gate", "d_w_gate"),
+                         ("d_routed_up", "d_w_up"), ("d_routed_down", "d_w_down"), ("d_shared_gate", "d_s_gate"),
+                         ("d_shared_up", "d_s_up"), ("d_shared_down", "d_s_down")]:
+        assert_close_inf(np64(g[gname]), ref[rname], tol, f"pad {pad} {gname}")

@@ -46,10 +46,10 @@ def check(f, ref, T, k, E):
     n_mb = ref["n_mb"]
     assert hdr[6] == n_mb
     np.testing.assert_array_equal(f["mb_offsets"][: (n_mb + 1) * E].reshape(n_mb + 1, E), ref["mb_offsets"])
-    # internal tile table: per-expert prefix sums of ceil(padded / BM), then + shared tiles
+    # internal tile table: per-expert prefix sums of ceil(kept / BM), then + shared tiles
     for q, bm in enumerate(mok.TILE_BMS):
         tl = f["tiles"][q * (E + 2): (q + 1) * (E + 2)]
-        want = np.concatenate([[0], np.cumsum(-(-ref["padded"] // bm))])
+        want = np.concatenate([[0], np.cumsum(-(-ref["kept"] // bm))])
         np.testing.assert_array_equal(tl[: E + 1], want)
 
 
