@@ -181,8 +181,12 @@ size_t mok_schedule_bytes(const mok_config* cfg);
 mok_status mok_schedule_layout_query(const mok_config* cfg, mok_schedule_layout* out);
 
 /* Bytes of the caller-owned forward context (saved activations for
- * backward: G, U and h of every routed and shared row, bf16); 0 if
- * invalid. The same size serves both modes. */
+ * backward: G, U and h of every routed and shared row); 0 if invalid.
+ * BF16 mode: G, U and h in bf16. MXFP8 mode: G and U in fp32 as the
+ * forward accumulated them (the backward's SwiGLU derivative starts from the
+ * values h came from) and h as the E4M3 codes and E8M0 scales the down GEMM
+ * read; about twice the BF16 size. A context is read only by a backward of
+ * the mode that wrote it. */
 size_t mok_context_bytes(const mok_config* cfg, mok_mode mode);
 
 /* Device scratch a workspace of this config allocates, in bytes. */

@@ -294,7 +294,7 @@ extern "C" size_t mok_context_bytes(const mok_config* c, mok_mode mode) {
   if (mok_validate_config(c) != MOK_OK) return 0;
   if (mode != MOK_MODE_BF16 && mode != MOK_MODE_MXFP8) return 0;
   const Layout L = schedule_layout(*c);
-  return 3 * align_up(ctx_elems(*c, L) * 2, 256);
+  return ctx_layout(*c, L, mode == MOK_MODE_MXFP8).total;
 }
 
 extern "C" size_t mok_workspace_bytes(const mok_config* c) {
@@ -496,13 +496,12 @@ extern "C" mok_status mok_forward(mok_workspace* ws, mok_mode mode, const void* 
   a.router_w = router_weights;
   a.out = out;
   a.mxfp8 = mode == MOK_MODE_MXFP8;
-  const size_t ce = ctx_elems(ws->cfg, ws->layout);
   if (context) {
     char* cb = (char*)context;
-    const size_t part = align_up(ce * 2, 256);
-    a.ctx_g = cb;
-    a.ctx_u = cb + part;
-    a.h = cb + 2 * part;
+    const CtxLayout cl = ctx_layout(ws->cfg, ws->layout, a.mxfp8 != 0);
+    a.ctx_g = cb + cl.g;
+    a.ctx_u = cb + cl.u;
+    a.h = cb + cl.h;
   } else {
     a.h = ws->hbuf;
   }
@@ -530,16 +529,15 @@ extern "C" mok_status mok_backward(mok_workspace* ws, mok_mode mode, const void*
     return MOK_ERR_INVALID_ARGUMENT;
   DeviceGuard g(ws->device);
   if (!g.ok) return MOK_ERR_HIP;
-  const size_t ce = ctx_elems(ws->cfg, ws->layout);
-  const size_t part = align_up(ce * 2, 256);
+  const CtxLayout cl = ctx_layout(ws->cfg, ws->layout, mode == MOK_MODE_MXFP8);
   BwdArgs a{};
   a.w = weights;
   a.x = x;
   a.grad_out = grad_out;
   a.router_w = router_weights;
-  a.ctx_g = context;
-  a.ctx_u = (const char*)context + part;
-  a.ctx_h = (const char*)context + 2 * part;
+  a.ctx_g = (const char*)context + cl.g;
+  a.ctx_u = (const char*)context + cl.u;
+  a.ctx_h = (const char*)context + cl.h;
   a.g = grads;
   a.mxfp8 = mode == MOK_MODE_MXFP8;
   return to_status(launch_backward(ws, schedule, a, (hipStream_t)stream));

@@ -19,13 +19,16 @@
 //
 // Launch sequence (stream-ordered, no host synchronisation):
 //   transpose : W_d^T [E, I, H], W_g^T and W_u^T [E, H, I] (and shared)
-//   gather    : x and grad_out rows copied into schedule order
-//   bwd_dh    : NT grouped GEMM grad_out-rows x W_d^T; epilogue writes dG,
-//               dU, w*h and per-tile partial sums of d_router_weight
+//   bwd_dh    : NT grouped GEMM of grad_out rows (gathered by token in the
+//               operand loads) x W_d^T; epilogue writes dG, dU and per-tile
+//               partial sums of d_router_weight
 //   dw reduce : d_router_weights[t, j] = fixed-order sum of the partials
 //   bwd_dx    : NT grouped GEMM [dG | dU] x [W_g^T | W_u^T] -> dA rows
 //   dx        : fixed-order gather-sum of dA rows back to token order
-//   bwd_dw    : TN grouped GEMM, the three weight gradients per expert
+//   dW operands: x rows, w * grad_out rows, h, dG, dU written transposed
+//               per expert ([cols, K_e], K_e = its rows rounded up to 128)
+//   bwd_dw    : the same NT grouped GEMM (mode BWD_DW), the three weight
+//               gradients per expert, contracting over the expert's rows
 #include "device_common.h"
 #include "combine.h"
 #include "gemm_nt.h"
@@ -154,8 +157,8 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
     p.b0s = b.wdTs;
     p.sb0 = b.sdTq;
     p.sb0s = b.sdTs;
-    p.g_in = (const uint16_t*)a.ctx_g;
-    p.u_in = (const uint16_t*)a.ctx_u;
+    p.g_in = a.ctx_g;
+    p.u_in = a.ctx_u;
     p.hq_in = (const uint8_t*)a.ctx_h;
     p.hq_scale_in = (const uint8_t*)a.ctx_h + ce;
     p.dg_out32 = b.dg32;
@@ -280,8 +283,8 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
     p.a_tok = a.grad_out;
     p.b0 = b.wdT;
     p.sb0 = b.sdT;
-    p.g_in = (const uint16_t*)a.ctx_g;
-    p.u_in = (const uint16_t*)a.ctx_u;
+    p.g_in = a.ctx_g;
+    p.u_in = a.ctx_u;
     p.h_in = (const uint16_t*)a.ctx_h;
     p.dg_out = b.dg;
     p.du_out = b.du;

@@ -62,8 +62,8 @@ hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a
   nt::Params p{};
   fill_schedule(p, ws, v);
   p.router_w = a.router_w;
-  p.ctx_g = (uint16_t*)a.ctx_g;
-  p.ctx_u = (uint16_t*)a.ctx_u;
+  p.ctx_g = a.ctx_g;
+  p.ctx_u = a.ctx_u;
   // h: bf16 in BF16 mode; E4M3 codes then E8M0 scales in MXFP8 mode (in the
   // context's h region when a context is kept, else in the workspace).
   uint8_t* hq = nullptr;

@@ -21,7 +21,6 @@
 namespace mok {
 
 typedef int i32x4v __attribute__((ext_vector_type(4)));
-typedef short i16x4v __attribute__((vector_size(8)));   // ds_read_b64_tr_b16 result
 typedef short i16x8v __attribute__((vector_size(16)));
 
 // Physical chunk = logical chunk ^ swz(row). 16-byte reads of 16

@@ -91,11 +91,11 @@ struct Params {
   // outputs (row layouts as a_row: routed rows, then shared rows at rows_cap_max)
   void* out;                    // h (GATE_UP), y (DOWN), dA (BWD_DX)
   uint8_t* out_scale;           // h scales (GATE_UP, MXFP8)
-  uint16_t* ctx_g;              // G, U saved for backward (GATE_UP)
-  uint16_t* ctx_u;
+  void* ctx_g;                  // G, U saved for backward (GATE_UP): bf16, fp32 in MXFP8 mode
+  void* ctx_u;
   // BWD_DH epilogue
-  const uint16_t* g_in;
-  const uint16_t* u_in;
+  const void* g_in;             // the saved G, U: bf16, fp32 in MXFP8 mode
+  const void* u_in;
   const uint16_t* h_in;
   uint16_t* dg_out;
   uint16_t* du_out;
@@ -474,6 +474,10 @@ grouped_gemm_nt(Params p) {
     const int K = MODE == BWD_DW ? t.kdim : k_of<MODE>(p, shared);
     const int Nd = MODE == BWD_DW ? (t.job == 0 ? Iv : p.H) : n_of<MODE>(p, shared);  // valid output columns
     const int rows_here = t.m_end - t.m0;
+    // a tile without a valid row (the schedule counts tiles from kept rows,
+    // so none is listed; kept as a guard) would turn the byte counts of its
+    // buffer resources negative: skip it, the same decision in every wave
+    if (rows_here <= 0) continue;
     // 32-row MFMA blocks of this wave's 128 rows that hold valid rows
     // (uniform across the wave): 4 except in a segment's last tile
     const int live_blocks = min(4, max(0, (rows_here - wm * 128 + 31) / 32));
@@ -876,8 +880,8 @@ grouped_gemm_nt(Params p) {
         };
         store_out((uint16_t*)p.out + sh, std::integral_constant<int, 0>{});
         if (p.ctx_g) {
-          store_out(p.ctx_g + sh, std::integral_constant<int, 1>{});
-          store_out(p.ctx_u + sh, std::integral_constant<int, 2>{});
+          store_out((uint16_t*)p.ctx_g + sh, std::integral_constant<int, 1>{});
+          store_out((uint16_t*)p.ctx_u + sh, std::integral_constant<int, 2>{});
         }
       } else {
         // h = silu(g) * u in fp32, quantized along I in blocks of 32: the
@@ -917,7 +921,9 @@ grouped_gemm_nt(Params p) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(reg + r * SW + (lane & 1) * 16);
           if (ml < rows_here && col < Nd) *reinterpret_cast<u32x4*>(hq + (int64_t)(t.m0 + ml) * Nd + col) = v;
         }
-        if (p.ctx_g) {  // G and U for the backward, bf16 (direct stores)
+        if (p.ctx_g) {  // G and U for the backward, fp32 as accumulated (direct 16-byte stores)
+          float* cg = (float*)p.ctx_g;
+          float* cu = (float*)p.ctx_u;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int ml = wm * 128 + i * 32 + lr;
@@ -927,10 +933,10 @@ grouped_gemm_nt(Params p) {
               const int n = col0 + 8 * q + 4 * lh;
               if (n >= Nd) continue;
               const int64_t o = sh + (int64_t)(t.m0 + ml) * Nd + n;
-              *reinterpret_cast<uint2*>(p.ctx_g + o) = make_uint2(pack_bf16x2(acc[i][0][4 * q], acc[i][0][4 * q + 1]),
-                                                                  pack_bf16x2(acc[i][0][4 * q + 2], acc[i][0][4 * q + 3]));
-              *reinterpret_cast<uint2*>(p.ctx_u + o) = make_uint2(pack_bf16x2(acc[i][1][4 * q], acc[i][1][4 * q + 1]),
-                                                                  pack_bf16x2(acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]));
+              *reinterpret_cast<float4*>(cg + o) =
+                  make_float4(acc[i][0][4 * q], acc[i][0][4 * q + 1], acc[i][0][4 * q + 2], acc[i][0][4 * q + 3]);
+              *reinterpret_cast<float4*>(cu + o) =
+                  make_float4(acc[i][1][4 * q], acc[i][1][4 * q + 1], acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]);
             }
           }
         }
@@ -1013,9 +1019,14 @@ grouped_gemm_nt(Params p) {
             const float4 d0 = *reinterpret_cast<const float4*>(reg + r * SWF + cc);
             const float4 d1 = *reinterpret_cast<const float4*>(reg + r * SWF + cc + 4);
             const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-            const uint4 gv = *reinterpret_cast<const uint4*>(p.g_in + rowo);
-            const uint4 uv = *reinterpret_cast<const uint4*>(p.u_in + rowo);
-            const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+            // saved G and U: bf16 pairs (BF16), or fp32 (MXFP8, read per half below)
+            uint32_t gw[4] = {0, 0, 0, 0}, uw[4] = {0, 0, 0, 0};
+            if constexpr (!FP8) {
+              const uint4 gv = *reinterpret_cast<const uint4*>((const uint16_t*)p.g_in + rowo);
+              const uint4 uv = *reinterpret_cast<const uint4*>((const uint16_t*)p.u_in + rowo);
+              gw[0] = gv.x; gw[1] = gv.y; gw[2] = gv.z; gw[3] = gv.w;
+              uw[0] = uv.x; uw[1] = uv.y; uw[2] = uv.z; uw[3] = uv.w;
+            }
             float h[8];
             if constexpr (FP8) {
               // the forward's MXFP8 h: 8 codes, all in one block of 32
@@ -1033,11 +1044,22 @@ grouped_gemm_nt(Params p) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {  // two halves of 4 columns: fewer live registers
               float dg[4], du[4], hwv[4];
+              float4 g4 = make_float4(0.f, 0.f, 0.f, 0.f), u4 = g4;
+              if constexpr (FP8) {
+                g4 = *reinterpret_cast<const float4*>((const float*)p.g_in + rowo + 4 * hh);
+                u4 = *reinterpret_cast<const float4*>((const float*)p.u_in + rowo + 4 * hh);
+              }
 #pragma unroll
               for (int c4 = 0; c4 < 4; ++c4) {
                 const int c = 4 * hh + c4;
-                const float g = (c & 1) ? u2f(gw[c >> 1] & 0xFFFF0000u) : u2f(gw[c >> 1] << 16);
-                const float u = (c & 1) ? u2f(uw[c >> 1] & 0xFFFF0000u) : u2f(uw[c >> 1] << 16);
+                float g, u;
+                if constexpr (FP8) {
+                  g = c4 == 0 ? g4.x : c4 == 1 ? g4.y : c4 == 2 ? g4.z : g4.w;
+                  u = c4 == 0 ? u4.x : c4 == 1 ? u4.y : c4 == 2 ? u4.z : u4.w;
+                } else {
+                  g = (c & 1) ? u2f(gw[c >> 1] & 0xFFFF0000u) : u2f(gw[c >> 1] << 16);
+                  u = (c & 1) ? u2f(uw[c >> 1] & 0xFFFF0000u) : u2f(uw[c >> 1] << 16);
+                }
                 part += d[c] * h[c];
                 const float dh = w * d[c];
                 const float sg = sigmoid_f(g);

@@ -174,7 +174,7 @@ struct FwdArgs {
   const void* x;              // bf16 [T,H]
   const float* router_w;      // [T,k]
   void* out;                  // bf16 [T,H]
-  void* ctx_g;                // bf16 routed [rows_cap_max, I] then shared [T_max, I_s]; null = not kept
+  void* ctx_g;                // routed [rows_cap_max, I] then shared [T_max, I_s] (bf16; fp32 in MXFP8); null = not kept
   void* ctx_u;
   void* h;                    // h (routed rows then shared rows): bf16, or MXFP8 codes + scales
   void* y;                    // bf16 [(rows_cap_max + T_max), H]
@@ -221,9 +221,26 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
 // Columns of the per-row partial router-weight gradients.
 int dw_parts(const mok_config& c);
 
-// Context layout: G, U, h each [rows_cap_max*I + T_max*I_s] bf16.
+// Context layout: G, U, h, each [rows_cap_max*I + T_max*I_s] elements
+// (routed rows, then shared rows). BF16: G, U and h in bf16. MXFP8: G and U
+// in fp32 (the backward's SwiGLU derivative then starts from the values the
+// forward's h came from), h as E4M3 codes followed by one E8M0 scale per 32.
 inline size_t ctx_elems(const mok_config& c, const Layout& L) {
   return (size_t)L.rows_cap_max * c.intermediate + (size_t)c.max_tokens * c.shared_intermediate;
+}
+struct CtxLayout {
+  size_t g, u, h, total;  // byte offsets of G, U, h and the total size
+};
+inline CtxLayout ctx_layout(const mok_config& c, const Layout& L, bool mxfp8) {
+  const size_t ce = ctx_elems(c, L);
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  CtxLayout r;
+  const size_t gu = al(ce * (mxfp8 ? 4 : 2));
+  r.g = 0;
+  r.u = gu;
+  r.h = 2 * gu;
+  r.total = 2 * gu + (mxfp8 ? al(ce) + al(ce / 32) : al(ce * 2));
+  return r;
 }
 
 }  // namespace mok

@@ -34,17 +34,6 @@ from . import mxfp8
 from .schedule import build_schedule
 
 
-def bf16_round(v):
-    """Values rounded as a float32 result stored in bfloat16: to float32
-    (nearest even), then to the 8-bit-significand grid (nearest even).
-    Used where the layer saves an activation in bf16 and a later MXFP8
-    quantizer decides codes from it (see ``backward_mxfp8``).
-
-    Pin (tests/test_oracle_moe.py): equals torch's float32 -> bfloat16 cast."""
-    u = np.asarray(v, np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32).astype(np.float64)
-
 __all__ = ["sigmoid", "silu", "forward", "forward_per_token", "forward_tokens",
            "backward", "backward_slices", "forward_mxfp8", "forward_tokens_mxfp8", "backward_mxfp8",
            "segment_rows"]
@@ -449,7 +438,7 @@ def _qdq_rows_in_segment(v, q, block=32):
 
 def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
                    s_gate=None, s_up=None, s_down=None, sched=None,
-                   capacity_multiplier=1.0, expert_pad=32, qfun=None, saved=bf16_round):
+                   capacity_multiplier=1.0, expert_pad=32, qfun=None):
     """MXFP8 backward: every backward GEMM operand is quantized along that
     GEMM's contraction dimension, the forward activations being the MXFP8
     forward's (g, u from quantized x and weights; h quantized along I).
@@ -463,19 +452,19 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
     Reading: the pages give the MXFP8 backward only by name; quantizing each
     operand along its own contraction dimension is the plain reading of
     "MXFP8" (blocks along K) for a GEMM whose K differs from the forward's.
-    The backward differentiates through the context the forward saved
-    ([A] ``_MoKAutogradFunction``: backward consumes the saved context), and
-    the context holds g and u in bf16; since dg and du feed MXFP8 quantizers
-    (a rounding decision), they are formed from g and u as saved:
-    ``saved`` (default ``bf16_round``) is applied to g and u before the
-    SwiGLU derivative. ``saved=None`` keeps them exact.
+    Everything between the quantizers is exact (float64): g and u are the
+    MXFP8 forward's own, so this is the gradient of ``forward_mxfp8`` with
+    each backward GEMM's operands quantized.
 
-    Pin (tests/test_oracle_moe.py): with ``qfun`` the identity this must equal
-    ``backward`` (checks which operand goes where); the quantizer itself is
+    Pins (tests/test_oracle_moe.py): with ``qfun`` the identity this must equal
+    ``backward`` (checks which operand goes where); a recording ``qfun`` checks
+    that every operand is blocked along its GEMM's contraction dimension;
+    per-token locality (a token's dx and router-weight gradients do not move
+    when another token's grad_out does) and exact power-of-two equivariance
+    of dW_down rows pin the blocking semantically; the quantizer itself is
     pinned in tests/test_oracle_mxfp8.py.
     """
     q = mxfp8.qdq if qfun is None else qfun
-    sv = (lambda a: a) if saved is None else saved
     dO = np.asarray(grad_out, np.float64)
     xq = q(np.asarray(x, np.float64), axis=1)
     xraw = np.asarray(x, np.float64)
@@ -503,7 +492,6 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
         g = A @ Wg_f[e].T
         u = A @ Wu_f[e].T
         hq = q(silu(g) * u, axis=1)
-        g, u = sv(g), sv(u)
         dOq = q(dO[t], axis=1)
         dh_un = dOq @ Wd_b[e]
         dwr[a] = np.sum(dh_un * hq, axis=1)
@@ -530,7 +518,6 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
         g = xq @ Sg_f.T
         u = xq @ Su_f.T
         hq = q(silu(g) * u, axis=1)
-        g, u = sv(g), sv(u)
         dh = q(dO, axis=1) @ Sd_b
         s = sigmoid(g)
         dg = dh * u * s * (1.0 + g * (1.0 - s))
@@ -545,7 +532,7 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
 
 def backward_slices_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
                           s_gate=None, s_up=None, s_down=None, slot_row=None, tokens=(), expert_cols=(),
-                          shared_cols=(), saved=bf16_round):
+                          shared_cols=()):
     """Slices of ``backward_mxfp8`` computed on their own (for sampled checks
     at full sizes), with the same quantization of every operand:
       dx[t] and d_router_weights[t, :] for t in ``tokens``;
@@ -556,12 +543,9 @@ def backward_slices_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up
     index, which is the row order the 32-row blocks of Q_r follow. Weight
     and activation arguments may decode rows lazily (``w[e]``, ``x[t]``).
 
-    ``saved`` as in ``backward_mxfp8``.
-
     Pin (tests/test_oracle_moe.py): every slice equals ``backward_mxfp8`` on
     random small cases with drops and invalid ids."""
     q = mxfp8.qdq
-    sv = (lambda a: a) if saved is None else saved
     T = top_experts.shape[0]
     k = top_experts.shape[1]
     E = w_gate.shape[0]
@@ -603,7 +587,6 @@ def backward_slices_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up
             g = m["Wg_f"] @ xq
             u = m["Wu_f"] @ xq
             hq = qrow(silu(g) * u)
-            g, u = sv(g), sv(u)
             dh_un = dOq @ m["Wd_b"]
             if j is not None:
                 dwr[j] = dh_un @ hq
@@ -624,7 +607,7 @@ def backward_slices_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up
         hq_i = q(silu(g) * u, axis=1)[:, i - b0]
         dOq = q(dO, axis=1)
         dh = w * (dOq @ m["Wd_b"][:, i])
-        gi, ui = sv(g[:, i - b0]), sv(u[:, i - b0])
+        gi, ui = g[:, i - b0], u[:, i - b0]
         s = sigmoid(gi)
         dg = dh * ui * s * (1.0 + gi * (1.0 - s))
         du = dh * gi * s

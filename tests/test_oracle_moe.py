@@ -1,6 +1,10 @@
 """Pins for oracle.moe: dense-MLP special case via torch, two formulations,
 equivariance, linearity, autograd and finite differences for the backward,
-and structural checks of the MXFP8 emulation."""
+and checks of the MXFP8 emulation: its GEMM structure (identity quantizer),
+the blocking axis of every quantized operand (a table of each GEMM's
+contraction dimension), and properties that hold only when every operand is
+blocked along its own GEMM's contraction dimension (per-token locality,
+dead-row perturbations, exact power-of-two equivariance)."""
 import numpy as np
 import pytest
 import torch
@@ -167,7 +171,7 @@ def test_mxfp8_backward_structure_with_identity_quantizer():
     s = build_schedule(top, 3, 1.0, 32)
     dO = np.random.default_rng(14).standard_normal(x.shape)
     ident = lambda v, axis=-1: np.asarray(v, np.float64)
-    a = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, qfun=ident, saved=None)
+    a = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, qfun=ident)
     b = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
     for n in b:
         np.testing.assert_allclose(a[n], b[n], rtol=1e-11, atol=1e-11, err_msg=n)
@@ -246,28 +250,187 @@ def test_backward_slices_mxfp8_equal_backward_mxfp8(seed, mult):
         np.testing.assert_allclose(sl["d_s_down_cols"][i], full["d_s_down"][:, i], **tol)
 
 
-def test_bf16_round_matches_torch_cast():
-    rng = np.random.default_rng(21)
-    v = np.concatenate([rng.standard_normal(100000) * 10.0 ** rng.integers(-30, 30, size=100000),
-                        [0.0, -0.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 65504.0, 1e-40]])
-    ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
-    got = moe.bf16_round(v)
-    np.testing.assert_array_equal(got, ref)
-    assert np.signbit(got[v.size - 5])
+
+# ---------------------------------------------------------------------------
+# MXFP8: every operand blocked along its own GEMM's contraction dimension
+# ---------------------------------------------------------------------------
+
+def _axis_case(seed=31):
+    # distinct sizes (H = 64, I = 96, I_s = 160) and kept counts that are not
+    # multiples of 32, so that every (shape, blocked axis) pair names one
+    # operand class
+    rng = np.random.default_rng(seed)
+    T, H, I, E, k, Is = 45, 64, 96, 3, 2, 160
+    x = rng.standard_normal((T, H))
+    top = np.stack([np.arange(T) % 3, (np.arange(T) + 1) % 3], axis=1).astype(np.int64)
+    w = rng.uniform(0.1, 1.0, size=(T, k))
+    Wg, Wu = rng.standard_normal((E, I, H)) * 0.3, rng.standard_normal((E, I, H)) * 0.3
+    Wd = rng.standard_normal((E, H, I)) * 0.3
+    Sg, Su = rng.standard_normal((Is, H)) * 0.3, rng.standard_normal((Is, H)) * 0.3
+    Sd = rng.standard_normal((H, Is)) * 0.3
+    dO = rng.standard_normal((T, H))
+    return (T, H, I, E, k, Is), x, top, w, Wg, Wu, Wd, Sg, Su, Sd, dO
 
 
-def test_mxfp8_backward_saved_context_rounding_only_touches_swiglu_derivative():
-    # with an identity quantizer, rounding the saved g, u changes the result by
-    # the bf16 rounding only (relative 2^-8), and saved=None gives backward()
-    x, top, w, Wg, Wu, Wd, (Sg, Su, Sd) = rand_case(19, T=10, H=64, I=32, E=3, k=2, I_s=32)
+def _recording_qdq():
+    calls = []
+
+    def q(v, axis):
+        v = np.asarray(v, np.float64)
+        calls.append((tuple(v.shape), axis % v.ndim))
+        return mxfp8.qdq(v, axis)
+    return q, calls
+
+
+def test_mxfp8_every_operand_blocked_along_its_contraction_dimension():
+    """The blocked axis of every quantizer call, against a table written from
+    the rule "each GEMM's operands are blocked along that GEMM's contraction
+    dimension": gate/up contracts over H, down over I, dh over H, dA over I,
+    the weight gradients over an expert's rows (32-row blocks of its
+    zero-padded segment). A swapped axis anywhere changes the multiset."""
+    from collections import Counter
+    (T, H, I, E, k, Is), x, top, w, Wg, Wu, Wd, Sg, Su, Sd, dO = _axis_case()
+    s = build_schedule(top, E, 1.0, 32)
+    n = [int(v) for v in s["kept"]]
+    assert all(v % 32 for v in n) and T % 32
+    pad = lambda m: -(-m // 32) * 32  # noqa: E731
+    want = Counter()
+    # forward GEMMs (recomputed inside the backward): gate/up over H, down over I
+    want[((T, H), 1)] += 1                  # x, gate/up A operand
+    want[((E, I, H), 2)] += 2               # W_g, W_u, gate/up B operands
+    want[((Is, H), 1)] += 2                 # S_g, S_u
+    for ne in n:
+        want[((ne, I), 1)] += 1             # h of the routed rows (down's A operand)
+    want[((T, Is), 1)] += 1                 # h of the shared expert
+    # dh = grad_out rows . W_d, over H
+    want[((E, H, I), 1)] += 1               # W_d blocked along H
+    want[((H, Is), 0)] += 1                 # S_d blocked along H
+    for ne in n:
+        want[((ne, H), 1)] += 1             # grad_out rows of the expert
+    want[((T, H), 1)] += 1                  # grad_out rows of the shared expert
+    # dA = dG . W_g + dU . W_u, over I
+    want[((E, I, H), 1)] += 2               # W_g, W_u blocked along I
+    want[((Is, H), 0)] += 2                 # S_g, S_u blocked along I_s
+    for ne in n:
+        want[((ne, I), 1)] += 2             # dG, dU rows
+    want[((T, Is), 1)] += 2
+    # weight gradients, over the rows of each (padded) segment
+    for ne in n:
+        want[((pad(ne), H), 0)] += 2        # w * grad_out rows (dW_down), x rows (dW_gate, dW_up)
+        want[((pad(ne), I), 0)] += 3        # h (dW_down), dG (dW_gate), dU (dW_up)
+    want[((pad(T), H), 0)] += 2
+    want[((pad(T), Is), 0)] += 3
+    q, calls = _recording_qdq()
+    moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, qfun=q)
+    assert Counter(calls) == want, (Counter(calls) - want, want - Counter(calls))
+
+
+def _fwd_mx(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, s):
+    return moe.forward_mxfp8(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+
+
+def test_mxfp8_forward_token_locality():
+    """out[t] depends on x only through x[t]: x is blocked along H and h
+    along I, both inside one token's row. Blocks of 32 rows would couple the
+    tokens sharing a block (the 45 tokens span two such blocks)."""
+    _, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, _ = _axis_case(32)
     s = build_schedule(top, 3, 1.0, 32)
-    dO = np.random.default_rng(15).standard_normal(x.shape)
-    ident = lambda v, axis=-1: np.asarray(v, np.float64)
-    a = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, qfun=ident)
-    b = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
-    for n in b:
-        scale = np.max(np.abs(b[n]))
-        assert np.max(np.abs(a[n] - b[n])) <= 2.0 ** -6 * scale, n
-    # d_router_weights and dW_down do not use the derivative: unchanged
-    np.testing.assert_allclose(a["d_router_weights"], b["d_router_weights"], rtol=1e-11, atol=1e-11)
-    np.testing.assert_allclose(a["d_w_down"], b["d_w_down"], rtol=1e-11, atol=1e-11)
+    a = _fwd_mx(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, s)
+    for t0 in (0, 7, 40):
+        x2 = x.copy()
+        x2[t0] *= 37.0  # moves every block maximum of that row
+        b = _fwd_mx(x2, top, w, Wg, Wu, Wd, Sg, Su, Sd, s)
+        others = np.arange(x.shape[0]) != t0
+        np.testing.assert_array_equal(a[others], b[others])
+        assert np.max(np.abs(a[t0] - b[t0])) > 0
+
+
+def test_mxfp8_forward_weight_rows_are_blocked_along_h_and_down_rows_along_i():
+    """Gate/up weights blocked along H: with W_u[e, i] = 0 (so h_i = 0
+    whatever g_i is), rescaling W_g[e, i] by a non-power of two leaves the
+    output unchanged, and likewise W_u[e, i] with W_g[e, i] = 0; blocked along I, the other rows of its 32-row block
+    would be requantized. Down weights blocked along I: rescaling row h' of
+    W_d[e] moves only output column h'."""
+    _, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, _ = _axis_case(33)
+    s = build_schedule(top, 3, 1.0, 32)
+    Wu = Wu.copy()
+    Wu[1, 5] = 0.0
+    Su = Su.copy()
+    Su[70] = 0.0
+    a = _fwd_mx(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, s)
+    Wg2, Sg2 = Wg.copy(), Sg.copy()
+    Wg2[1, 5] *= 23.0
+    Sg2[70] *= 23.0
+    np.testing.assert_array_equal(a, _fwd_mx(x, top, w, Wg2, Wu, Wd, Sg2, Su, Sd, s))
+    # and the other way round: W_g[e, i] = 0 (g_i = 0, so h_i = 0), W_u[e, i] rescaled
+    Wg3, Sg3 = Wg.copy(), Sg.copy()
+    Wg3[2, 50] = 0.0
+    Sg3[3] = 0.0
+    a3 = _fwd_mx(x, top, w, Wg3, Wu, Wd, Sg3, Su, Sd, s)
+    Wu3, Su3 = Wu.copy(), Su.copy()
+    Wu3[2, 50] *= 23.0
+    Su3[3] *= 23.0
+    np.testing.assert_array_equal(a3, _fwd_mx(x, top, w, Wg3, Wu3, Wd, Sg3, Su3, Sd, s))
+    Wd2, Sd2 = Wd.copy(), Sd.copy()
+    Wd2[2, 9] *= 23.0
+    Sd2[9] *= 23.0
+    b = _fwd_mx(x, top, w, Wg, Wu, Wd2, Sg, Su, Sd2, s)
+    cols = np.arange(x.shape[1]) != 9
+    np.testing.assert_array_equal(a[:, cols], b[:, cols])
+    assert np.max(np.abs(a[:, 9] - b[:, 9])) > 0
+
+
+def test_mxfp8_backward_token_locality():
+    """dx[t] and the router-weight gradients of t depend on grad_out only
+    through grad_out[t]: grad_out rows are blocked along H and dG, dU along
+    I. 32-row blocks of either would couple tokens."""
+    _, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, dO = _axis_case(34)
+    s = build_schedule(top, 3, 1.0, 32)
+    a = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+    for t0 in (3, 33):
+        d2 = dO.copy()
+        d2[t0] *= 37.0
+        b = moe.backward_mxfp8(d2, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+        others = np.arange(x.shape[0]) != t0
+        for n in ("dx", "d_router_weights"):
+            np.testing.assert_array_equal(a[n][others], b[n][others])
+            assert np.max(np.abs(a[n][t0] - b[n][t0])) > 0
+
+
+def test_mxfp8_backward_down_weight_columns_are_blocked_along_h():
+    """dh = grad_out rows . W_d contracts over H, so W_d is blocked along H
+    (within one column i). With row i of W_g and W_u zero (g_i = u_i = 0,
+    hence h_i = dG_i = dU_i = 0 whatever dh_i is), rescaling column i of
+    W_d[e] leaves dx and the router-weight gradients unchanged; blocked
+    along I, the rest of its row block would be requantized."""
+    _, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, dO = _axis_case(35)
+    s = build_schedule(top, 3, 1.0, 32)
+    Wg, Wu, Sg, Su = Wg.copy(), Wu.copy(), Sg.copy(), Su.copy()
+    Wg[0, 40] = Wu[0, 40] = 0.0
+    Sg[100] = Su[100] = 0.0
+    a = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+    Wd2, Sd2 = Wd.copy(), Sd.copy()
+    Wd2[0, :, 40] *= 23.0
+    Sd2[:, 100] *= 23.0
+    b = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd2, Sg, Su, Sd2, sched=s)
+    for n in ("dx", "d_router_weights", "d_w_gate", "d_w_up", "d_s_gate", "d_s_up"):
+        np.testing.assert_array_equal(a[n], b[n], err_msg=n)
+
+
+def test_mxfp8_backward_down_weight_gradient_rows_scale_with_grad_out_columns():
+    """dW_down = Q_r(w * grad_out rows)^T Q_r(h) contracts over rows: the
+    blocks of the grad_out operand run down one column. Doubling column h' of
+    grad_out (a power of two: quantization commutes exactly) doubles row h'
+    of every dW_down and leaves the other rows bit-identical; blocks along H
+    would requantize the rest of the row block."""
+    _, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, dO = _axis_case(36)
+    s = build_schedule(top, 3, 1.0, 32)
+    a = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+    d2 = dO.copy()
+    d2[:, 17] *= 2.0
+    b = moe.backward_mxfp8(d2, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+    rows = np.arange(x.shape[1]) != 17
+    np.testing.assert_array_equal(a["d_w_down"][:, rows], b["d_w_down"][:, rows])
+    np.testing.assert_array_equal(2.0 * a["d_w_down"][:, 17], b["d_w_down"][:, 17])
+    np.testing.assert_array_equal(a["d_s_down"][rows], b["d_s_down"][rows])
+    np.testing.assert_array_equal(2.0 * a["d_s_down"][17], b["d_s_down"][17])
