@@ -35,8 +35,8 @@ from .schedule import build_schedule
 
 
 __all__ = ["sigmoid", "silu", "forward", "forward_per_token", "forward_tokens",
-           "backward", "backward_slices", "forward_mxfp8", "forward_tokens_mxfp8", "backward_mxfp8",
-           "segment_rows"]
+           "backward", "backward_slices", "quantize_weights_mxfp8", "forward_mxfp8", "forward_tokens_mxfp8",
+           "backward_mxfp8", "backward_slices_mxfp8", "segment_rows"]
 
 
 def sigmoid(z):
@@ -55,6 +55,15 @@ def segment_rows(sched: dict, e: int):
     return rows, a, a // sched["k"]
 
 
+def _token_set(T, tokens):
+    """Boolean mask over the T tokens (all True for tokens=None)."""
+    if tokens is None:
+        return np.ones(T, bool)
+    m = np.zeros(T, bool)
+    m[np.asarray(list(tokens), np.int64)] = True
+    return m
+
+
 def _expert_mlp(A, Wg, Wu, Wd):
     g = A @ Wg.T
     u = A @ Wu.T
@@ -64,10 +73,14 @@ def _expert_mlp(A, Wg, Wu, Wd):
 
 def forward(x, top_experts, router_weights, w_gate, w_up, w_down,
             s_gate=None, s_up=None, s_down=None, sched=None,
-            capacity_multiplier=1.0, expert_pad=32, return_parts=False):
+            capacity_multiplier=1.0, expert_pad=32, return_parts=False, tokens=None):
     """Layer output [T,H] in float64, expert-grouped formulation: each
     expert's kept rows are gathered, run through its SwiGLU MLP, weighted and
     added back at their tokens.
+
+    ``tokens`` (optional) restricts the work to the rows of those tokens (for
+    checks at full size; the schedule is still the whole batch's): their
+    output rows are exact, every other row is left 0.
 
     Pins (tests/test_oracle_moe.py): with E=1, k=1, w=1 and no shared expert
     it equals a dense SwiGLU MLP written with torch CPU ops; it equals the
@@ -81,19 +94,25 @@ def forward(x, top_experts, router_weights, w_gate, w_up, w_down,
     if sched is None:
         sched = build_schedule(top_experts, E, capacity_multiplier, expert_pad)
     wflat = np.asarray(router_weights, np.float64).reshape(-1)
+    sel = _token_set(T, tokens)
     out = np.zeros((T, H))
     parts = {}
     for e in range(E):
         rows, a, t = segment_rows(sched, e)
+        keep = sel[t]
+        rows, a, t = rows[keep], a[keep], t[keep]
         if rows.size == 0:
             continue
-        g, u, h, y = _expert_mlp(x[t], w_gate[e], w_up[e], w_down[e])
+        g, u, h, y = _expert_mlp(x[t], np.asarray(w_gate[e], np.float64), np.asarray(w_up[e], np.float64),
+                                 np.asarray(w_down[e], np.float64))
         np.add.at(out, t, wflat[a][:, None] * y)
         if return_parts:
             parts[e] = dict(rows=rows, a=a, t=t, g=g, u=u, h=h, y=y)
     if s_gate is not None:
-        g, u, h, y = _expert_mlp(x, s_gate, s_up, s_down)
-        out += y
+        ts = np.flatnonzero(sel)
+        g, u, h, y = _expert_mlp(x[ts], np.asarray(s_gate, np.float64), np.asarray(s_up, np.float64),
+                                 np.asarray(s_down, np.float64))
+        out[ts] += y
         if return_parts:
             parts["shared"] = dict(g=g, u=u, h=h, y=y)
     if return_parts:
@@ -157,8 +176,13 @@ def forward_tokens(tokens, x, top_experts, router_weights, w_gate, w_up, w_down,
 
 def backward(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
              s_gate=None, s_up=None, s_down=None, sched=None,
-             capacity_multiplier=1.0, expert_pad=32):
+             capacity_multiplier=1.0, expert_pad=32, tokens=None, dw_experts=None):
     """Gradients of sum(grad_out * out) with respect to every float input.
+
+    ``tokens`` and ``dw_experts`` (optional) restrict the work for checks at
+    full size: dx and d_router_weights are exact for the listed tokens, the
+    weight gradients for the listed experts (the string "shared" names the
+    shared expert); entries outside them are unspecified.
 
     Returns dict: dx [T,H], d_router_weights [T,k], d_w_gate, d_w_up
     [E,I,H], d_w_down [E,H,I], d_s_gate, d_s_up [I_s,H], d_s_down [H,I_s]
@@ -186,6 +210,8 @@ def backward(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
     if sched is None:
         sched = build_schedule(top_experts, E, capacity_multiplier, expert_pad)
     wflat = np.asarray(router_weights, np.float64).reshape(-1)
+    sel = _token_set(T, tokens)
+    want_dw = (lambda e: True) if dw_experts is None else (lambda e: e in dw_experts)  # noqa: E731
     dx = np.zeros((T, H))
     dwr = np.zeros(T * k)
     dWg = np.zeros((E, I, H))
@@ -193,33 +219,42 @@ def backward(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
     dWd = np.zeros((E, H, I))
     for e in range(E):
         rows, a, t = segment_rows(sched, e)
+        if not want_dw(e):  # the weight gradients need every row; dx and dw only the listed tokens'
+            keep = sel[t]
+            rows, a, t = rows[keep], a[keep], t[keep]
         if rows.size == 0:
             continue
+        Wg_e, Wu_e, Wd_e = (np.asarray(w[e], np.float64) for w in (w_gate, w_up, w_down))
         A = x[t]
-        g, u, h, y = _expert_mlp(A, w_gate[e], w_up[e], w_down[e])
+        g, u, h, y = _expert_mlp(A, Wg_e, Wu_e, Wd_e)
         dOt = dO[t]
         dwr[a] = np.sum(dOt * y, axis=1)
         dy = wflat[a][:, None] * dOt
-        dh = dy @ w_down[e]
+        dh = dy @ Wd_e
         s = sigmoid(g)
         dg = dh * u * s * (1.0 + g * (1.0 - s))
         du = dh * g * s
-        dWd[e] = dy.T @ h
-        dWg[e] = dg.T @ A
-        dWu[e] = du.T @ A
-        np.add.at(dx, t, dg @ w_gate[e] + du @ w_up[e])
+        if want_dw(e):
+            dWd[e] = dy.T @ h
+            dWg[e] = dg.T @ A
+            dWu[e] = du.T @ A
+        np.add.at(dx, t, dg @ Wg_e + du @ Wu_e)
     res = dict(dx=dx, d_router_weights=dwr.reshape(T, k), d_w_gate=dWg, d_w_up=dWu,
                d_w_down=dWd, d_s_gate=None, d_s_up=None, d_s_down=None)
     if s_gate is not None:
-        g, u, h, y = _expert_mlp(x, s_gate, s_up, s_down)
-        dh = dO @ s_down
+        Sg, Su, Sd = (np.asarray(w, np.float64) for w in (s_gate, s_up, s_down))
+        ts = np.arange(T) if want_dw("shared") else np.flatnonzero(sel)
+        xs, dOs = x[ts], dO[ts]
+        g, u, h, y = _expert_mlp(xs, Sg, Su, Sd)
+        dh = dOs @ Sd
         s = sigmoid(g)
         dg = dh * u * s * (1.0 + g * (1.0 - s))
         du = dh * g * s
-        res["d_s_down"] = dO.T @ h
-        res["d_s_gate"] = dg.T @ x
-        res["d_s_up"] = du.T @ x
-        dx += dg @ s_gate + du @ s_up
+        if want_dw("shared"):
+            res["d_s_down"] = dOs.T @ h
+            res["d_s_gate"] = dg.T @ xs
+            res["d_s_up"] = du.T @ xs
+        dx[ts] += dg @ Sg + du @ Su
     return res
 
 
@@ -323,10 +358,42 @@ def backward_slices(grad_out, x, top_experts, router_weights, w_gate, w_up, w_do
 # MXFP8 emulation
 # ---------------------------------------------------------------------------
 
+def quantize_weights_mxfp8(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None,
+                           for_backward=False, qfun=None):
+    """The weights as the MXFP8 GEMMs read them: dequantize(quantize(.)) in
+    blocks of 32 along the contraction dimension of the GEMM that reads them.
+      forward:  gate/up blocked along H (W_g, W_u [E,I,H] axis 2; S_g, S_u
+                [I_s,H] axis 1), down along I (W_d [E,H,I] axis 2; S_d
+                [H,I_s] axis 1): keys Wg_f, Wu_f, Wd_f (Sg_f, Su_f, Sd_f);
+      backward: gate/up along H again (the forward is recomputed), down along
+                H (dh contracts over H: W_d axis 1, S_d axis 0) and gate/up
+                along I (dA contracts over I: W_g, W_u axis 1, S_g, S_u axis
+                0): keys Wg_f, Wu_f, Wd_b, Wg_b, Wu_b (Sg_f, Su_f, Sd_b, Sg_b,
+                Su_b).
+    The shared keys are absent without a shared expert. ``qfun`` replaces
+    the quantizer (signature of ``mxfp8.qdq``); the test suite passes one that
+    records its calls, or one that runs ``mxfp8.qdq`` on slices in parallel
+    (the blocks never cross the slices, so the values are the same)."""
+    q = mxfp8.qdq if qfun is None else qfun
+    f = lambda a: np.asarray(a, np.float64)  # noqa: E731
+    r = dict(Wg_f=q(f(w_gate), axis=2), Wu_f=q(f(w_up), axis=2))
+    if for_backward:
+        r.update(Wd_b=q(f(w_down), axis=1), Wg_b=q(f(w_gate), axis=1), Wu_b=q(f(w_up), axis=1))
+    else:
+        r.update(Wd_f=q(f(w_down), axis=2))
+    if s_gate is not None:
+        r.update(Sg_f=q(f(s_gate), axis=1), Su_f=q(f(s_up), axis=1))
+        if for_backward:
+            r.update(Sd_b=q(f(s_down), axis=0), Sg_b=q(f(s_gate), axis=0), Su_b=q(f(s_up), axis=0))
+        else:
+            r.update(Sd_f=q(f(s_down), axis=1))
+    return r
+
+
 def forward_mxfp8(x, top_experts, router_weights, w_gate, w_up, w_down,
                   s_gate=None, s_up=None, s_down=None, sched=None,
                   capacity_multiplier=1.0, expert_pad=32, return_parts=False,
-                  quantize_h=True):
+                  quantize_h=True, qweights=None, tokens=None):
     """MXFP8 forward: x, W_g, W_u (blocks along H) and W_d (blocks along I),
     shared weights included, are replaced by dequantize(quantize(.)); h is
     computed in float64 from those and itself quantized along I before the
@@ -337,17 +404,23 @@ def forward_mxfp8(x, top_experts, router_weights, w_gate, w_up, w_down,
     the quantization of x and h along the contraction dimension inside the
     layer is the plain reading of "MXFP8 forward" (blocks along K).
 
+    ``qweights`` (optional): the result of ``quantize_weights_mxfp8`` for
+    these weights, computed beforehand. ``tokens`` (optional) restricts the
+    work to those tokens' rows as in ``forward`` (other rows are left 0).
+
     Pin (tests/test_oracle_moe.py): when x and every weight already sit on
     the MX grid, the only difference to ``forward`` is h's quantization, so
     replacing the h step by the identity must reproduce ``forward`` exactly.
     """
     q = mxfp8.qdq
     qh = mxfp8.qdq if quantize_h else (lambda v, axis: v)
-    xq = q(np.asarray(x, np.float64), axis=1)
-    Wg = q(np.asarray(w_gate, np.float64), axis=2)
-    Wu = q(np.asarray(w_up, np.float64), axis=2)
-    Wd = q(np.asarray(w_down, np.float64), axis=2)
-    T, H = xq.shape
+    if qweights is None:
+        qweights = quantize_weights_mxfp8(w_gate, w_up, w_down, s_gate, s_up, s_down)
+    Wg, Wu, Wd = qweights["Wg_f"], qweights["Wu_f"], qweights["Wd_f"]
+    T, H = np.shape(x)
+    sel = _token_set(T, tokens)
+    xq = np.zeros((T, H))
+    xq[sel] = q(np.asarray(x, np.float64)[sel], axis=1)  # blocks along H: rows are independent
     E = Wg.shape[0]
     if sched is None:
         sched = build_schedule(top_experts, E, capacity_multiplier, expert_pad)
@@ -356,6 +429,8 @@ def forward_mxfp8(x, top_experts, router_weights, w_gate, w_up, w_down,
     parts = {}
     for e in range(E):
         rows, a, t = segment_rows(sched, e)
+        keep = sel[t]
+        rows, a, t = rows[keep], a[keep], t[keep]
         if rows.size == 0:
             continue
         A = xq[t]
@@ -367,13 +442,11 @@ def forward_mxfp8(x, top_experts, router_weights, w_gate, w_up, w_down,
         if return_parts:
             parts[e] = dict(rows=rows, a=a, t=t, g=g, u=u, hq=h, y=y)
     if s_gate is not None:
-        Sg = q(np.asarray(s_gate, np.float64), axis=1)
-        Su = q(np.asarray(s_up, np.float64), axis=1)
-        Sd = q(np.asarray(s_down, np.float64), axis=1)
-        g = xq @ Sg.T
-        u = xq @ Su.T
+        ts = np.flatnonzero(sel)
+        g = xq[ts] @ qweights["Sg_f"].T
+        u = xq[ts] @ qweights["Su_f"].T
         h = qh(silu(g) * u, axis=1)
-        out += h @ Sd.T
+        out[ts] += h @ qweights["Sd_f"].T
         if return_parts:
             parts["shared"] = dict(g=g, u=u, hq=h)
     if return_parts:
@@ -438,7 +511,8 @@ def _qdq_rows_in_segment(v, q, block=32):
 
 def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
                    s_gate=None, s_up=None, s_down=None, sched=None,
-                   capacity_multiplier=1.0, expert_pad=32, qfun=None):
+                   capacity_multiplier=1.0, expert_pad=32, qfun=None, qweights=None,
+                   tokens=None, dw_experts=None):
     """MXFP8 backward: every backward GEMM operand is quantized along that
     GEMM's contraction dimension, the forward activations being the MXFP8
     forward's (g, u from quantized x and weights; h quantized along I).
@@ -456,6 +530,11 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
     MXFP8 forward's own, so this is the gradient of ``forward_mxfp8`` with
     each backward GEMM's operands quantized.
 
+    ``qweights`` (optional): ``quantize_weights_mxfp8(..., for_backward=True)``
+    of these weights, computed beforehand. ``tokens`` and ``dw_experts``
+    restrict the work as in ``backward`` (a listed expert's weight gradients
+    use all of its rows, as its 32-row blocks need).
+
     Pins (tests/test_oracle_moe.py): with ``qfun`` the identity this must equal
     ``backward`` (checks which operand goes where); a recording ``qfun`` checks
     that every operand is blocked along its GEMM's contraction dimension;
@@ -465,17 +544,17 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
     pinned in tests/test_oracle_mxfp8.py.
     """
     q = mxfp8.qdq if qfun is None else qfun
+    if qweights is None:
+        qweights = quantize_weights_mxfp8(w_gate, w_up, w_down, s_gate, s_up, s_down, for_backward=True, qfun=q)
+    Wg_f, Wu_f, Wd_b, Wg_b, Wu_b = (qweights[n] for n in ("Wg_f", "Wu_f", "Wd_b", "Wg_b", "Wu_b"))
     dO = np.asarray(grad_out, np.float64)
-    xq = q(np.asarray(x, np.float64), axis=1)
     xraw = np.asarray(x, np.float64)
     T, H = xraw.shape
+    sel = _token_set(T, tokens)
+    want_dw = (lambda e: True) if dw_experts is None else (lambda e: e in dw_experts)  # noqa: E731
+    xq = q(xraw, axis=1)
     k = top_experts.shape[1]
-    E, I, _ = w_gate.shape
-    Wg_f = q(np.asarray(w_gate, np.float64), axis=2)
-    Wu_f = q(np.asarray(w_up, np.float64), axis=2)
-    Wd_b = q(np.asarray(w_down, np.float64), axis=1)       # [E,H,I] blocks along H
-    Wg_b = q(np.asarray(w_gate, np.float64), axis=1)       # [E,I,H] blocks along I
-    Wu_b = q(np.asarray(w_up, np.float64), axis=1)
+    E, I, _ = Wg_f.shape
     if sched is None:
         sched = build_schedule(top_experts, E, capacity_multiplier, expert_pad)
     wflat = np.asarray(router_weights, np.float64).reshape(-1)
@@ -486,6 +565,9 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
     dWd = np.zeros((E, H, I))
     for e in range(E):
         rows, a, t = segment_rows(sched, e)
+        if not want_dw(e):  # the weight gradients need every row; dx and dw only the listed tokens'
+            keep = sel[t]
+            rows, a, t = rows[keep], a[keep], t[keep]
         if rows.size == 0:
             continue
         A = xq[t]
@@ -502,31 +584,29 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
         du = dh * g * s
         dx_rows = q(dg, axis=1) @ Wg_b[e] + q(du, axis=1) @ Wu_b[e]
         np.add.at(dx, t, dx_rows)
-        dy = w * dO[t]
-        dWd[e] = _qdq_rows_in_segment(dy, q).T @ _qdq_rows_in_segment(hq, q)
-        xr = _qdq_rows_in_segment(xraw[t], q)
-        dWg[e] = _qdq_rows_in_segment(dg, q).T @ xr
-        dWu[e] = _qdq_rows_in_segment(du, q).T @ xr
+        if want_dw(e):
+            dy = w * dO[t]
+            dWd[e] = _qdq_rows_in_segment(dy, q).T @ _qdq_rows_in_segment(hq, q)
+            xr = _qdq_rows_in_segment(xraw[t], q)
+            dWg[e] = _qdq_rows_in_segment(dg, q).T @ xr
+            dWu[e] = _qdq_rows_in_segment(du, q).T @ xr
     res = dict(dx=dx, d_router_weights=dwr.reshape(T, k), d_w_gate=dWg, d_w_up=dWu,
                d_w_down=dWd, d_s_gate=None, d_s_up=None, d_s_down=None)
     if s_gate is not None:
-        Sg_f = q(np.asarray(s_gate, np.float64), axis=1)
-        Su_f = q(np.asarray(s_up, np.float64), axis=1)
-        Sd_b = q(np.asarray(s_down, np.float64), axis=0)
-        Sg_b = q(np.asarray(s_gate, np.float64), axis=0)
-        Su_b = q(np.asarray(s_up, np.float64), axis=0)
-        g = xq @ Sg_f.T
-        u = xq @ Su_f.T
+        ts = np.arange(T) if want_dw("shared") else np.flatnonzero(sel)
+        g = xq[ts] @ qweights["Sg_f"].T
+        u = xq[ts] @ qweights["Su_f"].T
         hq = q(silu(g) * u, axis=1)
-        dh = q(dO, axis=1) @ Sd_b
+        dh = q(dO[ts], axis=1) @ qweights["Sd_b"]
         s = sigmoid(g)
         dg = dh * u * s * (1.0 + g * (1.0 - s))
         du = dh * g * s
-        dx += q(dg, axis=1) @ Sg_b + q(du, axis=1) @ Su_b
-        res["d_s_down"] = _qdq_rows_in_segment(dO, q).T @ _qdq_rows_in_segment(hq, q)
-        xr = _qdq_rows_in_segment(xraw, q)
-        res["d_s_gate"] = _qdq_rows_in_segment(dg, q).T @ xr
-        res["d_s_up"] = _qdq_rows_in_segment(du, q).T @ xr
+        dx[ts] += q(dg, axis=1) @ qweights["Sg_b"] + q(du, axis=1) @ qweights["Su_b"]
+        if want_dw("shared"):
+            res["d_s_down"] = _qdq_rows_in_segment(dO, q).T @ _qdq_rows_in_segment(hq, q)
+            xr = _qdq_rows_in_segment(xraw, q)
+            res["d_s_gate"] = _qdq_rows_in_segment(dg, q).T @ xr
+            res["d_s_up"] = _qdq_rows_in_segment(du, q).T @ xr
     return res
 
 

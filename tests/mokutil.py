@@ -1,5 +1,7 @@
 """Shared helpers of the test suite: device transfer of seeded inputs,
-lazily decoded bf16 weight arrays for the oracle, tolerance checks.
+lazily decoded bf16 weight arrays for the oracle, tolerance checks, and a
+process pool that runs the oracle's own MXFP8 quantizer on slices of large
+weight tensors in parallel.
 
 Holds none of the layer's arithmetic."""
 from __future__ import annotations
@@ -79,3 +81,54 @@ def assert_close_inf(got: np.ndarray, ref: np.ndarray, tol: float, what: str = "
     err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
     assert err <= tol * max(scale, 1e-30), f"{what}: max|err| {err:.4g} > {tol} * {scale:.4g}"
     return err, scale
+
+
+# ---------------------------------------------------------------------------
+# The oracle's quantizer on slices of a large tensor, in worker processes
+# ---------------------------------------------------------------------------
+
+def _qdq_chunk(args):
+    from oracle import mxfp8
+    v, axis = args
+    return mxfp8.qdq(v, axis)
+
+
+_POOL = None
+
+
+def _pool():
+    # spawned (not forked) workers: the parent may hold a GPU context
+    global _POOL
+    if _POOL is None:
+        import multiprocessing as mp
+        n = max(1, min(16, os.cpu_count() or 1))
+        _POOL = mp.get_context("spawn").Pool(n)
+    return _POOL
+
+
+def par_qdq(v, axis):
+    """``oracle.mxfp8.qdq(v, axis)``, computed on slices of ``v`` along
+    another axis in worker processes. Blocks of 32 run along ``axis`` only,
+    so no block crosses a slice and the values are those of one call."""
+    from oracle import mxfp8
+    v = np.ascontiguousarray(v, np.float64)
+    axis %= v.ndim
+    split = 0 if axis != 0 else 1
+    n = v.shape[split]
+    if v.size < (1 << 22) or n < 2:
+        return mxfp8.qdq(v, axis)
+    pieces = min(n, 64)
+    bounds = [n * i // pieces for i in range(pieces + 1)]
+    sl = lambda lo, hi: tuple(slice(lo, hi) if d == split else slice(None) for d in range(v.ndim))  # noqa: E731
+    outs = _pool().map(_qdq_chunk, [(v[sl(lo, hi)], axis) for lo, hi in zip(bounds[:-1], bounds[1:])],
+                       chunksize=1)
+    return np.concatenate(outs, axis=split)
+
+
+def oracle_qweights(inp: dict, for_backward: bool = False) -> dict:
+    """``oracle.moe.quantize_weights_mxfp8`` of a workload's weights, with
+    the quantizer run in parallel (``par_qdq``)."""
+    from oracle import moe as omoe
+    return omoe.quantize_weights_mxfp8(f64(inp["w_gate"]), f64(inp["w_up"]), f64(inp["w_down"]),
+                                       f64(inp["s_gate"]), f64(inp["s_up"]), f64(inp["s_down"]),
+                                       for_backward=for_backward, qfun=par_qdq)

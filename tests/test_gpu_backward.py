@@ -4,10 +4,10 @@ reuses the schedule and the context saved by mok_forward.
 
 Small cases are compared element by element over whole tensors (several
 tiles, ragged expert segments, drops and invalid ids, a shared expert of
-another width). The 32768-token workload runs at full size with slices
-computed one by one by the oracle: dx and the router-weight gradients of
-sampled tokens, rows of dW_gate / dW_up and columns of dW_down of sampled
-(expert, i) pairs, and the same slices of the shared expert."""
+another width). The 32768-token workload runs at full size: its forward
+output, dx and router-weight gradients of 1024 sampled tokens, and the whole
+weight gradients of four routed experts and of the shared expert, against
+the expert-grouped oracle restricted to those tokens and experts."""
 import numpy as np
 import pytest
 
@@ -100,40 +100,38 @@ def test_backward_bf16_deterministic():
         assert torch.equal(g1[k_].view(torch.uint8), g2[k_].view(torch.uint8)), k_
 
 
-def test_backward_bf16_32768_tokens_sampled():
+def test_backward_bf16_32768_tokens_full_size():
+    """The 32768-token workload at full size: the forward output and the
+    dx and router-weight gradients of 1024 sampled tokens, and the whole
+    weight gradients of four routed experts and of the shared expert,
+    against the expert-grouped float64 oracle (restricted to those tokens
+    and experts, its schedule the whole batch's)."""
     c = CONFIGS["t32768_bf16_fwdbwd"]
     inp = make_inputs(c)
     print("generated 32768-token inputs", flush=True)
-    _, g, _ = gpu_fwd_bwd(c, inp, c.capacity_multiplier)
+    out, g, _ = gpu_fwd_bwd(c, inp, c.capacity_multiplier)
     print("gpu forward+backward done", flush=True)
-    sched = oracle_schedule(inp["top_experts"], c.E, c.capacity_multiplier, c.expert_pad)
     rng = np.random.default_rng(4)
-    toks = sorted(set([0, c.T - 1] + list(rng.integers(0, c.T, size=4))))
-    cols = [(0, 0), (17, int(rng.integers(0, c.I))), (31, c.I - 1)]
-    scols = [0, int(rng.integers(0, c.I_s))]
-    sl = omoe.backward_slices(Bf16Array(inp["grad_out"]), Bf16Array(inp["x"]), inp["top_experts"],
-                              inp["router_weights"], Bf16Array(inp["w_gate"]), Bf16Array(inp["w_up"]),
-                              Bf16Array(inp["w_down"]), f64(inp["s_gate"]), f64(inp["s_up"]),
-                              f64(inp["s_down"]), slot_row=sched["slot_row"], tokens=toks, expert_cols=cols,
-                              shared_cols=scols)
-    dx = np64(g["dx"][toks])
-    assert_close_inf(dx, np.stack([sl["dx"][t] for t in toks]), TOL_BF16, "dx")
-    assert_close_inf(np64(g["d_router_weights"][toks]), np.stack([sl["d_router_weights"][t] for t in toks]),
-                     TOL_BF16, "d_router_weights")
-    wg = g["d_routed_gate"]
-    wu = g["d_routed_up"]
-    wd = g["d_routed_down"]
-    assert_close_inf(np.stack([np64(wg[e, i]) for e, i in cols]), np.stack([sl["d_w_gate_rows"][p] for p in cols]),
-                     TOL_BF16, "dW_gate rows")
-    assert_close_inf(np.stack([np64(wu[e, i]) for e, i in cols]), np.stack([sl["d_w_up_rows"][p] for p in cols]),
-                     TOL_BF16, "dW_up rows")
-    assert_close_inf(np.stack([np64(wd[e, :, i]) for e, i in cols]),
-                     np.stack([sl["d_w_down_cols"][p] for p in cols]), TOL_BF16, "dW_down cols")
-    assert_close_inf(np.stack([np64(g["d_shared_gate"][i]) for i in scols]),
-                     np.stack([sl["d_s_gate_rows"][i] for i in scols]), TOL_BF16, "dS_gate rows")
-    assert_close_inf(np.stack([np64(g["d_shared_up"][i]) for i in scols]),
-                     np.stack([sl["d_s_up_rows"][i] for i in scols]), TOL_BF16, "dS_up rows")
-    assert_close_inf(np.stack([np64(g["d_shared_down"][:, i]) for i in scols]),
-                     np.stack([sl["d_s_down_cols"][i] for i in scols]), TOL_BF16, "dS_down cols")
+    toks = np.unique(np.concatenate([[0, c.T - 1], rng.choice(c.T, size=1022, replace=False)]))
+    experts = [0, 11, 22, c.E - 1]
+    wg, wu, wd = Bf16Array(inp["w_gate"]), Bf16Array(inp["w_up"]), Bf16Array(inp["w_down"])
+    args = (f64(inp["x"]), inp["top_experts"], inp["router_weights"], wg, wu, wd,
+            f64(inp["s_gate"]), f64(inp["s_up"]), f64(inp["s_down"]))
+    ref_out = omoe.forward(*args, tokens=toks)
+    err, scale = assert_close_inf(np64(out[toks]), ref_out[toks], TOL_BF16, "out")
+    print(f"  out ({toks.size} tokens): max err {err:.3g} of max {scale:.3g}", flush=True)
+    ref = omoe.backward(f64(inp["grad_out"]), *args, tokens=toks, dw_experts=experts + ["shared"])
+    print("oracle backward done", flush=True)
+
+    def check(got, want, name):
+        err, scale = assert_close_inf(got, want, TOL_BF16, name)
+        print(f"  {name}: max err {err:.3g} of max {scale:.3g}", flush=True)
+
+    check(np64(g["dx"][toks]), ref["dx"][toks], f"dx ({toks.size} tokens)")
+    check(np64(g["d_router_weights"][toks]), ref["d_router_weights"][toks], "d_router_weights")
+    for gname, rname in (("d_routed_gate", "d_w_gate"), ("d_routed_up", "d_w_up"), ("d_routed_down", "d_w_down")):
+        check(np.stack([np64(g[gname][e]) for e in experts]), ref[rname][experts], f"{gname} experts {experts}")
+    for gname, rname in (("d_shared_gate", "d_s_gate"), ("d_shared_up", "d_s_up"), ("d_shared_down", "d_s_down")):
+        check(np64(g[gname]), ref[rname], gname)
     for k_, v in g.items():
         assert torch.isfinite(v.float()).all(), k_

@@ -8,14 +8,13 @@ device.
 
 Small cases are compared over whole tensors (ragged segments of several
 32-row blocks, drops and invalid ids, no shared expert, experts that get no
-rows). The 8192-token workload runs at full size with slices computed one by
-one by the oracle: dx and router-weight gradients of sampled tokens, rows of
-dW_gate / dW_up and columns of dW_down of sampled (expert, i) pairs, and the
-shared expert's slices."""
+rows). The 8192-token workload runs at full size: the forward output of
+every token, dx and router-weight gradients of 1024 sampled tokens, and the
+whole weight gradients of four routed experts and of the shared expert."""
 import numpy as np
 import pytest
 
-from mokutil import TOL_MXFP8, Bf16Array, assert_close_inf, f64, to_dev
+from mokutil import TOL_MXFP8, assert_close_inf, f64, oracle_qweights, to_dev
 
 from oracle import moe as omoe
 from oracle.schedule import build_schedule as oracle_schedule
@@ -125,40 +124,40 @@ def test_backward_mxfp8_rejects_unsupported_shapes():
     assert ei.value.status == MOK_ERR_UNSUPPORTED
 
 
-def test_backward_mxfp8_8192_tokens_sampled():
+def test_backward_mxfp8_8192_tokens_full_size():
+    """The MXFP8 forward+backward at the 8192-token shape, full size: the
+    forward output of every token, dx and router-weight gradients of 1024
+    sampled tokens, and the whole weight gradients of four routed experts
+    and of the shared expert, against the MXFP8 oracle (restricted to those
+    tokens and experts; its weight quantization runs on slices in worker
+    processes)."""
     c = CONFIGS["t8192_mxfp8_fwdbwd"]
     inp = make_inputs(c)
     print("generated 8192-token inputs", flush=True)
-    _, g, _ = gpu_fwd_bwd_mxfp8(c, inp, c.capacity_multiplier)
+    out, g, _ = gpu_fwd_bwd_mxfp8(c, inp, c.capacity_multiplier)
     print("gpu forward+backward done", flush=True)
-    sched = oracle_schedule(inp["top_experts"], c.E, c.capacity_multiplier, c.expert_pad)
     rng = np.random.default_rng(5)
-    toks = sorted(set([0, c.T - 1] + list(rng.integers(0, c.T, size=4))))
-    cols = [(0, 0), (37, int(rng.integers(0, c.I))), (c.E - 1, c.I - 1)]
-    scols = [0, int(rng.integers(0, c.I_s))]
-    sl = omoe.backward_slices_mxfp8(Bf16Array(inp["grad_out"]), Bf16Array(inp["x"]), inp["top_experts"],
-                                    inp["router_weights"], Bf16Array(inp["w_gate"]), Bf16Array(inp["w_up"]),
-                                    Bf16Array(inp["w_down"]), f64(inp["s_gate"]), f64(inp["s_up"]),
-                                    f64(inp["s_down"]), slot_row=sched["slot_row"], tokens=toks, expert_cols=cols,
-                                    shared_cols=scols)
-    print("oracle slices done", flush=True)
-    def check(got, ref, name):
-        err, scale = assert_close_inf(got, ref, TOL_MXFP8, name)
+    toks = np.unique(np.concatenate([[0, c.T - 1], rng.choice(c.T, size=1022, replace=False)]))
+    experts = [0, 37, 64, c.E - 1]
+    sh = dict(s_gate=f64(inp["s_gate"]), s_up=f64(inp["s_up"]), s_down=f64(inp["s_down"]))
+    ref_out = omoe.forward_mxfp8(f64(inp["x"]), inp["top_experts"], inp["router_weights"], None, None, None,
+                                 qweights=oracle_qweights(inp), **sh)
+    err, scale = assert_close_inf(np64(out), ref_out, TOL_MXFP8, "out")
+    print(f"  out (all tokens): max err {err:.3g} of max {scale:.3g}", flush=True)
+    ref = omoe.backward_mxfp8(f64(inp["grad_out"]), f64(inp["x"]), inp["top_experts"], inp["router_weights"],
+                              None, None, None, qweights=oracle_qweights(inp, for_backward=True), tokens=toks,
+                              dw_experts=experts + ["shared"], **sh)
+    print("oracle backward done", flush=True)
+
+    def check(got, want, name):
+        err, scale = assert_close_inf(got, want, TOL_MXFP8, name)
         print(f"  {name}: max err {err:.3g} of max {scale:.3g}", flush=True)
 
-    check(np64(g["dx"][toks]), np.stack([sl["dx"][t] for t in toks]), "dx")
-    check(np64(g["d_router_weights"][toks]), np.stack([sl["d_router_weights"][t] for t in toks]), "d_router_weights")
-    wg, wu, wd = g["d_routed_gate"], g["d_routed_up"], g["d_routed_down"]
-    check(np.stack([np64(wg[e, i]) for e, i in cols]), np.stack([sl["d_w_gate_rows"][p] for p in cols]),
-          "dW_gate rows")
-    check(np.stack([np64(wu[e, i]) for e, i in cols]), np.stack([sl["d_w_up_rows"][p] for p in cols]), "dW_up rows")
-    check(np.stack([np64(wd[e, :, i]) for e, i in cols]), np.stack([sl["d_w_down_cols"][p] for p in cols]),
-          "dW_down cols")
-    check(np.stack([np64(g["d_shared_gate"][i]) for i in scols]), np.stack([sl["d_s_gate_rows"][i] for i in scols]),
-          "dS_gate rows")
-    check(np.stack([np64(g["d_shared_up"][i]) for i in scols]), np.stack([sl["d_s_up_rows"][i] for i in scols]),
-          "dS_up rows")
-    check(np.stack([np64(g["d_shared_down"][:, i]) for i in scols]),
-          np.stack([sl["d_s_down_cols"][i] for i in scols]), "dS_down cols")
+    check(np64(g["dx"][toks]), ref["dx"][toks], f"dx ({toks.size} tokens)")
+    check(np64(g["d_router_weights"][toks]), ref["d_router_weights"][toks], "d_router_weights")
+    for gname, rname in (("d_routed_gate", "d_w_gate"), ("d_routed_up", "d_w_up"), ("d_routed_down", "d_w_down")):
+        check(np.stack([np64(g[gname][e]) for e in experts]), ref[rname][experts], f"{gname} experts {experts}")
+    for gname, rname in (("d_shared_gate", "d_s_gate"), ("d_shared_up", "d_s_up"), ("d_shared_down", "d_s_down")):
+        check(np64(g[gname]), ref[rname], gname)
     for k_, v in g.items():
         assert torch.isfinite(v.float()).all(), k_

@@ -2,13 +2,14 @@
 units, combine of minibatch b on the mover compute units of a second stream)
 gives the same bits as the single-pass forward, for ragged minibatches,
 minibatches past the batch (T below max_tokens), no shared expert, many
-experts, MXFP8 mode, and with a context kept for the backward. The
-single-pass forward is itself checked against the oracle in
-test_gpu_forward.py / test_gpu_forward_mxfp8.py; here the property is that
-the pipeline's minibatch split never changes a result bit."""
+experts, MXFP8 mode, and with a context kept for the backward; at 8192
+tokens the pipelined output is also compared with the oracle on every
+token."""
+import numpy as np
 import pytest
 
-from mokutil import to_dev
+from mokutil import TOL_BF16, assert_close_inf, f64, to_dev
+from oracle import moe as omoe
 from workloads import CONFIGS, MoEShape, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -64,12 +65,19 @@ def test_minibatch_pipeline_matches_single_pass(case):
 
 
 def test_minibatch_pipeline_8192_tokens():
+    # bit-identical to the single pass, and every token against the oracle
     c = CONFIGS["t8192_bf16_fwd"]
-    d = to_dev(make_inputs(c))
+    inp = make_inputs(c)
+    d = to_dev(inp)
     ref, _, _ = run_forward(c, d, c.T, mok.MOK_MODE_BF16, 0, 0, False)
     got, got2, _ = run_forward(c, d, c.T, mok.MOK_MODE_BF16, 2048, 16, False)
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
     assert torch.equal(got2.view(torch.int16), ref.view(torch.int16))
+    want = omoe.forward(f64(inp["x"]), inp["top_experts"], inp["router_weights"], f64(inp["w_gate"]),
+                        f64(inp["w_up"]), f64(inp["w_down"]), f64(inp["s_gate"]), f64(inp["s_up"]),
+                        f64(inp["s_down"]), capacity_multiplier=c.capacity_multiplier)
+    err, scale = assert_close_inf(got.float().cpu().numpy().astype(np.float64), want, TOL_BF16, "pipeline out")
+    print(f"pipeline at 8192 tokens: max err {err:.3g} of max {scale:.3g}", flush=True)
 
 
 def test_minibatch_pipeline_graph_replay():

@@ -53,13 +53,14 @@ def check(f, ref, T, k, E):
         np.testing.assert_array_equal(tl[: E + 1], want)
 
 
-@pytest.mark.parametrize("name", ["tiny_bf16_fwd", "t8192_bf16_fwd", "skew_bf16_fwd", "t8192_mxfp8_fwd",
-                                  "t32768_bf16_fwdbwd"])
-@pytest.mark.parametrize("mult", [1.0, 0.5])
+# every workload at its capacity 1.0; the skewed and tiny ones also at 0.5
+WORKLOAD_CASES = [(n, 1.0) for n in ("tiny_bf16_fwd", "t8192_bf16_fwd", "skew_bf16_fwd", "t8192_mxfp8_fwd",
+                                     "t32768_bf16_fwdbwd")] + [("skew_bf16_fwd", 0.5), ("tiny_bf16_fwd", 0.5)]
+
+
+@pytest.mark.parametrize("name,mult", WORKLOAD_CASES, ids=[f"{n}-{m}" for n, m in WORKLOAD_CASES])
 def test_build_schedule_workloads(name, mult):
     c = CONFIGS[name]
-    if mult != 1.0 and name not in ("skew_bf16_fwd", "tiny_bf16_fwd"):
-        pytest.skip("capacity 0.5 is run on the skewed and tiny workloads")
     top = make_inputs(c.with_(H=32, I=32, I_s=0), with_grad=False)["top_experts"]  # routing only
     print(f"schedule {name} mult={mult} T={c.T} E={c.E} k={c.k}", flush=True)
     _, _, _, f, ref = run_case(top, c.E, mult)

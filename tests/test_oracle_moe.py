@@ -434,3 +434,55 @@ def test_mxfp8_backward_down_weight_gradient_rows_scale_with_grad_out_columns():
     np.testing.assert_array_equal(2.0 * a["d_w_down"][:, 17], b["d_w_down"][:, 17])
     np.testing.assert_array_equal(a["d_s_down"][rows], b["d_s_down"][rows])
     np.testing.assert_array_equal(2.0 * a["d_s_down"][17], b["d_s_down"][17])
+
+
+# ---------------------------------------------------------------------------
+# Restricted forms used by the full-size GPU checks
+# ---------------------------------------------------------------------------
+
+def test_token_and_expert_restrictions_equal_the_whole_computation():
+    x, top, w, Wg, Wu, Wd, (Sg, Su, Sd) = rand_case(41, T=40, H=6, I=5, E=4, k=2, I_s=3, id_lo=-1, id_hi=5)
+    dO = np.random.default_rng(42).standard_normal(x.shape)
+    s = build_schedule(top, 4, 0.4, 2)
+    toks = [0, 3, 17, 39]
+    full = moe.forward(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+    part = moe.forward(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, tokens=toks)
+    np.testing.assert_allclose(part[toks], full[toks], rtol=1e-12, atol=1e-12)
+    assert not np.any(np.delete(part, toks, axis=0))
+    fb = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+    pb = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, tokens=toks, dw_experts=[1, "shared"])
+    for n in ("dx", "d_router_weights"):
+        np.testing.assert_allclose(pb[n][toks], fb[n][toks], rtol=1e-12, atol=1e-12)
+    for n in ("d_w_gate", "d_w_up", "d_w_down"):
+        np.testing.assert_allclose(pb[n][1], fb[n][1], rtol=1e-12, atol=1e-12)
+    for n in ("d_s_gate", "d_s_up", "d_s_down"):
+        np.testing.assert_allclose(pb[n], fb[n], rtol=1e-12, atol=1e-12)
+
+
+def test_mxfp8_restrictions_and_prequantized_weights_equal_the_whole_computation():
+    (T, H, I, E, k, Is), x, top, w, Wg, Wu, Wd, Sg, Su, Sd, dO = _axis_case(43)
+    s = build_schedule(top, E, 0.5, 32)
+    toks = [1, 2, 30, 44]
+    full = moe.forward_mxfp8(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+    qf = moe.quantize_weights_mxfp8(Wg, Wu, Wd, Sg, Su, Sd)
+    part = moe.forward_mxfp8(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, qweights=qf, tokens=toks)
+    np.testing.assert_array_equal(part[toks], full[toks])
+    np.testing.assert_array_equal(moe.forward_mxfp8(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, qweights=qf), full)
+    fb = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+    qb = moe.quantize_weights_mxfp8(Wg, Wu, Wd, Sg, Su, Sd, for_backward=True)
+    pb = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, qweights=qb, tokens=toks,
+                            dw_experts=[2, "shared"])
+    for n in ("dx", "d_router_weights"):
+        np.testing.assert_array_equal(pb[n][toks], fb[n][toks])
+    for n in ("d_w_gate", "d_w_up", "d_w_down"):
+        np.testing.assert_array_equal(pb[n][2], fb[n][2])
+    for n in ("d_s_gate", "d_s_up", "d_s_down"):
+        np.testing.assert_array_equal(pb[n], fb[n])
+
+
+def test_parallel_quantizer_equals_one_call():
+    from mokutil import par_qdq
+    rng = np.random.default_rng(44)
+    for shape, axis in (((3, 64, 1 << 15), 2), ((3, 1 << 15, 64), 1), ((1 << 17, 64), 0), ((64, 1 << 17), 1)):
+        v = rng.standard_normal(shape) * 10.0 ** rng.integers(-3, 3, size=shape[-1])
+        np.testing.assert_array_equal(par_qdq(v, axis), mxfp8.qdq(v, axis))
