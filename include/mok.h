@@ -87,6 +87,10 @@ typedef struct mok_config {
                                    the combine of minibatch b-1 runs on these, on a stream the workspace owns
                                    ([R] "Tuning...": fwd_num_comm_sms, minibatch_size). The result bits do not
                                    depend on either value. */
+  float swiglu_limit;           /* SwiGLU input limit L ([A] _MoKRuntime(mok_config, swiglu_limit); the pages give
+                                   no formula): L > 0 computes h = silu(min(g, L)) * clamp(u, -L, L), and the
+                                   backward passes no gradient where a clamp is active (g > L, |u| > L);
+                                   0 or +inf = no limit. Negative or NaN: MOK_ERR_INVALID_ARGUMENT. */
 } mok_config;
 
 /* Routed and shared expert weights, layouts of [A] _MoKRuntime.forward:

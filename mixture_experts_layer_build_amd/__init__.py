@@ -45,12 +45,13 @@ class MoKConfig:
     expert_pad: int = 32
     minibatch_size: int = 0
     num_mover_wgs: int = 0
+    swiglu_limit: float = 0.0     # 0 = no limit (see include/mok.h)
 
     def c(self) -> _lib.MokConfig:
         return _lib.MokConfig(C.sizeof(_lib.MokConfig), self.hidden, self.intermediate, self.num_experts,
                               self.topk, self.shared_intermediate, self.max_tokens,
                               float(self.capacity_multiplier), self.expert_pad, self.minibatch_size,
-                              self.num_mover_wgs)
+                              self.num_mover_wgs, float(self.swiglu_limit))
 
 
 def schedule_bytes(cfg: MoKConfig) -> int:

@@ -46,6 +46,7 @@ class MokConfig(C.Structure):
         ("expert_pad", C.c_int32),
         ("minibatch_size", C.c_int32),
         ("num_mover_wgs", C.c_int32),
+        ("swiglu_limit", C.c_float),
     ]
 
 

@@ -30,6 +30,7 @@ CPU are rejected.
 """
 from __future__ import annotations
 
+import dataclasses
 import weakref
 
 import torch
@@ -43,12 +44,16 @@ _WEIGHT_NAMES = ("shared_gate", "shared_up", "shared_down", "routed_gate", "rout
 
 
 class MoKRuntime:
-    """One layer's configuration and precision mode. The workspace comes
-    from the per-(device, config) cache, so layers of one shape share it."""
+    """One layer's configuration, precision mode and SwiGLU input limit
+    ([A] ``_MoKRuntime(mok_config, swiglu_limit)``; None keeps the config's
+    own ``swiglu_limit``). The workspace comes from the per-(device, config)
+    cache, so layers of one shape and limit share it."""
 
-    def __init__(self, cfg: MoKConfig, mode: int = MOK_MODE_BF16):
+    def __init__(self, cfg: MoKConfig, mode: int = MOK_MODE_BF16, swiglu_limit: float | None = None):
         if mode not in (MOK_MODE_BF16, MOK_MODE_MXFP8):
             raise ValueError("mode must be MOK_MODE_BF16 or MOK_MODE_MXFP8")
+        if swiglu_limit is not None:
+            cfg = dataclasses.replace(cfg, swiglu_limit=float(swiglu_limit))
         self.cfg = cfg
         self.mode = mode
         # name -> (weak reference to the weight, its version, its address, codes, scales)

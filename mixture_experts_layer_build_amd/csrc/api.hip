@@ -254,6 +254,7 @@ extern "C" mok_status mok_validate_config(const mok_config* c) {
       c->shared_intermediate < 0 || c->expert_pad <= 0 || c->minibatch_size < 0 || c->num_mover_wgs < 0)
     return MOK_ERR_INVALID_ARGUMENT;
   if (!(c->capacity_multiplier > 0.0f) || !std::isfinite(c->capacity_multiplier)) return MOK_ERR_INVALID_ARGUMENT;
+  if (!(c->swiglu_limit >= 0.0f)) return MOK_ERR_INVALID_ARGUMENT;  // negative or NaN
   if (c->hidden % 128 != 0 || c->intermediate % 64 != 0 || c->shared_intermediate % 64 != 0)
     return MOK_ERR_UNSUPPORTED;
   if (c->num_experts > 1024 || c->topk > 64 || c->expert_pad % 32 != 0) return MOK_ERR_UNSUPPORTED;

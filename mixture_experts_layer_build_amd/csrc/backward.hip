@@ -146,6 +146,7 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
     p.I = I;
     p.Is = Is;
     p.rows_cap_max = rcm;
+    p.swiglu_lim = swiglu_lim(c);
   };
   {
     nt::Params p{};
@@ -275,6 +276,7 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
     p.I = I;
     p.Is = Is;
     p.rows_cap_max = rcm;
+    p.swiglu_lim = swiglu_lim(c);
   };
   {
     nt::Params p{};

@@ -40,6 +40,7 @@ static void fill_schedule(nt::Params& p, const mok_workspace* ws, const SchedVie
   p.I = c.intermediate;
   p.Is = c.shared_intermediate;
   p.rows_cap_max = ws->layout.rows_cap_max;
+  p.swiglu_lim = swiglu_lim(c);
 }
 
 // Compute units given to the combine in the minibatch pipeline (0 = no

@@ -77,6 +77,8 @@ struct Params {
   int mb;                       // tokens per minibatch; 0 = every row
   int E, k, H, I, Is;
   int64_t rows_cap_max;
+  // SwiGLU input limit L: h = silu(min(g, L)) * clamp(u, -L, L); +inf = none
+  float swiglu_lim;
   // A operand
   const void* a_tok;            // token-indexed rows [T, K] (x, x codes, grad_out)
   const uint8_t* a_tok_scale;   // their E8M0 scales [T, K/32]
@@ -143,6 +145,11 @@ struct alignas(16) Lds {
 // results are rounded to bf16 or E4M3 right after.
 __device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 __device__ __forceinline__ float silu_f(float g) { return g * sigmoid_f(g); }
+// SwiGLU with its inputs limited: the gate from above at L, the up
+// projection to [-L, L] (L = +inf leaves both unchanged).
+__device__ __forceinline__ float swiglu_f(float g, float u, float L) {
+  return silu_f(__builtin_fminf(g, L)) * __builtin_fminf(__builtin_fmaxf(u, -L), L);
+}
 
 template <int MODE>
 __device__ __forceinline__ int n_tile_width() {
@@ -862,7 +869,7 @@ grouped_gemm_nt(Params p) {
 #pragma unroll
               for (int c = 0; c < 4; ++c) {
                 const float g = acc[i][0][4 * q + c], u = acc[i][1][4 * q + c];
-                v[c] = SEL == 0 ? silu_f(g) * u : (SEL == 1 ? g : u);
+                v[c] = SEL == 0 ? swiglu_f(g, u, p.swiglu_lim) : (SEL == 1 ? g : u);
               }
               *reinterpret_cast<uint2*>(reg + (i * 32 + lr) * SW + 8 * q + 4 * lh) =
                   make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -899,7 +906,7 @@ grouped_gemm_nt(Params p) {
           uint32_t amax = 0;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            hv[r] = silu_f(acc[i][0][r]) * acc[i][1][r];
+            hv[r] = swiglu_f(acc[i][0][r], acc[i][1][r], p.swiglu_lim);
             amax = max(amax, f2u(hv[r]) & 0x7FFFFFFFu);
           }
           amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
@@ -1062,9 +1069,13 @@ grouped_gemm_nt(Params p) {
                 }
                 part += d[c] * h[c];
                 const float dh = w * d[c];
-                const float sg = sigmoid_f(g);
-                dg[c4] = dh * u * sg * (1.0f + g * (1.0f - sg));
-                du[c4] = dh * g * sg;
+                // through the limit: the clamped inputs, and no gradient where a
+                // clamp is active (g > L, |u| > L)
+                const float L = p.swiglu_lim;
+                const float gc = __builtin_fminf(g, L), uc = __builtin_fminf(__builtin_fmaxf(u, -L), L);
+                const float sg = sigmoid_f(gc);
+                dg[c4] = g <= L ? dh * uc * sg * (1.0f + gc * (1.0f - sg)) : 0.0f;
+                du[c4] = uc == u ? dh * gc * sg : 0.0f;
                 hwv[c4] = w * h[c];
               }
               if constexpr (FP8) {

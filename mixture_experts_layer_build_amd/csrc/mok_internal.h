@@ -218,6 +218,12 @@ struct BwdArgs {
 };
 hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& a, hipStream_t s);
 
+// The SwiGLU input limit the kernels apply: +inf (no clamp) unless the
+// configuration sets a positive finite limit.
+inline float swiglu_lim(const mok_config& c) {
+  return (c.swiglu_limit > 0.0f && c.swiglu_limit < __builtin_inff()) ? c.swiglu_limit : __builtin_inff();
+}
+
 // Columns of the per-row partial router-weight gradients.
 int dw_parts(const mok_config& c);
 

@@ -34,7 +34,7 @@ from . import mxfp8
 from .schedule import build_schedule
 
 
-__all__ = ["sigmoid", "silu", "forward", "forward_per_token", "forward_tokens",
+__all__ = ["sigmoid", "silu", "swiglu", "swiglu_backward", "forward", "forward_per_token", "forward_tokens",
            "backward", "backward_slices", "quantize_weights_mxfp8", "forward_mxfp8", "forward_tokens_mxfp8",
            "backward_mxfp8", "backward_slices_mxfp8", "segment_rows"]
 
@@ -55,6 +55,38 @@ def segment_rows(sched: dict, e: int):
     return rows, a, a // sched["k"]
 
 
+def swiglu(g, u, limit=None):
+    """h = silu(g) * u. With a limit L > 0 (the ``swiglu_limit`` of [A]
+    ``_MoKRuntime``, which the pages name without a formula; the reading
+    taken: a limit on SwiGLU's two inputs) h = silu(min(g, L)) *
+    clamp(u, -L, L). None, 0 or inf: no limit.
+
+    Pins (tests/test_oracle_moe.py): a dense torch MLP with torch.clamp, and
+    a limit above every input equal to no limit."""
+    if limit is None or not (0 < limit < np.inf):
+        return silu(g) * u
+    return silu(np.minimum(g, limit)) * np.clip(u, -limit, limit)
+
+
+def swiglu_backward(g, u, dh, limit=None):
+    """(dg, du) for h = swiglu(g, u, limit) and the gradient dh of h:
+    dg = dh * u_c * s (1 + g_c (1 - s)) with s = sigmoid(g_c), du = dh *
+    silu(g_c), where g_c, u_c are the limited inputs, and no gradient
+    through an active limit (g > L; |u| > L), as a clamp's derivative.
+
+    Pins (tests/test_oracle_moe.py): torch.autograd through torch.clamp, and
+    central finite differences away from the limit."""
+    if limit is None or not (0 < limit < np.inf):
+        s = sigmoid(g)
+        return dh * u * s * (1.0 + g * (1.0 - s)), dh * g * s
+    gc = np.minimum(g, limit)
+    uc = np.clip(u, -limit, limit)
+    s = sigmoid(gc)
+    dg = np.where(g <= limit, dh * uc * s * (1.0 + gc * (1.0 - s)), 0.0)
+    du = np.where(np.abs(u) <= limit, dh * gc * s, 0.0)
+    return dg, du
+
+
 def _token_set(T, tokens):
     """Boolean mask over the T tokens (all True for tokens=None)."""
     if tokens is None:
@@ -64,19 +96,19 @@ def _token_set(T, tokens):
     return m
 
 
-def _expert_mlp(A, Wg, Wu, Wd):
+def _expert_mlp(A, Wg, Wu, Wd, limit=None):
     g = A @ Wg.T
     u = A @ Wu.T
-    h = silu(g) * u
+    h = swiglu(g, u, limit)
     return g, u, h, h @ Wd.T
 
 
 def forward(x, top_experts, router_weights, w_gate, w_up, w_down,
             s_gate=None, s_up=None, s_down=None, sched=None,
-            capacity_multiplier=1.0, expert_pad=32, return_parts=False, tokens=None):
+            capacity_multiplier=1.0, expert_pad=32, return_parts=False, tokens=None, swiglu_limit=None):
     """Layer output [T,H] in float64, expert-grouped formulation: each
     expert's kept rows are gathered, run through its SwiGLU MLP, weighted and
-    added back at their tokens.
+    added back at their tokens. ``swiglu_limit``: see ``swiglu``.
 
     ``tokens`` (optional) restricts the work to the rows of those tokens (for
     checks at full size; the schedule is still the whole batch's): their
@@ -104,14 +136,14 @@ def forward(x, top_experts, router_weights, w_gate, w_up, w_down,
         if rows.size == 0:
             continue
         g, u, h, y = _expert_mlp(x[t], np.asarray(w_gate[e], np.float64), np.asarray(w_up[e], np.float64),
-                                 np.asarray(w_down[e], np.float64))
+                                 np.asarray(w_down[e], np.float64), swiglu_limit)
         np.add.at(out, t, wflat[a][:, None] * y)
         if return_parts:
             parts[e] = dict(rows=rows, a=a, t=t, g=g, u=u, h=h, y=y)
     if s_gate is not None:
         ts = np.flatnonzero(sel)
         g, u, h, y = _expert_mlp(x[ts], np.asarray(s_gate, np.float64), np.asarray(s_up, np.float64),
-                                 np.asarray(s_down, np.float64))
+                                 np.asarray(s_down, np.float64), swiglu_limit)
         out[ts] += y
         if return_parts:
             parts["shared"] = dict(g=g, u=u, h=h, y=y)
@@ -176,8 +208,9 @@ def forward_tokens(tokens, x, top_experts, router_weights, w_gate, w_up, w_down,
 
 def backward(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
              s_gate=None, s_up=None, s_down=None, sched=None,
-             capacity_multiplier=1.0, expert_pad=32, tokens=None, dw_experts=None):
-    """Gradients of sum(grad_out * out) with respect to every float input.
+             capacity_multiplier=1.0, expert_pad=32, tokens=None, dw_experts=None, swiglu_limit=None):
+    """Gradients of sum(grad_out * out) with respect to every float input
+    (``swiglu_limit``: see ``swiglu`` and ``swiglu_backward``).
 
     ``tokens`` and ``dw_experts`` (optional) restrict the work for checks at
     full size: dx and d_router_weights are exact for the listed tokens, the
@@ -226,14 +259,12 @@ def backward(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
             continue
         Wg_e, Wu_e, Wd_e = (np.asarray(w[e], np.float64) for w in (w_gate, w_up, w_down))
         A = x[t]
-        g, u, h, y = _expert_mlp(A, Wg_e, Wu_e, Wd_e)
+        g, u, h, y = _expert_mlp(A, Wg_e, Wu_e, Wd_e, swiglu_limit)
         dOt = dO[t]
         dwr[a] = np.sum(dOt * y, axis=1)
         dy = wflat[a][:, None] * dOt
         dh = dy @ Wd_e
-        s = sigmoid(g)
-        dg = dh * u * s * (1.0 + g * (1.0 - s))
-        du = dh * g * s
+        dg, du = swiglu_backward(g, u, dh, swiglu_limit)
         if want_dw(e):
             dWd[e] = dy.T @ h
             dWg[e] = dg.T @ A
@@ -245,11 +276,9 @@ def backward(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
         Sg, Su, Sd = (np.asarray(w, np.float64) for w in (s_gate, s_up, s_down))
         ts = np.arange(T) if want_dw("shared") else np.flatnonzero(sel)
         xs, dOs = x[ts], dO[ts]
-        g, u, h, y = _expert_mlp(xs, Sg, Su, Sd)
+        g, u, h, y = _expert_mlp(xs, Sg, Su, Sd, swiglu_limit)
         dh = dOs @ Sd
-        s = sigmoid(g)
-        dg = dh * u * s * (1.0 + g * (1.0 - s))
-        du = dh * g * s
+        dg, du = swiglu_backward(g, u, dh, swiglu_limit)
         if want_dw("shared"):
             res["d_s_down"] = dOs.T @ h
             res["d_s_gate"] = dg.T @ xs
@@ -393,7 +422,7 @@ def quantize_weights_mxfp8(w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=
 def forward_mxfp8(x, top_experts, router_weights, w_gate, w_up, w_down,
                   s_gate=None, s_up=None, s_down=None, sched=None,
                   capacity_multiplier=1.0, expert_pad=32, return_parts=False,
-                  quantize_h=True, qweights=None, tokens=None):
+                  quantize_h=True, qweights=None, tokens=None, swiglu_limit=None):
     """MXFP8 forward: x, W_g, W_u (blocks along H) and W_d (blocks along I),
     shared weights included, are replaced by dequantize(quantize(.)); h is
     computed in float64 from those and itself quantized along I before the
@@ -407,6 +436,7 @@ def forward_mxfp8(x, top_experts, router_weights, w_gate, w_up, w_down,
     ``qweights`` (optional): the result of ``quantize_weights_mxfp8`` for
     these weights, computed beforehand. ``tokens`` (optional) restricts the
     work to those tokens' rows as in ``forward`` (other rows are left 0).
+    ``swiglu_limit``: see ``swiglu``.
 
     Pin (tests/test_oracle_moe.py): when x and every weight already sit on
     the MX grid, the only difference to ``forward`` is h's quantization, so
@@ -436,7 +466,7 @@ def forward_mxfp8(x, top_experts, router_weights, w_gate, w_up, w_down,
         A = xq[t]
         g = A @ Wg[e].T
         u = A @ Wu[e].T
-        h = qh(silu(g) * u, axis=1)
+        h = qh(swiglu(g, u, swiglu_limit), axis=1)
         y = h @ Wd[e].T
         np.add.at(out, t, wflat[a][:, None] * y)
         if return_parts:
@@ -445,7 +475,7 @@ def forward_mxfp8(x, top_experts, router_weights, w_gate, w_up, w_down,
         ts = np.flatnonzero(sel)
         g = xq[ts] @ qweights["Sg_f"].T
         u = xq[ts] @ qweights["Su_f"].T
-        h = qh(silu(g) * u, axis=1)
+        h = qh(swiglu(g, u, swiglu_limit), axis=1)
         out[ts] += h @ qweights["Sd_f"].T
         if return_parts:
             parts["shared"] = dict(g=g, u=u, hq=h)
@@ -512,7 +542,7 @@ def _qdq_rows_in_segment(v, q, block=32):
 def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_down,
                    s_gate=None, s_up=None, s_down=None, sched=None,
                    capacity_multiplier=1.0, expert_pad=32, qfun=None, qweights=None,
-                   tokens=None, dw_experts=None):
+                   tokens=None, dw_experts=None, swiglu_limit=None):
     """MXFP8 backward: every backward GEMM operand is quantized along that
     GEMM's contraction dimension, the forward activations being the MXFP8
     forward's (g, u from quantized x and weights; h quantized along I).
@@ -533,7 +563,8 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
     ``qweights`` (optional): ``quantize_weights_mxfp8(..., for_backward=True)``
     of these weights, computed beforehand. ``tokens`` and ``dw_experts``
     restrict the work as in ``backward`` (a listed expert's weight gradients
-    use all of its rows, as its 32-row blocks need).
+    use all of its rows, as its 32-row blocks need). ``swiglu_limit``: see
+    ``swiglu`` and ``swiglu_backward``.
 
     Pins (tests/test_oracle_moe.py): with ``qfun`` the identity this must equal
     ``backward`` (checks which operand goes where); a recording ``qfun`` checks
@@ -573,15 +604,13 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
         A = xq[t]
         g = A @ Wg_f[e].T
         u = A @ Wu_f[e].T
-        hq = q(silu(g) * u, axis=1)
+        hq = q(swiglu(g, u, swiglu_limit), axis=1)
         dOq = q(dO[t], axis=1)
         dh_un = dOq @ Wd_b[e]
         dwr[a] = np.sum(dh_un * hq, axis=1)
         w = wflat[a][:, None]
         dh = w * dh_un
-        s = sigmoid(g)
-        dg = dh * u * s * (1.0 + g * (1.0 - s))
-        du = dh * g * s
+        dg, du = swiglu_backward(g, u, dh, swiglu_limit)
         dx_rows = q(dg, axis=1) @ Wg_b[e] + q(du, axis=1) @ Wu_b[e]
         np.add.at(dx, t, dx_rows)
         if want_dw(e):
@@ -596,11 +625,9 @@ def backward_mxfp8(grad_out, x, top_experts, router_weights, w_gate, w_up, w_dow
         ts = np.arange(T) if want_dw("shared") else np.flatnonzero(sel)
         g = xq[ts] @ qweights["Sg_f"].T
         u = xq[ts] @ qweights["Su_f"].T
-        hq = q(silu(g) * u, axis=1)
+        hq = q(swiglu(g, u, swiglu_limit), axis=1)
         dh = q(dO[ts], axis=1) @ qweights["Sd_b"]
-        s = sigmoid(g)
-        dg = dh * u * s * (1.0 + g * (1.0 - s))
-        du = dh * g * s
+        dg, du = swiglu_backward(g, u, dh, swiglu_limit)
         dx[ts] += q(dg, axis=1) @ qweights["Sg_b"] + q(du, axis=1) @ qweights["Su_b"]
         if want_dw("shared"):
             res["d_s_down"] = _qdq_rows_in_segment(dO, q).T @ _qdq_rows_in_segment(hq, q)

@@ -190,3 +190,41 @@ def test_expert_pad_not_dividing_the_tile(mxfp8, pad):
                          ("d_routed_up", "d_w_up"), ("d_routed_down", "d_w_down"), ("d_shared_gate", "d_s_gate"),
                          ("d_shared_up", "d_s_up"), ("d_shared_down", "d_s_down")]:
         assert_close_inf(np64(g[gname]), ref[rname], tol, f"pad {pad} {gname}")
+
+
+@pytest.mark.parametrize("limit", [0.35, 1.0])
+@pytest.mark.parametrize("mxfp8", [False, True], ids=["bf16", "mxfp8"])
+def test_swiglu_limit(mxfp8, limit):
+    # h = silu(min(g, L)) * clamp(u, -L, L); gradients blocked where a clamp
+    # is active. With L = 0.35 about a quarter of the gate values and half of
+    # the up values are clamped (both have a spread of ~0.56 here), with
+    # L = 1.0 4 % and 7 %.
+    c = MoEShape("limit", T=300, H=256, I=256, E=5, k=3, I_s=128, seed=99, w_std=0.035,
+                 mode="mxfp8" if mxfp8 else "bf16", passes="fwd+bwd")
+    inp = make_inputs(c)
+    d = to_dev(inp)
+    cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=c.T,
+                        shared_intermediate=c.I_s, swiglu_limit=limit)
+    ws = mok.Workspace(cfg)
+    mode = mok.MOK_MODE_MXFP8 if mxfp8 else mok.MOK_MODE_BF16
+    sched = mok.build_schedule(ws, d["top_experts"])
+    ctx = torch.empty(mok.context_bytes(cfg, mode), dtype=torch.uint8, device="cuda")
+    w_fwd = quantize_weights(d["weights"]) if mxfp8 else d["weights"]
+    print(f"swiglu limit {limit} {'mxfp8' if mxfp8 else 'bf16'}", flush=True)
+    out = mok.forward(ws, sched, d["x"], d["router_weights"], w_fwd, mode=mode, context=ctx)
+    g = mok.backward(ws, sched, ctx, d["grad_out"], d["x"], d["router_weights"], d["weights"], mode=mode)
+    torch.cuda.synchronize()
+    args = (f64(inp["x"]), inp["top_experts"], inp["router_weights"], f64(inp["w_gate"]), f64(inp["w_up"]),
+            f64(inp["w_down"]), f64(inp["s_gate"]), f64(inp["s_up"]), f64(inp["s_down"]))
+    tol = TOL_MXFP8 if mxfp8 else TOL_BF16
+    ref_out = (omoe.forward_mxfp8 if mxfp8 else omoe.forward)(*args, swiglu_limit=limit)
+    assert_close_inf(np64(out), ref_out, tol, "out")
+    # the limit changes the result well beyond the tolerance
+    free = (omoe.forward_mxfp8 if mxfp8 else omoe.forward)(*args)
+    assert np.max(np.abs(free - ref_out)) > 4 * tol * np.max(np.abs(ref_out))
+    ref = (omoe.backward_mxfp8 if mxfp8 else omoe.backward)(f64(inp["grad_out"]), *args, swiglu_limit=limit)
+    for gname, rname in [("dx", "dx"), ("d_router_weights", "d_router_weights"), ("d_routed_gate", "d_w_gate"),
+                         ("d_routed_up", "d_w_up"), ("d_routed_down", "d_w_down"), ("d_shared_gate", "d_s_gate"),
+                         ("d_shared_up", "d_s_up"), ("d_shared_down", "d_s_down")]:
+        err, scale = assert_close_inf(np64(g[gname]), ref[rname], tol, f"limit {limit} {gname}")
+        print(f"  {gname}: max err {err:.3g} of max {scale:.3g}", flush=True)

@@ -89,8 +89,13 @@ def test_dropped_assignments_contribute_nothing():
     np.testing.assert_array_equal(a, b)
 
 
-def torch_forward(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, keep):
-    """The layer written directly in torch ops (float64) for autograd."""
+def torch_forward(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, keep, limit=None):
+    """The layer written directly in torch ops (float64) for autograd; with
+    a limit, SwiGLU's inputs go through torch.clamp."""
+    def act(g, u):
+        if limit is None:
+            return F.silu(g) * u
+        return F.silu(torch.clamp(g, max=limit)) * torch.clamp(u, -limit, limit)
     T, k = top.shape
     out = torch.zeros_like(x)
     for j in range(k):
@@ -99,26 +104,31 @@ def torch_forward(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, keep):
             if not m.any():
                 continue
             xs = x[m]
-            h = F.silu(xs @ Wg[e].T) * (xs @ Wu[e].T)
+            h = act(xs @ Wg[e].T, xs @ Wu[e].T)
             out = out.index_add(0, torch.nonzero(m)[:, 0], w[m, j:j + 1] * (h @ Wd[e].T))
     if Sg is not None:
-        out = out + (F.silu(x @ Sg.T) * (x @ Su.T)) @ Sd.T
+        out = out + act(x @ Sg.T, x @ Su.T) @ Sd.T
     return out
 
 
-@pytest.mark.parametrize("mult", [1.0, 0.4])
-def test_backward_matches_torch_autograd(mult):
+@pytest.mark.parametrize("mult,limit", [(1.0, None), (0.4, None), (1.0, 0.8), (0.4, 1.5)])
+def test_backward_matches_torch_autograd(mult, limit):
     x, top, w, Wg, Wu, Wd, (Sg, Su, Sd) = rand_case(6, T=16, id_lo=-1, id_hi=5)
     s = build_schedule(top, 4, mult, 4)
     keep = (s["slot_row"] >= 0).reshape(top.shape)
     rng = np.random.default_rng(11)
     dO = rng.standard_normal(x.shape)
     tens = [torch.tensor(a, requires_grad=True) for a in (x, w, Wg, Wu, Wd, Sg, Su, Sd)]
-    out = torch_forward(tens[0], top, *tens[1:], keep)
-    np.testing.assert_allclose(out.detach().numpy(), moe.forward(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s),
+    out = torch_forward(tens[0], top, *tens[1:], keep, limit=limit)
+    np.testing.assert_allclose(out.detach().numpy(),
+                               moe.forward(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, swiglu_limit=limit),
                                rtol=1e-12, atol=1e-12)
+    if limit is not None:  # the limit is active on a good share of the inputs
+        g_all = np.concatenate([(x @ Wg[e].T).ravel() for e in range(4)])
+        u_all = np.concatenate([(x @ Wu[e].T).ravel() for e in range(4)])
+        assert np.mean(g_all > limit) > 0.1 and np.mean(np.abs(u_all) > limit) > 0.1
     (out * torch.from_numpy(dO)).sum().backward()
-    g = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s)
+    g = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, swiglu_limit=limit)
     names = ["dx", "d_router_weights", "d_w_gate", "d_w_up", "d_w_down", "d_s_gate", "d_s_up", "d_s_down"]
     for n, t in zip(names, tens):
         np.testing.assert_allclose(g[n], t.grad.numpy(), rtol=1e-10, atol=1e-10, err_msg=n)
@@ -486,3 +496,76 @@ def test_parallel_quantizer_equals_one_call():
     for shape, axis in (((3, 64, 1 << 15), 2), ((3, 1 << 15, 64), 1), ((1 << 17, 64), 0), ((64, 1 << 17), 1)):
         v = rng.standard_normal(shape) * 10.0 ** rng.integers(-3, 3, size=shape[-1])
         np.testing.assert_array_equal(par_qdq(v, axis), mxfp8.qdq(v, axis))
+
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU input limit
+# ---------------------------------------------------------------------------
+
+def test_swiglu_limit_dense_mlp_matches_torch_clamp():
+    rng = np.random.default_rng(50)
+    T, H, I, L = 9, 16, 12, 0.7
+    x = rng.standard_normal((T, H))
+    Wg, Wu, Wd = (rng.standard_normal(s) for s in ((1, I, H), (1, I, H), (1, H, I)))
+    out = moe.forward(x, np.zeros((T, 1), np.int64), np.ones((T, 1)), Wg, Wu, Wd, swiglu_limit=L)
+    xt = torch.from_numpy(x)
+    g = torch.clamp(F.linear(xt, torch.from_numpy(Wg[0])), max=L)
+    u = torch.clamp(F.linear(xt, torch.from_numpy(Wu[0])), -L, L)
+    ref = F.linear(F.silu(g) * u, torch.from_numpy(Wd[0])).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_swiglu_limit_above_every_input_changes_nothing():
+    x, top, w, Wg, Wu, Wd, (Sg, Su, Sd) = rand_case(51)
+    dO = np.random.default_rng(52).standard_normal(x.shape)
+    big = 1e6
+    np.testing.assert_array_equal(moe.forward(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, swiglu_limit=big),
+                                  moe.forward(x, top, w, Wg, Wu, Wd, Sg, Su, Sd))
+    a = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, swiglu_limit=big)
+    b = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd)
+    for n in b:
+        np.testing.assert_array_equal(a[n], b[n], err_msg=n)
+    for off in (None, 0.0, np.inf):
+        np.testing.assert_array_equal(moe.forward(x, top, w, Wg, Wu, Wd, Sg, Su, Sd, swiglu_limit=off),
+                                      moe.forward(x, top, w, Wg, Wu, Wd, Sg, Su, Sd))
+
+
+def test_swiglu_limit_backward_finite_differences():
+    # central differences at points where no input sits within 1e-3 of a limit
+    x, top, w, Wg, Wu, Wd, (Sg, Su, Sd) = rand_case(53, T=6, H=5, I=4, E=3, k=2, I_s=3)
+    L = 0.6
+    s = build_schedule(top, 3, 1.0, 2)
+    dO = np.random.default_rng(54).standard_normal(x.shape)
+    g = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, swiglu_limit=L)
+    args = dict(x=x, w=w, Wg=Wg, Wu=Wu, Wd=Wd, Sg=Sg, Su=Su, Sd=Sd)
+    gname = dict(x="dx", w="d_router_weights", Wg="d_w_gate", Wu="d_w_up", Wd="d_w_down",
+                 Sg="d_s_gate", Su="d_s_up", Sd="d_s_down")
+
+    def loss(a):
+        return float(np.sum(dO * moe.forward(a["x"], top, a["w"], a["Wg"], a["Wu"], a["Wd"], a["Sg"], a["Su"],
+                                             a["Sd"], sched=s, swiglu_limit=L)))
+    pre = np.concatenate([(x @ W.T).ravel() for W in list(Wg) + list(Wu) + [Sg, Su]])
+    assert np.min(np.abs(np.abs(pre) - L)) > 1e-3 and np.mean(np.abs(pre) > L) > 0.1
+    rng = np.random.default_rng(55)
+    eps = 1e-7
+    for name, arr in args.items():
+        for _ in range(4):
+            idx = tuple(rng.integers(n) for n in arr.shape)
+            p = {kk: vv.copy() for kk, vv in args.items()}
+            m = {kk: vv.copy() for kk, vv in args.items()}
+            p[name][idx] += eps
+            m[name][idx] -= eps
+            fd = (loss(p) - loss(m)) / (2 * eps)
+            assert abs(fd - g[gname[name]][idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx)
+
+
+def test_swiglu_limit_mxfp8_structure_with_identity_quantizer():
+    x, top, w, Wg, Wu, Wd, (Sg, Su, Sd) = rand_case(56, T=10, H=64, I=32, E=3, k=2, I_s=32)
+    s = build_schedule(top, 3, 1.0, 32)
+    dO = np.random.default_rng(57).standard_normal(x.shape)
+    ident = lambda v, axis=-1: np.asarray(v, np.float64)  # noqa: E731
+    a = moe.backward_mxfp8(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, qfun=ident, swiglu_limit=0.9)
+    b = moe.backward(dO, x, top, w, Wg, Wu, Wd, Sg, Su, Sd, sched=s, swiglu_limit=0.9)
+    for n in b:
+        np.testing.assert_allclose(a[n], b[n], rtol=1e-11, atol=1e-11, err_msg=n)
