@@ -150,6 +150,14 @@ __device__ __forceinline__ float silu_f(float g) { return g * sigmoid_f(g); }
 __device__ __forceinline__ float swiglu_f(float g, float u, float L) {
   return silu_f(__builtin_fminf(g, L)) * __builtin_fminf(__builtin_fmaxf(u, -L), L);
 }
+// G and U as saved for the backward: an input that the limit clamped is
+// saved as +-inf, so the backward knows the forward's clamp decision exactly
+// (a bf16-rounded value near L would not tell), and reads the clamped value
+// back as min(g, L), clamp(u, -L, L).
+__device__ __forceinline__ float saved_gate(float g, float L) { return g > L ? __builtin_inff() : g; }
+__device__ __forceinline__ float saved_up(float u, float L) {
+  return u > L ? __builtin_inff() : (u < -L ? -__builtin_inff() : u);
+}
 
 template <int MODE>
 __device__ __forceinline__ int n_tile_width() {
@@ -869,7 +877,8 @@ grouped_gemm_nt(Params p) {
 #pragma unroll
               for (int c = 0; c < 4; ++c) {
                 const float g = acc[i][0][4 * q + c], u = acc[i][1][4 * q + c];
-                v[c] = SEL == 0 ? swiglu_f(g, u, p.swiglu_lim) : (SEL == 1 ? g : u);
+                v[c] = SEL == 0 ? swiglu_f(g, u, p.swiglu_lim)
+                                : (SEL == 1 ? saved_gate(g, p.swiglu_lim) : saved_up(u, p.swiglu_lim));
               }
               *reinterpret_cast<uint2*>(reg + (i * 32 + lr) * SW + 8 * q + 4 * lh) =
                   make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -940,10 +949,13 @@ grouped_gemm_nt(Params p) {
               const int n = col0 + 8 * q + 4 * lh;
               if (n >= Nd) continue;
               const int64_t o = sh + (int64_t)(t.m0 + ml) * Nd + n;
+              const float L = p.swiglu_lim;
               *reinterpret_cast<float4*>(cg + o) =
-                  make_float4(acc[i][0][4 * q], acc[i][0][4 * q + 1], acc[i][0][4 * q + 2], acc[i][0][4 * q + 3]);
+                  make_float4(saved_gate(acc[i][0][4 * q], L), saved_gate(acc[i][0][4 * q + 1], L),
+                              saved_gate(acc[i][0][4 * q + 2], L), saved_gate(acc[i][0][4 * q + 3], L));
               *reinterpret_cast<float4*>(cu + o) =
-                  make_float4(acc[i][1][4 * q], acc[i][1][4 * q + 1], acc[i][1][4 * q + 2], acc[i][1][4 * q + 3]);
+                  make_float4(saved_up(acc[i][1][4 * q], L), saved_up(acc[i][1][4 * q + 1], L),
+                              saved_up(acc[i][1][4 * q + 2], L), saved_up(acc[i][1][4 * q + 3], L));
             }
           }
         }
@@ -1069,13 +1081,13 @@ grouped_gemm_nt(Params p) {
                 }
                 part += d[c] * h[c];
                 const float dh = w * d[c];
-                // through the limit: the clamped inputs, and no gradient where a
-                // clamp is active (g > L, |u| > L)
+                // through the limit: the clamped inputs, and no gradient where the
+                // forward clamped (saved as +-inf)
                 const float L = p.swiglu_lim;
                 const float gc = __builtin_fminf(g, L), uc = __builtin_fminf(__builtin_fmaxf(u, -L), L);
                 const float sg = sigmoid_f(gc);
-                dg[c4] = g <= L ? dh * uc * sg * (1.0f + gc * (1.0f - sg)) : 0.0f;
-                du[c4] = uc == u ? dh * gc * sg : 0.0f;
+                dg[c4] = g < __builtin_inff() ? dh * uc * sg * (1.0f + gc * (1.0f - sg)) : 0.0f;
+                du[c4] = __builtin_fabsf(u) < __builtin_inff() ? dh * gc * sg : 0.0f;
                 hwv[c4] = w * h[c];
               }
               if constexpr (FP8) {

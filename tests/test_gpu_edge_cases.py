@@ -192,16 +192,44 @@ def test_expert_pad_not_dividing_the_tile(mxfp8, pad):
         assert_close_inf(np64(g[gname]), ref[rname], tol, f"pad {pad} {gname}")
 
 
+def _limit_in_a_gap(target: float, inp: dict, mult: float, mxfp8: bool) -> tuple[float, float]:
+    """A limit near ``target`` with no gate or up value of the batch within
+    the widest margin found: the clamp is a decision the kernel takes on fp32
+    accumulations and the oracle on float64, so a value within rounding of L
+    could be clamped on one side only. Returns (limit, margin)."""
+    from oracle import mxfp8 as omx
+    from oracle.schedule import build_schedule
+    q = (lambda v, a: omx.qdq(v, a)) if mxfp8 else (lambda v, a: v)  # noqa: E731
+    x = q(f64(inp["x"]), 1)
+    E = inp["w_gate"].shape[0]
+    s = build_schedule(inp["top_experts"], E, mult, 32)
+    vals = []
+    for e in range(E):
+        rows, _, t = omoe.segment_rows(s, e)
+        vals += [(x[t] @ q(f64(inp["w_gate"][e]), 1).T).ravel(), np.abs(x[t] @ q(f64(inp["w_up"][e]), 1).T).ravel()]
+    if inp.get("s_gate") is not None:
+        vals += [(x @ q(f64(inp["s_gate"]), 1).T).ravel(), np.abs(x @ q(f64(inp["s_up"]), 1).T).ravel()]
+    v = np.sort(np.concatenate(vals))
+    cand = np.linspace(0.9 * target, 1.1 * target, 4001)
+    idx = np.clip(np.searchsorted(v, cand), 1, v.size - 1)
+    margin = np.minimum(np.abs(v[idx] - cand), np.abs(v[idx - 1] - cand))
+    best = int(np.argmax(margin))
+    return float(np.float32(cand[best])), float(margin[best])
+
+
 @pytest.mark.parametrize("limit", [0.35, 1.0])
 @pytest.mark.parametrize("mxfp8", [False, True], ids=["bf16", "mxfp8"])
 def test_swiglu_limit(mxfp8, limit):
     # h = silu(min(g, L)) * clamp(u, -L, L); gradients blocked where a clamp
     # is active. With L = 0.35 about a quarter of the gate values and half of
     # the up values are clamped (both have a spread of ~0.56 here), with
-    # L = 1.0 4 % and 7 %.
-    c = MoEShape("limit", T=300, H=256, I=256, E=5, k=3, I_s=128, seed=99, w_std=0.035,
+    # L = 1.0 4 % and 7 %. Each limit is moved to a gap of the batch's gate
+    # and up values (within 10 %), so no clamp decision hangs on rounding.
+    c = MoEShape("limit", T=160, H=256, I=256, E=4, k=2, I_s=128, seed=99, w_std=0.035,
                  mode="mxfp8" if mxfp8 else "bf16", passes="fwd+bwd")
     inp = make_inputs(c)
+    limit, margin = _limit_in_a_gap(limit, inp, 1.0, mxfp8)
+    assert margin > 1e-5, margin  # far above fp32 accumulation error (~1e-6) at these sizes
     d = to_dev(inp)
     cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=c.T,
                         shared_intermediate=c.I_s, swiglu_limit=limit)
@@ -210,7 +238,7 @@ def test_swiglu_limit(mxfp8, limit):
     sched = mok.build_schedule(ws, d["top_experts"])
     ctx = torch.empty(mok.context_bytes(cfg, mode), dtype=torch.uint8, device="cuda")
     w_fwd = quantize_weights(d["weights"]) if mxfp8 else d["weights"]
-    print(f"swiglu limit {limit} {'mxfp8' if mxfp8 else 'bf16'}", flush=True)
+    print(f"swiglu limit {limit} (margin {margin:.2e}) {'mxfp8' if mxfp8 else 'bf16'}", flush=True)
     out = mok.forward(ws, sched, d["x"], d["router_weights"], w_fwd, mode=mode, context=ctx)
     g = mok.backward(ws, sched, ctx, d["grad_out"], d["x"], d["router_weights"], d["weights"], mode=mode)
     torch.cuda.synchronize()
