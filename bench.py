@@ -174,15 +174,19 @@ def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sampl
     sched = torch.empty(ws.layout.total_bytes, dtype=torch.uint8, device="cuda")
     out = torch.empty_like(d["x"])
     weights = d["weights"]
+    bwd_weights = weights
     if mode == mok.MOK_MODE_MXFP8:
-        # weights pre-quantized once, outside the step (the pages' MXFP8 workflow)
+        # weights pre-quantized once, outside the step (the pages' MXFP8
+        # workflow): along each forward GEMM's contraction for the forward,
+        # transposed along each backward GEMM's contraction for the backward
         q = {}
         for n, t in d["weights"].items():
             codes, sc = mok.mxfp8_quantize(t.reshape(-1, t.shape[-1]), axis=1)
             q[n] = codes.view(t.shape)
             q[n + "_scale"] = sc
         weights = q
-        bf16_weights = d["weights"]
+        if training:
+            bwd_weights = mok.mxfp8_backward_weights(d["weights"])
     grads = None
 
     def step():
@@ -190,8 +194,7 @@ def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sampl
         mok.build_schedule(ws, d["top"], sched)
         mok.forward(ws, sched, d["x"], d["w"], weights, mode=mode, out=out, context=ctx)
         if training:
-            grads = mok.backward(ws, sched, ctx, d["g"], d["x"], d["w"],
-                                 bf16_weights if mode == mok.MOK_MODE_MXFP8 else weights, mode=mode, grads=grads)
+            grads = mok.backward(ws, sched, ctx, d["g"], d["x"], d["w"], bwd_weights, mode=mode, grads=grads)
 
     if use_autograd:
         from mixture_experts_layer_build_amd.autograd import MoKRuntime, moe_layer

@@ -246,12 +246,23 @@ mok_status mok_forward(mok_workspace* ws, mok_mode mode, const void* schedule, s
 /*
  * Backward ([A] _MoKRuntime.backward): gradients of sum(grad_out * out) for
  * every float input, reusing the forward's schedule and context. grad_out,
- * x bf16 [T, H]; router_weights fp32 [T, k]; `weights` are the BF16 weights
- * in both modes (scale pointers ignored): in MXFP8 mode they are quantized on
- * the device along each backward GEMM's own contraction dimension, as are
- * the activation-side operands (grad_out rows along H; dG, dU along I; the
- * weight gradients' operands in 32-row blocks of each expert's rows), and
- * the context must come from an MXFP8 forward of the same schedule.
+ * x bf16 [T, H]; router_weights fp32 [T, k]. In BF16 mode `weights` are the
+ * BF16 weights (scale pointers ignored). In MXFP8 mode every backward GEMM
+ * operand is quantized along that GEMM's own contraction dimension (grad_out
+ * rows along H; dG, dU along I; the weight gradients' operands in 32-row
+ * blocks of each expert's rows), the context must come from an MXFP8 forward
+ * of the same schedule, and `weights` is either
+ *   - the BF16 weights with every scale pointer NULL: they are transposed
+ *     and quantized on the device in this call, or
+ *   - the weights already transposed and quantized by
+ *     mok_mxfp8_quantize_transposed, with every scale pointer set (the
+ *     pages' workflow of weights pre-quantized by a separate call, [R]
+ *     "Tuning the five hyperparameters before production"): routed_down
+ *     [E, I, H] codes with [E*I, H/32] scales (W_d^T, blocks along H);
+ *     routed_gate / routed_up [E, H, I] with [E*H, I/32] (blocks along I);
+ *     shared_down [I_s, H] with [I_s, H/32]; shared_gate / shared_up
+ *     [H, I_s] with [H, I_s/32].
+ *   Some but not all scale pointers set: MOK_ERR_INVALID_ARGUMENT.
  * MXFP8 mode returns MOK_ERR_UNSUPPORTED unless H, I and I_s are multiples
  * of 128. Uses only the workspace's scratch (no allocation). Every weight
  * gradient is written in full (zero for experts with no kept rows, and for
@@ -283,6 +294,22 @@ mok_status mok_backward(mok_workspace* ws, mok_mode mode, const void* schedule, 
  */
 mok_status mok_mxfp8_quantize(const void* src, int src_is_fp32, int64_t rows, int64_t cols, int64_t ld_src,
                               int axis, uint8_t* dst, int64_t ld_dst, uint8_t* dst_scale, void* stream);
+
+/*
+ * Transposed MXFP8 quantization of a batch of bf16 matrices, the weights'
+ * form for the MXFP8 backward ([R] "Tuning the five hyperparameters before
+ * production": weights are quantized by a separate call). src: device bf16
+ * [batches, rows, cols], dense. dst: E4M3 [batches, cols, rows] (the
+ * transpose), quantized in blocks of 32 consecutive elements along its rows
+ * (the source's `rows` dimension, which is the backward GEMM's contraction);
+ * dst_scale: E8M0 [batches, cols, rows/32]. Codes and scales follow the rule
+ * of mok_mxfp8_quantize. rows % 128 == 0 and cols % 64 == 0, src and dst
+ * 16-byte aligned, dst_scale 4-byte aligned (MOK_ERR_UNSUPPORTED otherwise).
+ * Runs on the current device. For W_d [E, H, I]: batches E, rows H, cols I;
+ * W_g / W_u [E, I, H]: rows I, cols H; the shared weights with batches 1.
+ */
+mok_status mok_mxfp8_quantize_transposed(const void* src, int64_t batches, int64_t rows, int64_t cols, uint8_t* dst,
+                                         uint8_t* dst_scale, void* stream);
 
 /* ---- diagnostics (these synchronise; never on the hot path) ---------- */
 

@@ -24,7 +24,8 @@ from . import _lib
 from ._lib import (MOK_MODE_BF16, MOK_MODE_MXFP8, HDR_FIELDS, TILE_BMS, MokError)
 
 __all__ = ["MoKConfig", "Workspace", "create_workspace", "get_workspace", "clear_workspace_cache",
-           "build_schedule", "forward", "backward", "mxfp8_quantize", "schedule_fields",
+           "build_schedule", "forward", "backward", "mxfp8_quantize",
+           "mxfp8_quantize_transposed", "mxfp8_backward_weights", "schedule_fields",
            "schedule_bytes", "context_bytes", "MokError", "MOK_MODE_BF16", "MOK_MODE_MXFP8", "lib"]
 
 
@@ -273,3 +274,36 @@ def mxfp8_quantize(src: torch.Tensor, axis: int = 1, out: torch.Tensor | None = 
     _lib.check("mok_mxfp8_quantize", lib().mok_mxfp8_quantize(
         _ptr(s2), int(src.dtype == torch.float32), rows, cols, cols, axis, _ptr(out), cols, _ptr(scale), _stream()))
     return out, scale
+
+
+def mxfp8_quantize_transposed(src: torch.Tensor, out: torch.Tensor | None = None, scale: torch.Tensor | None = None):
+    """Transpose the last two dimensions of a bf16 device tensor [..., R, C]
+    (a weight, or a batch of them) and MXFP8-quantize it along the new rows
+    (blocks of 32 along R). Returns (codes uint8 [..., C, R], scales uint8
+    [..., C, R/32])."""
+    if src.dtype != torch.bfloat16:
+        raise ValueError("src must be bf16")
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    R, Cc = src.shape[-2], src.shape[-1]
+    B = src.numel() // (R * Cc) if src.numel() else 0
+    lead = tuple(src.shape[:-2])
+    if out is None:
+        out = torch.empty(lead + (Cc, R), dtype=torch.uint8, device=src.device)
+    if scale is None:
+        scale = torch.empty(lead + (Cc, R // 32), dtype=torch.uint8, device=src.device)
+    _lib.check("mok_mxfp8_quantize_transposed", lib().mok_mxfp8_quantize_transposed(
+        _ptr(src), B, R, Cc, _ptr(out), _ptr(scale), _stream()))
+    return out, scale
+
+
+def mxfp8_backward_weights(weights: dict) -> dict:
+    """The BF16 weights in the form the MXFP8 backward takes them
+    pre-quantized (see include/mok.h, mok_backward): each transposed and
+    quantized along the backward GEMM's contraction, with *_scale entries."""
+    q = {}
+    for name, t in weights.items():
+        if t is None or name.endswith("_scale"):
+            continue
+        q[name], q[name + "_scale"] = mxfp8_quantize_transposed(t)
+    return q

@@ -23,7 +23,7 @@ MOK_MODE_MXFP8 = 1
 EXPORTS = (
     "mok_status_string", "mok_validate_config", "mok_schedule_bytes", "mok_schedule_layout_query",
     "mok_context_bytes", "mok_workspace_bytes", "mok_workspace_create", "mok_workspace_destroy",
-    "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize", "mok_kernel_name",
+    "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize", "mok_mxfp8_quantize_transposed", "mok_kernel_name",
     "mok_workspace_set_timing", "mok_workspace_set_timing_mask", "mok_workspace_read_timing",
 )
 
@@ -97,6 +97,7 @@ def load() -> C.CDLL:
         "mok_backward": (i32, [vp, i32, vp, sz, vp, sz, vp, vp, vp, C.POINTER(MokWeights),
                                C.POINTER(MokGrads), vp]),
         "mok_mxfp8_quantize": (i32, [vp, i32, i64, i64, i64, i32, vp, i64, vp, vp]),
+        "mok_mxfp8_quantize_transposed": (i32, [vp, i64, i64, i64, vp, vp, vp]),
         "mok_kernel_name": (C.c_char_p, [i32]),
         "mok_workspace_set_timing": (i32, [vp, i32]),
         "mok_workspace_set_timing_mask": (i32, [vp, C.c_uint32]),

@@ -17,13 +17,14 @@ read for one GPU:
   through ``ctx.save_for_backward``: saved-tensor hooks (activation
   checkpointing, CPU offload) see them, and nothing else on ``ctx`` holds a
   tensor, so a layer's context lives only as long as autograd keeps it.
-- In MXFP8 mode the parameters stay BF16 (the backward reads them in BF16)
-  and the forward takes them quantized by ``mxfp8_quantize`` along H (gate,
-  up) and I (down) ([R] "Tuning the five hyperparameters before
-  production": MXFP8 takes pre-quantized weights). The quantized copy is
-  kept per parameter and made again whenever the parameter's in-place
-  version counter moves (an optimizer step, a ``copy_``), so a step never
-  runs on stale codes.
+- In MXFP8 mode the parameters stay BF16; the forward takes them quantized
+  by ``mxfp8_quantize`` along H (gate, up) and I (down), the backward
+  transposed and quantized along each backward GEMM's contraction by
+  ``mxfp8_quantize_transposed`` ([R] "Tuning the five hyperparameters
+  before production": MXFP8 takes pre-quantized weights). Each quantized
+  copy is kept per parameter and made again whenever the parameter's
+  in-place version counter moves (an optimizer step, a ``copy_``), so a
+  step never runs on stale codes.
 
 Every step of the layer runs in the library's HIP kernels; tensors on the
 CPU are rejected.
@@ -36,7 +37,7 @@ import weakref
 import torch
 
 from . import (MOK_MODE_BF16, MOK_MODE_MXFP8, MoKConfig, backward, build_schedule, context_bytes, forward,
-               get_workspace, mxfp8_quantize)
+               get_workspace, mxfp8_quantize, mxfp8_quantize_transposed)
 
 __all__ = ["MoKRuntime", "MoKAutogradFunction", "MoKExperts", "moe_layer"]
 
@@ -64,17 +65,23 @@ class MoKRuntime:
             raise ValueError("the MoE layer runs on the GPU only: inputs must be CUDA tensors")
         return get_workspace(self.cfg, device.index if device.index is not None else torch.cuda.current_device())
 
-    def quantized(self, name: str, w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
-        """MXFP8 codes and scales of a BF16 weight along its last dimension,
-        made again when the weight changed since they were made."""
-        hit = self._q.get(name)
+    def quantized(self, name: str, w: torch.Tensor, transposed: bool = False) -> tuple[torch.Tensor, torch.Tensor]:
+        """MXFP8 codes and scales of a BF16 weight along its last dimension
+        (the forward's form), or transposed and quantized along its
+        second-to-last (the backward's form), made again when the weight
+        changed since they were made."""
+        key = (name, transposed)
+        hit = self._q.get(key)
         if hit is not None:
             ref, version, ptr, codes, sc = hit
             if ref() is w and version == w._version and ptr == w.data_ptr():
                 return codes, sc
-        codes, sc = mxfp8_quantize(w.detach().reshape(-1, w.shape[-1]), axis=1)
-        codes = codes.view(w.shape)
-        self._q[name] = (weakref.ref(w), w._version, w.data_ptr(), codes, sc)
+        if transposed:
+            codes, sc = mxfp8_quantize_transposed(w.detach())
+        else:
+            codes, sc = mxfp8_quantize(w.detach().reshape(-1, w.shape[-1]), axis=1)
+            codes = codes.view(w.shape)
+        self._q[key] = (weakref.ref(w), w._version, w.data_ptr(), codes, sc)
         return codes, sc
 
     def forward_weights(self, w: dict) -> dict:
@@ -85,6 +92,18 @@ class MoKRuntime:
             if t is None:
                 continue
             q[name], q[name + "_scale"] = self.quantized(name, t)
+        return q
+
+    def backward_weights(self, w: dict) -> dict:
+        """MXFP8: the weights transposed and quantized for the backward's
+        GEMMs, kept like the forward's codes until the weight changes."""
+        if self.mode == MOK_MODE_BF16:
+            return w
+        q = {}
+        for name, t in w.items():
+            if t is None:
+                continue
+            q[name], q[name + "_scale"] = self.quantized(name, t, transposed=True)
         return q
 
 
@@ -159,7 +178,7 @@ class MoKAutogradFunction(torch.autograd.Function):
             grad_out = grad_out.to(torch.bfloat16)
         grad_out = grad_out.contiguous()
         ws = runtime.workspace(x.device)
-        g = backward(ws, sched, context, grad_out, x, router_weights, w, mode=runtime.mode)
+        g = backward(ws, sched, context, grad_out, x, router_weights, runtime.backward_weights(w), mode=runtime.mode)
         need = ctx.needs_input_grad
 
         def pick(i, name):

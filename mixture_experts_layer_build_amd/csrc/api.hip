@@ -466,7 +466,8 @@ extern "C" mok_status mok_build_schedule(mok_workspace* ws, const int64_t* top_e
   return launch_schedule(ws, top_experts, T, schedule, (hipStream_t)stream) == hipSuccess ? MOK_OK : MOK_ERR_HIP;
 }
 
-static mok_status check_weights(const mok_config& c, mok_mode mode, const mok_weights* w, bool need_scales) {
+namespace mok {
+mok_status check_weights(const mok_config& c, mok_mode mode, const mok_weights* w, bool need_scales) {
   if (!w || !w->routed_gate || !w->routed_up || !w->routed_down) return MOK_ERR_INVALID_ARGUMENT;
   const bool sh = c.shared_intermediate > 0;
   if (sh != (w->shared_gate != nullptr) || sh != (w->shared_up != nullptr) || sh != (w->shared_down != nullptr))
@@ -478,6 +479,7 @@ static mok_status check_weights(const mok_config& c, mok_mode mode, const mok_we
   }
   return MOK_OK;
 }
+}  // namespace mok
 
 extern "C" mok_status mok_forward(mok_workspace* ws, mok_mode mode, const void* schedule, size_t schedule_bytes,
                                   const void* x, const float* router_weights, const mok_weights* weights, void* out,
@@ -521,6 +523,14 @@ extern "C" mok_status mok_backward(mok_workspace* ws, mok_mode mode, const void*
   mok_status st = check_weights(ws->cfg, mode, weights, false);
   if (st != MOK_OK) return st;
   if (mode == MOK_MODE_MXFP8 && (!mxfp8_shapes_ok(ws->cfg) || !ws->bwd.mxfp8_ready)) return MOK_ERR_UNSUPPORTED;
+  // MXFP8: the scale pointers say whether the weights come transposed and
+  // quantized (all set) or in BF16 (none set)
+  const bool sh_w = ws->cfg.shared_intermediate > 0;
+  const int n_scales = (weights->routed_gate_scale != nullptr) + (weights->routed_up_scale != nullptr) +
+                       (weights->routed_down_scale != nullptr) + (weights->shared_gate_scale != nullptr) +
+                       (weights->shared_up_scale != nullptr) + (weights->shared_down_scale != nullptr);
+  const bool weights_t = mode == MOK_MODE_MXFP8 && n_scales > 0;
+  if (weights_t && n_scales != (sh_w ? 6 : 3)) return MOK_ERR_INVALID_ARGUMENT;
   const bool sh = ws->cfg.shared_intermediate > 0;
   if (!grads->dx || !grads->d_router_weights || !grads->d_routed_gate || !grads->d_routed_up ||
       !grads->d_routed_down)
@@ -541,6 +551,7 @@ extern "C" mok_status mok_backward(mok_workspace* ws, mok_mode mode, const void*
   a.ctx_h = (const char*)context + cl.h;
   a.g = grads;
   a.mxfp8 = mode == MOK_MODE_MXFP8;
+  a.weights_t = weights_t;
   return to_status(launch_backward(ws, schedule, a, (hipStream_t)stream));
 }
 
@@ -559,6 +570,23 @@ extern "C" mok_status mok_mxfp8_quantize(const void* src, int src_is_fp32, int64
   if ((((uintptr_t)src) & 15) || (((uintptr_t)dst) & 7)) return MOK_ERR_UNSUPPORTED;
   if (axis == 0 && (((uintptr_t)dst_scale) & 7)) return MOK_ERR_UNSUPPORTED;
   return launch_quantize(src, src_is_fp32, rows, cols, ld_src, axis, dst, ld_dst, dst_scale, (hipStream_t)stream) ==
+                 hipSuccess
+             ? MOK_OK
+             : MOK_ERR_HIP;
+}
+
+extern "C" mok_status mok_mxfp8_quantize_transposed(const void* src, int64_t batches, int64_t rows, int64_t cols,
+                                                    uint8_t* dst, uint8_t* dst_scale, void* stream) {
+  if (batches < 0 || rows < 0 || cols < 0) return MOK_ERR_INVALID_ARGUMENT;
+  if (batches == 0 || rows == 0 || cols == 0) return MOK_OK;
+  if (!src || !dst || !dst_scale) return MOK_ERR_INVALID_ARGUMENT;
+  if (rows % 128 != 0 || cols % 64 != 0) return MOK_ERR_UNSUPPORTED;
+  if ((((uintptr_t)src) & 15) || (((uintptr_t)dst) & 15) || (((uintptr_t)dst_scale) & 3)) return MOK_ERR_UNSUPPORTED;
+  int dev = -1, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return MOK_ERR_HIP;
+  return launch_quantize_t_matrix(src, batches, rows, cols, dst, dst_scale, cus * 4, (hipStream_t)stream) ==
                  hipSuccess
              ? MOK_OK
              : MOK_ERR_HIP;

@@ -103,6 +103,7 @@ int dw_parts(const mok_config& c) {
 // MXFP8 backward: every GEMM operand quantized along that GEMM's own
 // contraction dimension (blocks of 32, E8M0 scales), fp32 accumulation.
 //   dh_hat = Q_H(grad_out rows) Q_H(W_down)            -> dG, dU (fp32), partial dw
+//   (one pass over dG, dU: Q_r for the weight gradients and Q_I for dA)
 //   dA     = Q_I(dG) Q_I(W_gate) + Q_I(dU) Q_I(W_up)   -> dx (fixed-order sum)
 //   dW_down = Q_r(w grad_out rows)^T Q_r(h),  dW_gate = Q_r(dG)^T Q_r(x rows),  dW_up likewise
 // with Q_r in 32-row blocks of each expert's segment and h the forward's
@@ -117,9 +118,23 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
   const mok_grads* g = a.g;
   BwdScratch& b = ws->bwd;
   const int qgrid = ws->num_cus * 4;
-  {
+  // The weights transposed and quantized along each backward GEMM's
+  // contraction: W_down [E,H,I] -> [E,I,H] along H; W_gate / W_up [E,I,H] ->
+  // [E,H,I] along I. Either given so by the caller (scale pointers set,
+  // from mok_mxfp8_quantize_transposed) or made here from the BF16 weights.
+  struct Wt {
+    const uint8_t *c, *s;
+  } wd{b.wdTq, b.wdTs}, wg{b.wgTq, b.wgTs}, wu{b.wuTq, b.wuTs}, sd{b.sdTq, b.sdTs}, sg{b.sgTq, b.sgTs},
+      su{b.suTq, b.suTs};
+  if (a.weights_t) {
+    wd = {(const uint8_t*)w->routed_down, w->routed_down_scale};
+    wg = {(const uint8_t*)w->routed_gate, w->routed_gate_scale};
+    wu = {(const uint8_t*)w->routed_up, w->routed_up_scale};
+    sd = {(const uint8_t*)w->shared_down, w->shared_down_scale};
+    sg = {(const uint8_t*)w->shared_gate, w->shared_gate_scale};
+    su = {(const uint8_t*)w->shared_up, w->shared_up_scale};
+  } else {
     LaunchTimer tm(ws, MOK_K_BWD_TRANSPOSE, s);
-    // W_down [E,H,I] -> [E,I,H] along H; W_gate / W_up [E,I,H] -> [E,H,I] along I
     MOK_HIP_TRY(launch_quantize_t_matrix(w->routed_down, E, H, I, b.wdTq, b.wdTs, qgrid, s));
     MOK_HIP_TRY(launch_quantize_t_matrix(w->routed_gate, E, I, H, b.wgTq, b.wgTs, qgrid, s));
     MOK_HIP_TRY(launch_quantize_t_matrix(w->routed_up, E, I, H, b.wuTq, b.wuTs, qgrid, s));
@@ -154,10 +169,10 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
     p.router_w = a.router_w;
     p.a_tok = ws->xq;
     p.a_tok_scale = ws->xq_scale;
-    p.b0 = b.wdTq;
-    p.b0s = b.wdTs;
-    p.sb0 = b.sdTq;
-    p.sb0s = b.sdTs;
+    p.b0 = wd.c;
+    p.b0s = wd.s;
+    p.sb0 = sd.c;
+    p.sb0s = sd.s;
     p.g_in = a.ctx_g;
     p.u_in = a.ctx_u;
     p.hq_in = (const uint8_t*)a.ctx_h;
@@ -179,9 +194,14 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
     MOK_HIP_TRY(hipGetLastError());
   }
   {
+    // dG and dU (fp32) in 32-row blocks for the weight gradients, and in the
+    // same pass along I (their kept rows, row-major) for dA
     LaunchTimer tm(ws, MOK_K_BWD_QUANT, s);
-    MOK_HIP_TRY(launch_quantize_rows_sched(b.dg32, v.header, rcm, I, Is, c.max_tokens, ws->hq, ws->hq_scale, s));
-    MOK_HIP_TRY(launch_quantize_rows_sched(b.du32, v.header, rcm, I, Is, c.max_tokens, b.duq, b.duq_scale, s));
+    const TqArrays& q = b.tq;
+    MOK_HIP_TRY(launch_quantize_t_rows(4, v, b.dg32, nullptr, nullptr, nullptr, E, k, I, Is, rcm, q.kr_cap, q.dg,
+                                       q.dgs, qgrid, s, false, ws->hq, ws->hq_scale));
+    MOK_HIP_TRY(launch_quantize_t_rows(4, v, b.du32, nullptr, nullptr, nullptr, E, k, I, Is, rcm, q.kr_cap, q.du,
+                                       q.dus, qgrid, s, false, b.duq, b.duq_scale));
   }
   {
     nt::Params p{};
@@ -190,14 +210,14 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
     p.a_row_scale = ws->hq_scale;
     p.a_row2 = b.duq;
     p.a_row2_scale = b.duq_scale;
-    p.b0 = b.wgTq;
-    p.b0s = b.wgTs;
-    p.b1 = b.wuTq;
-    p.b1s = b.wuTs;
-    p.sb0 = b.sgTq;
-    p.sb0s = b.sgTs;
-    p.sb1 = b.suTq;
-    p.sb1s = b.suTs;
+    p.b0 = wg.c;
+    p.b0s = wg.s;
+    p.b1 = wu.c;
+    p.b1s = wu.s;
+    p.sb0 = sg.c;
+    p.sb0s = sg.s;
+    p.sb1 = su.c;
+    p.sb1s = su.s;
     p.out = ws->ybuf;
     LaunchTimer tm(ws, MOK_K_BWD_DX_ROWS, s);
     nt::grouped_gemm_nt<nt::BWD_DX, true><<<grid, nt::NTHR, 0, s>>>(p);
@@ -221,10 +241,6 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
                                        q.dy, q.dys, qgrid, s));
     MOK_HIP_TRY(launch_quantize_t_rows(3, v, nullptr, hq, hq + ce, nullptr, E, k, I, Is, rcm, q.kr_cap, q.h, q.hs,
                                        qgrid, s));
-    MOK_HIP_TRY(launch_quantize_t_rows(4, v, b.dg32, nullptr, nullptr, nullptr, E, k, I, Is, rcm, q.kr_cap, q.dg,
-                                       q.dgs, qgrid, s));
-    MOK_HIP_TRY(launch_quantize_t_rows(4, v, b.du32, nullptr, nullptr, nullptr, E, k, I, Is, rcm, q.kr_cap, q.du,
-                                       q.dus, qgrid, s));
   }
   {
     nt::Params p{};

@@ -190,15 +190,13 @@ hipError_t launch_quantize_t_matrix(const void* src, int64_t batches, int64_t R,
 // scales when out_bf16, kinds 0-2 only) from one source:
 // src_kind 0 = x token rows, 1 = router weight times grad_out token rows,
 // 2 = schedule-row bf16 rows, 3 = schedule-row MXFP8 rows (h), 4 =
-// schedule-row fp32 rows (dG, dU).
+// schedule-row fp32 rows (dG, dU). Kind 4 with rowq also writes the kept
+// rows quantized along their columns (row-major, the h codes' layout).
 hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* src, const uint8_t* src_codes,
                                   const uint8_t* src_scale, const float* router_w, int E, int k, int cols_r, int cols_s,
                                   int64_t rows_cap_max, int64_t kr_cap, uint8_t* dst, uint8_t* dst_scale, int grid,
-                                  hipStream_t s, bool out_bf16 = false);
-// dG / dU rows (fp32) quantized along I: routed rows [0, offsets[E]) and
-// shared rows [rows_cap_max, rows_cap_max + T).
-hipError_t launch_quantize_rows_sched(const void* src, const int32_t* hdr, int64_t rows_cap_max, int I, int Is,
-                                      int64_t max_tokens, uint8_t* dst, uint8_t* dst_scale, hipStream_t s);
+                                  hipStream_t s, bool out_bf16 = false, uint8_t* rowq = nullptr,
+                                  uint8_t* rowq_scale = nullptr);
 
 // Axis-1 MXFP8 quantization of a bf16 [T, cols] tensor whose row count T is
 // read on the device from a schedule header; the grid covers max_rows.
@@ -215,6 +213,7 @@ struct BwdArgs {
   const void* ctx_h;
   const mok_grads* g;
   int mxfp8;
+  int weights_t;  // MXFP8: `w` holds the weights transposed and quantized (mok_mxfp8_quantize_transposed)
 };
 hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& a, hipStream_t s);
 
@@ -223,6 +222,10 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
 inline float swiglu_lim(const mok_config& c) {
   return (c.swiglu_limit > 0.0f && c.swiglu_limit < __builtin_inff()) ? c.swiglu_limit : __builtin_inff();
 }
+
+// Host-side checks shared by the entry points (api.hip).
+bool mxfp8_shapes_ok(const mok_config& c);
+mok_status check_weights(const mok_config& c, mok_mode mode, const mok_weights* w, bool need_scales);
 
 // Columns of the per-row partial router-weight gradients.
 int dw_parts(const mok_config& c);

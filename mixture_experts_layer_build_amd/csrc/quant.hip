@@ -263,6 +263,8 @@ struct TqParams {
   const uint8_t* src_scale;
   uint8_t* dst;
   uint8_t* dst_scale;
+  uint8_t* rowq;        // TQ_ROWS32 (optional): the same rows quantized along their columns, row-major
+  uint8_t* rowq_scale;  // (the layout of the forward's h codes: routed rows, then shared rows)
 };
 
 // The weight-gradient GEMMs' operands: for expert e, rows of its segment in
@@ -316,6 +318,7 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
   float mul = 1.0f;
   int X = 0;
   bool have = false;
+  int64_t qo = 0, qso = 0;  // TQ_ROWS32 with rowq: the block's code and scale offsets
   auto fetch = [&](const Unit& w) {
     have = false;
     mul = 1.0f;
@@ -327,7 +330,9 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
     if (lr >= nrows) return;  // zero row past the segment's end
     const int64_t row = shared ? lr : p.offsets[w.e] + (int64_t)lr;
     if constexpr (SRC == TQ_ROWS32) {
-      const float* s = p.src32 + (shared ? p.rows_cap_max * p.cols_r : 0) + row * w.cols + c0;
+      qo = (shared ? p.rows_cap_max * p.cols_r : 0) + row * w.cols + c0;
+      qso = (shared ? p.rows_cap_max * (p.cols_r / 32) : 0) + row * (w.cols / 32) + c0 / 32;
+      const float* s = p.src32 + qo;
 #pragma unroll
       for (int q = 0; q < NV; ++q) raw[q] = *reinterpret_cast<const uint4*>(s + 4 * q);
     } else if constexpr (SRC == TQ_MX) {
@@ -359,6 +364,25 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) trow[i] = 0.f;
       return;
+    }
+    if constexpr (SRC == TQ_ROWS32) {
+      // the thread's 32 values are one block along the row: its codes for
+      // the GEMM that contracts over the columns (dA), from the same fp32
+      if (p.rowq) {
+        uint32_t amax = 0;
+#pragma unroll
+        for (int q = 0; q < NV; ++q)
+          amax = max(max(amax, max(raw[q].x & 0x7FFFFFFFu, raw[q].y & 0x7FFFFFFFu)),
+                     max(raw[q].z & 0x7FFFFFFFu, raw[q].w & 0x7FFFFFFFu));
+        const int Xr = mx_block_exponent(amax);
+        uint32_t cw[NV];
+#pragma unroll
+        for (int q = 0; q < NV; ++q)
+          cw[q] = e4m3x4_encode_scaled(u2f(raw[q].x), u2f(raw[q].y), u2f(raw[q].z), u2f(raw[q].w), Xr);
+        *reinterpret_cast<uint4*>(p.rowq + qo) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+        *reinterpret_cast<uint4*>(p.rowq + qo + 16) = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+        p.rowq_scale[qso] = (uint8_t)(Xr + 127);
+      }
     }
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
@@ -505,45 +529,6 @@ __global__ void __launch_bounds__(256) transpose_rows_bf16(TqParams p) {
   }
 }
 
-// dG / dU rows (fp32) along their I columns: the routed rows [0, offsets[E])
-// of width I and the shared rows [rows_cap_max, rows_cap_max + T) of width
-// I_s, laid out as the forward's h codes (scales [rows, cols / 32]).
-__global__ void __launch_bounds__(256) quant_rows_sched_f32(const float* __restrict__ src, const int32_t* __restrict__ hdr,
-                                                            int64_t rcm, int I, int Is, uint8_t* __restrict__ dst,
-                                                            uint8_t* __restrict__ scale) {
-  // 8 lanes per 32-element block, 4 fp32 elements per lane
-  const int64_t nb_r = rcm * (I / 32);
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t b = g >> 3;
-  const int part = (int)(g & 7);
-  bool live;
-  int64_t eoff, soff;
-  if (b < nb_r) {
-    const int64_t row = b / (I / 32), blk = b - row * (I / 32);
-    live = row < hdr[HDR_ROWS_TOTAL];
-    eoff = row * I + blk * 32;
-    soff = row * (I / 32) + blk;
-  } else {
-    const int64_t bs = b - nb_r;
-    const int64_t row = Is > 0 ? bs / (Is / 32) : 0, blk = Is > 0 ? bs - row * (Is / 32) : 0;
-    live = Is > 0 && row < hdr[HDR_T];
-    eoff = rcm * I + row * Is + blk * 32;
-    soff = rcm * (I / 32) + row * (Is / 32) + blk;
-  }
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (live) v = *reinterpret_cast<const float4*>(src + eoff + part * 4);
-  uint32_t amax = max(max(f2u(v.x) & 0x7FFFFFFFu, f2u(v.y) & 0x7FFFFFFFu),
-                      max(f2u(v.z) & 0x7FFFFFFFu, f2u(v.w) & 0x7FFFFFFFu));
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 4));
-  if (!live) return;
-  const int X = mx_block_exponent(amax);
-  const uint32_t c = e4m3x4_encode_scaled(v.x, v.y, v.z, v.w, X);
-  *reinterpret_cast<uint32_t*>(dst + eoff + part * 4) = c;
-  if (part == 0) scale[soff] = (uint8_t)(X + 127);
-}
-
 }  // namespace
 
 hipError_t launch_quantize_t_matrix(const void* src, int64_t batches, int64_t R, int64_t C, uint8_t* dst,
@@ -558,8 +543,10 @@ hipError_t launch_quantize_t_matrix(const void* src, int64_t batches, int64_t R,
 hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* src, const uint8_t* src_codes,
                                   const uint8_t* src_scale, const float* router_w, int E, int k, int cols_r, int cols_s,
                                   int64_t rows_cap_max, int64_t kr_cap, uint8_t* dst, uint8_t* dst_scale, int grid,
-                                  hipStream_t s, bool out_bf16) {
+                                  hipStream_t s, bool out_bf16, uint8_t* rowq, uint8_t* rowq_scale) {
   TqParams p{};
+  p.rowq = rowq;
+  p.rowq_scale = rowq_scale;
   p.hdr = v.header;
   p.offsets = v.offsets;
   p.kept = v.kept;
@@ -594,16 +581,6 @@ hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* 
       default: quant_t_rows<TQ_MX><<<grid, 256, 0, s>>>(p); break;
     }
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_quantize_rows_sched(const void* src, const int32_t* hdr, int64_t rows_cap_max, int I, int Is,
-                                      int64_t max_tokens, uint8_t* dst, uint8_t* dst_scale, hipStream_t s) {
-  const int64_t blocks = rows_cap_max * (I / 32) + (Is > 0 ? max_tokens * (Is / 32) : 0);
-  const int64_t grid = (blocks * 8 + 255) / 256;
-  if (grid == 0) return hipSuccess;
-  quant_rows_sched_f32<<<dim3((unsigned)grid), dim3(256), 0, s>>>((const float*)src, hdr, rows_cap_max, I, Is, dst,
-                                                                   dst_scale);
   return hipGetLastError();
 }
 

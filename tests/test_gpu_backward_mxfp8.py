@@ -161,3 +161,40 @@ def test_backward_mxfp8_8192_tokens_full_size():
         check(np64(g[gname]), ref[rname], gname)
     for k_, v in g.items():
         assert torch.isfinite(v.float()).all(), k_
+
+
+def test_mxfp8_quantize_transposed_matches_the_oracle_quantizer():
+    # the weights' backward form: transposed, then blocks of 32 along the new
+    # rows; bit-exact against the oracle quantizer on the transposed matrix
+    from oracle import mxfp8 as omx
+    rng = np.random.default_rng(61)
+    for shape in ((3, 256, 192), (384, 128), (2, 128, 128)):
+        v = (rng.standard_normal(shape) * 10.0 ** rng.integers(-4, 4, size=shape[-1])).astype(np.float32)
+        t = torch.from_numpy(v).to(torch.bfloat16).cuda()
+        codes, sc = mok.mxfp8_quantize_transposed(t)
+        torch.cuda.synchronize()
+        vt = np.swapaxes(t.float().cpu().numpy().astype(np.float64), -1, -2)
+        rc, rs = omx.quantize(vt.reshape(-1, vt.shape[-1]), axis=1)
+        np.testing.assert_array_equal(codes.cpu().numpy().reshape(rc.shape), rc, err_msg=str(shape))
+        np.testing.assert_array_equal(sc.cpu().numpy().reshape(rs.shape), rs, err_msg=str(shape))
+
+
+@pytest.mark.parametrize("Is", [128, 0])
+def test_backward_mxfp8_prequantized_weights_bit_identical(Is):
+    # weights given transposed and quantized (scale pointers set) or in BF16
+    # (quantized inside the call): the same codes, so the same bits
+    c = MoEShape("preq", T=400, H=256, I=256, E=6, k=3, I_s=Is, seed=14, w_std=0.05, mode="mxfp8",
+                 passes="fwd+bwd")
+    inp = make_inputs(c)
+    _, g1, (ws, sched, ctx, d) = gpu_fwd_bwd_mxfp8(c, inp, 1.0)
+    g1 = {k_: v.clone() for k_, v in g1.items()}
+    wt = mok.mxfp8_backward_weights(d["weights"])
+    g2 = mok.backward(ws, sched, ctx, d["grad_out"], d["x"], d["router_weights"], wt, mode=mok.MOK_MODE_MXFP8)
+    torch.cuda.synchronize()
+    for k_ in g1:
+        assert torch.equal(g1[k_].view(torch.uint8), g2[k_].view(torch.uint8)), k_
+    # some but not all scale pointers set is an argument error
+    bad = dict(wt)
+    del bad["routed_up_scale"]
+    with pytest.raises(mok.MokError):
+        mok.backward(ws, sched, ctx, d["grad_out"], d["x"], d["router_weights"], bad, mode=mok.MOK_MODE_MXFP8)
