@@ -275,6 +275,28 @@ mok_status mok_backward(mok_workspace* ws, mok_mode mode, const void* schedule, 
                         void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * inference forward of mok_forward (context = NULL) without a workspace.
+ * Its scratch (h, the weighted down rows y, and x's MXFP8 codes) is a fixed
+ * device array of the library, 128 MiB per GPU, held from the first call on
+ * a GPU until the process ends; the call allocates nothing. Scratch needed,
+ * with n = rows_cap_max * I + max_tokens * I_s (rows_cap_max from
+ * mok_schedule_layout_query) and each part rounded up to 256 bytes: h, 2n
+ * bytes (BF16) or n + n/32 (MXFP8); y, (rows_cap_max + max_tokens) * H * 2;
+ * in MXFP8 also x's codes and scales, m + m/32 with m = max_tokens * H. A
+ * config that needs more returns MOK_ERR_UNSUPPORTED before anything is
+ * enqueued. cfg is the config of the workspace whose
+ * mok_build_schedule wrote `schedule` (minibatch pipeline fields are
+ * ignored: no pipeline). Runs on the current device (`stream` must belong
+ * to it). Arguments and results otherwise as mok_forward. Calls on one GPU
+ * share the array: calls that overlap on one GPU race.
+ */
+mok_status mok_forward_static(const mok_config* cfg, mok_mode mode, const void* schedule, size_t schedule_bytes,
+                              const void* x, const float* router_weights, const mok_weights* weights, void* out,
+                              void* stream);
+
+/*
  * MXFP8 quantization ([R] "Tuning the five hyperparameters before
  * production": the separate quantize call for pre-quantizing weights).
  * src: device [rows, cols] with row stride ld_src elements, bf16

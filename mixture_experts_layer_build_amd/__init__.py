@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import (MOK_MODE_BF16, MOK_MODE_MXFP8, HDR_FIELDS, TILE_BMS, MokError)
 
 __all__ = ["MoKConfig", "Workspace", "create_workspace", "get_workspace", "clear_workspace_cache",
-           "build_schedule", "forward", "backward", "mxfp8_quantize",
+           "build_schedule", "forward", "forward_static", "backward", "mxfp8_quantize",
            "mxfp8_quantize_transposed", "mxfp8_backward_weights", "schedule_fields",
            "schedule_bytes", "context_bytes", "MokError", "MOK_MODE_BF16", "MOK_MODE_MXFP8", "lib"]
 
@@ -226,6 +226,26 @@ def forward(ws: Workspace, schedule: torch.Tensor, x: torch.Tensor, router_weigh
     _lib.check("mok_forward", lib().mok_forward(
         ws.handle, mode, _ptr(schedule), schedule.numel(), _ptr(x), _ptr(router_weights), C.byref(ws_w),
         _ptr(out), _ptr(context), 0 if context is None else context.numel(), _stream()))
+    return out
+
+
+def forward_static(cfg: MoKConfig, schedule: torch.Tensor, x: torch.Tensor, router_weights: torch.Tensor,
+                   weights: dict, mode: int = MOK_MODE_BF16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The inference forward (no context) of ``forward`` without a
+    workspace: its scratch is the library's fixed device array (128 MiB per
+    GPU), so nothing is allocated on the device. Runs on the current device;
+    ``schedule`` comes from ``build_schedule`` with a workspace of the same
+    config. Raises MokError (MOK_ERR_UNSUPPORTED) when the config needs more
+    scratch than the array holds. Calls that overlap on one GPU race."""
+    if x.dtype != torch.bfloat16 or router_weights.dtype != torch.float32:
+        raise ValueError("x must be bf16 and router_weights fp32")
+    if out is None:
+        out = torch.empty_like(x)
+    c = cfg.c()
+    ws_w = _weights(weights)
+    _lib.check("mok_forward_static", lib().mok_forward_static(
+        C.byref(c), mode, _ptr(schedule), schedule.numel(), _ptr(x), _ptr(router_weights), C.byref(ws_w),
+        _ptr(out), _stream()))
     return out
 
 

@@ -23,7 +23,7 @@ MOK_MODE_MXFP8 = 1
 EXPORTS = (
     "mok_status_string", "mok_validate_config", "mok_schedule_bytes", "mok_schedule_layout_query",
     "mok_context_bytes", "mok_workspace_bytes", "mok_workspace_create", "mok_workspace_destroy",
-    "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize", "mok_mxfp8_quantize_transposed", "mok_kernel_name",
+    "mok_build_schedule", "mok_forward", "mok_forward_static", "mok_backward", "mok_mxfp8_quantize", "mok_mxfp8_quantize_transposed", "mok_kernel_name",
     "mok_workspace_set_timing", "mok_workspace_set_timing_mask", "mok_workspace_read_timing",
 )
 
@@ -94,6 +94,7 @@ def load() -> C.CDLL:
         "mok_workspace_destroy": (i32, [vp]),
         "mok_build_schedule": (i32, [vp, vp, i64, vp, sz, vp]),
         "mok_forward": (i32, [vp, i32, vp, sz, vp, vp, C.POINTER(MokWeights), vp, vp, sz, vp]),
+        "mok_forward_static": (i32, [cfgp, i32, vp, sz, vp, vp, C.POINTER(MokWeights), vp, vp]),
         "mok_backward": (i32, [vp, i32, vp, sz, vp, sz, vp, vp, vp, C.POINTER(MokWeights),
                                C.POINTER(MokGrads), vp]),
         "mok_mxfp8_quantize": (i32, [vp, i32, i64, i64, i64, i32, vp, i64, vp, vp]),
