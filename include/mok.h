@@ -81,12 +81,16 @@ typedef struct mok_config {
   int32_t expert_pad;           /* P: each expert segment padded to a multiple of P rows ([R] "Tuning...": expert padding) */
   int32_t minibatch_size;       /* tokens per minibatch: the schedule's sub-offsets, and the granularity of the
                                    forward's minibatch pipeline; 0 = one minibatch ([R] "Tuning...": minibatch_size) */
-  int32_t num_mover_wgs;        /* compute units given to the combine in the minibatch pipeline (rounded down to a
-                                   multiple of 8); 0 = no pipeline. With minibatch_size > 0 and num_mover_wgs >= 8,
-                                   mok_forward runs the down GEMM of minibatch b on the other compute units while
-                                   the combine of minibatch b-1 runs on these, on a stream the workspace owns
-                                   ([R] "Tuning...": fwd_num_comm_sms, minibatch_size). The result bits do not
-                                   depend on either value. */
+  int32_t num_mover_wgs;        /* mover workgroups of the forward's minibatch pipeline (rounded down to a multiple
+                                   of 8, at most the compute units less 32); 0 = no pipeline. With 0 <
+                                   minibatch_size < max_tokens, num_mover_wgs >= 8 and num_experts <= 256, the down
+                                   GEMM and the combine run as one launch of one workgroup per compute unit: the
+                                   others run the down tiles minibatch by minibatch and count each finished tile,
+                                   and these combine minibatch b as soon as its count is complete, while the tiles
+                                   of later minibatches run ([R] "Tuning...": fwd_num_comm_sms, minibatch_size).
+                                   A mover's wait is bounded (about 2 s in all); one that runs out of time is
+                                   counted in mok_workspace_read_status. The result bits do not depend on either
+                                   value. */
   float swiglu_limit;           /* SwiGLU input limit L ([A] _MoKRuntime(mok_config, swiglu_limit); the pages give
                                    no formula): L > 0 computes h = silu(min(g, L)) * clamp(u, -L, L), and the
                                    backward passes no gradient where a clamp is active (g > L, |u| > L);
@@ -358,6 +362,15 @@ typedef enum mok_kernel_id {
 } mok_kernel_id;
 
 const char* mok_kernel_name(int kernel_id);
+/* Waits for the device, then returns (and resets) two counts since the last
+ * call: *pipeline_timeouts, mover waits of the forward's minibatch pipeline
+ * that ran out of time (their minibatches' outputs are then incomplete; 0 in
+ * normal operation), and *schedule_mismatches, launches of this workspace
+ * that were given a schedule whose header carries another configuration's
+ * hash (such a launch does nothing: its outputs are not written). Either
+ * pointer may be NULL. Returns MOK_ERR_CONFIG_MISMATCH when
+ * schedule_mismatches is non-zero. */
+mok_status mok_workspace_read_status(mok_workspace* ws, int32_t* pipeline_timeouts, int32_t* schedule_mismatches);
 /* enable != 0: time every kernel; 0: none. */
 mok_status mok_workspace_set_timing(mok_workspace* ws, int enable);
 /* Time only the kernels whose bit (1 << mok_kernel_id) is set; 0 = none.

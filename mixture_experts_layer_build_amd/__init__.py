@@ -151,6 +151,17 @@ class Workspace:
         _lib.check("mok_workspace_read_timing", lib().mok_workspace_read_timing(self.handle, ms, cnt, n))
         return {lib().mok_kernel_name(i).decode(): (float(ms[i]), int(cnt[i])) for i in range(n) if cnt[i]}
 
+    def read_status(self) -> tuple[int, int]:
+        """(mover waits of the minibatch pipeline that ran out of time,
+        launches given a schedule of another configuration) since the last
+        call, both 0 in normal operation; synchronises the device. Does not
+        raise on a mismatch: the count says it."""
+        v, m = C.c_int32(0), C.c_int32(0)
+        st = lib().mok_workspace_read_status(self.handle, C.byref(v), C.byref(m))
+        if st not in (_lib.MOK_OK, _lib.MOK_ERR_CONFIG_MISMATCH):
+            _lib.check("mok_workspace_read_status", st)
+        return int(v.value), int(m.value)
+
 
 def create_workspace(cfg: MoKConfig, device: int | None = None) -> Workspace:
     """A new workspace owned by the caller (not cached)."""

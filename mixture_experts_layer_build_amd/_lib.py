@@ -25,6 +25,7 @@ EXPORTS = (
     "mok_context_bytes", "mok_workspace_bytes", "mok_workspace_create", "mok_workspace_destroy",
     "mok_build_schedule", "mok_forward", "mok_forward_static", "mok_backward", "mok_mxfp8_quantize", "mok_mxfp8_quantize_transposed", "mok_kernel_name",
     "mok_workspace_set_timing", "mok_workspace_set_timing_mask", "mok_workspace_read_timing",
+    "mok_workspace_read_status",
 )
 
 HDR_FIELDS = ("T", "k", "E", "C", "P", "rows_cap", "n_mb", "minibatch", "dropped", "invalid",
@@ -103,6 +104,7 @@ def load() -> C.CDLL:
         "mok_workspace_set_timing": (i32, [vp, i32]),
         "mok_workspace_set_timing_mask": (i32, [vp, C.c_uint32]),
         "mok_workspace_read_timing": (i32, [vp, C.POINTER(C.c_float), C.POINTER(i64), i32]),
+        "mok_workspace_read_status": (i32, [vp, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

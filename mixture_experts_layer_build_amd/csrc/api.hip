@@ -136,6 +136,7 @@ enum ScratchPart : int {
   SP_DGUH,       // dG, dU, w*h (3 x context-sized)
   SP_DWP,        // partial router-weight gradients
   SP_ROWS,       // transposed operands of the weight-gradient GEMMs
+  SP_PIPE,       // the minibatch pipeline's counters and its status word
   SP_COUNT
 };
 
@@ -207,7 +208,8 @@ size_t workspace_bytes(const mok_config& c, const Layout& L, size_t* parts) {
       3 * align_up((size_t)E * I * H * 2, 256) + 3 * align_up((size_t)Is * H * 2, 256),
       3 * align_up(ce * 2, 256),
       (size_t)(rowsR + Tm) * dw_parts(c) * 4,
-      bf16_dw_plan(c, L).rows};
+      bf16_dw_plan(c, L).rows,
+      (size_t)(L.n_mb_max + 64) * 4};
   if (mxfp8_shapes_ok(c)) {
     const Fp8BwdPlan f = fp8_bwd_plan(c, L);
     p[SP_WT] = std::max(p[SP_WT], f.wt);
@@ -414,21 +416,13 @@ extern "C" mok_status mok_workspace_create(const mok_config* c, int device, mok_
     }
     p += parts[SP_ROWS];
   }
-  // minibatch pipeline: an auxiliary stream (default priority) for the
-  // combine and one event per minibatch plus a join event
-  if (c->minibatch_size > 0 && c->num_mover_wgs > 0 && (int64_t)c->minibatch_size < c->max_tokens) {
-    const int64_t n_mbq = (c->max_tokens + c->minibatch_size - 1) / c->minibatch_size;
-    bool ok = hipStreamCreateWithFlags(&ws->aux_stream, hipStreamNonBlocking) == hipSuccess;
-    for (int64_t i = 0; ok && i <= n_mbq; ++i) {
-      hipEvent_t e;
-      ok = hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
-      if (ok) ws->mb_events.push_back(e);
-    }
-    if (!ok) {
-      (void)mok_workspace_destroy(ws);
-      return MOK_ERR_HIP;
-    }
+  ws->status = (int32_t*)p;  // status words first, then the counters
+  ws->pipe_cnt = (int32_t*)p + 64;
+  if (hipMemset(p, 0, parts[SP_PIPE]) != hipSuccess) {
+    (void)mok_workspace_destroy(ws);
+    return MOK_ERR_HIP;
   }
+  p += parts[SP_PIPE];
   *out = ws;
   return MOK_OK;
 }
@@ -444,8 +438,6 @@ extern "C" mok_status mok_workspace_destroy(mok_workspace* ws) {
       (void)hipEventDestroy(l.stop);
     }
     for (auto e : ws->event_pool) (void)hipEventDestroy(e);
-    for (auto e : ws->mb_events) (void)hipEventDestroy(e);
-    if (ws->aux_stream && hipStreamDestroy(ws->aux_stream) != hipSuccess) st = MOK_ERR_HIP;
     if (ws->scratch && hipFree(ws->scratch) != hipSuccess) st = MOK_ERR_HIP;
   }
   delete ws;
@@ -616,6 +608,20 @@ extern "C" mok_status mok_workspace_set_timing_mask(mok_workspace* ws, uint32_t 
   if (!ws) return MOK_ERR_INVALID_ARGUMENT;
   ws->timing_mask = kernel_mask & ((1u << MOK_K_COUNT) - 1u);
   return MOK_OK;
+}
+
+extern "C" mok_status mok_workspace_read_status(mok_workspace* ws, int32_t* pipeline_timeouts,
+                                                int32_t* schedule_mismatches) {
+  if (!ws) return MOK_ERR_INVALID_ARGUMENT;
+  DeviceGuard g(ws->device);
+  if (!g.ok) return MOK_ERR_HIP;
+  int32_t st[2] = {0, 0};
+  if (hipDeviceSynchronize() != hipSuccess) return MOK_ERR_HIP;
+  if (hipMemcpy(st, ws->status, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess) return MOK_ERR_HIP;
+  if (hipMemset(ws->status, 0, sizeof(st)) != hipSuccess) return MOK_ERR_HIP;
+  if (pipeline_timeouts) *pipeline_timeouts = st[0];
+  if (schedule_mismatches) *schedule_mismatches = st[1];
+  return st[1] > 0 ? MOK_ERR_CONFIG_MISMATCH : MOK_OK;
 }
 
 extern "C" mok_status mok_workspace_read_timing(mok_workspace* ws, float* total_ms, int64_t* launches, int n) {

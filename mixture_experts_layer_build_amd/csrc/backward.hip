@@ -72,9 +72,11 @@ __global__ void __launch_bounds__(256) transpose_bf16(const uint16_t* __restrict
 
 // d_router_weights[a] = sum over parts (fixed order) of dw_part[slot_row[a]],
 // 0 for dropped or invalid assignments.
-__global__ void __launch_bounds__(256) reduce_dw(const int32_t* __restrict__ hdr, const int32_t* __restrict__ slot_row,
+__global__ void __launch_bounds__(256) reduce_dw(const int32_t* __restrict__ hdr, int hash, int32_t* status,
+                                                 const int32_t* __restrict__ slot_row,
                                                  const float* __restrict__ dw_part, int parts, int n_parts_used, int k,
                                                  float* __restrict__ dwr) {
+  if (!sched_matches(hdr, hash, status)) return;
   const int64_t n = (int64_t)hdr[HDR_T] * k;
   for (int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; a < n; a += (int64_t)gridDim.x * blockDim.x) {
     const int row = slot_row[a];
@@ -111,7 +113,9 @@ int dw_parts(const mok_config& c) {
 static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, const BwdArgs& a, hipStream_t s) {
   const mok_config& c = ws->cfg;
   const int E = c.num_experts, H = c.hidden, I = c.intermediate, Is = c.shared_intermediate, k = c.topk;
-  const SchedView v = sched_view(const_cast<void*>(sched), ws->layout);
+  SchedView v = sched_view(const_cast<void*>(sched), ws->layout);
+  v.hash = (int)config_hash(ws->cfg);
+  v.status = ws->status;
   const int64_t rcm = ws->layout.rows_cap_max;
   const size_t ce = ctx_elems(c, ws->layout);
   const mok_weights* w = a.w;
@@ -146,7 +150,7 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
   }
   {
     LaunchTimer tm(ws, MOK_K_BWD_QUANT, s);
-    MOK_HIP_TRY(launch_quantize_rows_dev(a.grad_out, v.header, c.max_tokens, H, ws->xq, ws->xq_scale, s));
+    MOK_HIP_TRY(launch_quantize_rows_dev(a.grad_out, v, c.max_tokens, H, ws->xq, ws->xq_scale, s));
   }
   const int grid = ws->num_cus;
   auto sched_params = [&](nt::Params& p, int bm) {
@@ -162,6 +166,8 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
     p.Is = Is;
     p.rows_cap_max = rcm;
     p.swiglu_lim = swiglu_lim(c);
+    p.cfg_hash = v.hash;
+    p.status = v.status;
   };
   {
     nt::Params p{};
@@ -190,7 +196,8 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
     const int n_used = nt::kDwPartsPerNTile * ((I + nt::BN - 1) / nt::BN);
     const int64_t n = c.max_tokens * k;
     const int rgrid = (int)std::min<int64_t>((n + 255) / 256, (int64_t)ws->num_cus * 16);
-    reduce_dw<<<rgrid, 256, 0, s>>>(v.header, v.slot_row, b.dw_part, dw_parts(c), n_used, k, g->d_router_weights);
+    reduce_dw<<<rgrid, 256, 0, s>>>(v.header, v.hash, v.status, v.slot_row, b.dw_part, dw_parts(c), n_used, k,
+                                    g->d_router_weights);
     MOK_HIP_TRY(hipGetLastError());
   }
   {
@@ -227,8 +234,8 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
     LaunchTimer tm(ws, MOK_K_BWD_DX_SUM, s);
     const int cgrid = (int)std::min<int64_t>(c.max_tokens, (int64_t)ws->num_cus * 8);
     const uint16_t* y = (const uint16_t*)ws->ybuf;
-    sum_slot_rows<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, Is > 0 ? y + rcm * H : nullptr,
-                                        (uint16_t*)g->dx, H, k, 0, 0);
+    sum_slot_rows<<<cgrid, 256, 0, s>>>(v.header, v.hash, v.status, v.slot_row, y, Is > 0 ? y + rcm * H : nullptr,
+                                        (uint16_t*)g->dx, H, k);
     MOK_HIP_TRY(hipGetLastError());
   }
   {
@@ -263,7 +270,9 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
   if (a.mxfp8) return launch_backward_mxfp8(ws, sched, a, s);
   const mok_config& c = ws->cfg;
   const int E = c.num_experts, H = c.hidden, I = c.intermediate, Is = c.shared_intermediate, k = c.topk;
-  const SchedView v = sched_view(const_cast<void*>(sched), ws->layout);
+  SchedView v = sched_view(const_cast<void*>(sched), ws->layout);
+  v.hash = (int)config_hash(ws->cfg);
+  v.status = ws->status;
   const int64_t rcm = ws->layout.rows_cap_max;
   const mok_weights* w = a.w;
   const mok_grads* g = a.g;
@@ -293,6 +302,8 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
     p.Is = Is;
     p.rows_cap_max = rcm;
     p.swiglu_lim = swiglu_lim(c);
+    p.cfg_hash = v.hash;
+    p.status = v.status;
   };
   {
     nt::Params p{};
@@ -317,7 +328,8 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
     const int n_used = nt::kDwPartsPerNTile * ((I + nt::BN - 1) / nt::BN);
     const int64_t n = c.max_tokens * k;
     const int rgrid = (int)std::min<int64_t>((n + 255) / 256, (int64_t)ws->num_cus * 16);
-    reduce_dw<<<rgrid, 256, 0, s>>>(v.header, v.slot_row, b.dw_part, dw_parts(c), n_used, k, g->d_router_weights);
+    reduce_dw<<<rgrid, 256, 0, s>>>(v.header, v.hash, v.status, v.slot_row, b.dw_part, dw_parts(c), n_used, k,
+                                    g->d_router_weights);
     MOK_HIP_TRY(hipGetLastError());
   }
   {
@@ -338,8 +350,8 @@ hipError_t launch_backward(mok_workspace* ws, const void* sched, const BwdArgs& 
     LaunchTimer tm(ws, MOK_K_BWD_DX_SUM, s);
     const int cgrid = (int)std::min<int64_t>(c.max_tokens, (int64_t)ws->num_cus * 8);
     const uint16_t* y = (const uint16_t*)ws->ybuf;
-    sum_slot_rows<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, Is > 0 ? y + rcm * H : nullptr,
-                                        (uint16_t*)g->dx, H, k, 0, 0);
+    sum_slot_rows<<<cgrid, 256, 0, s>>>(v.header, v.hash, v.status, v.slot_row, y, Is > 0 ? y + rcm * H : nullptr,
+                                        (uint16_t*)g->dx, H, k);
     MOK_HIP_TRY(hipGetLastError());
   }
   {

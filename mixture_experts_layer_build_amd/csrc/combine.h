@@ -17,18 +17,16 @@
 namespace mok {
 namespace {
 
-// Tokens [t0, t1) with t0 = mb_index * mb, t1 = t0 + mb when mb > 0 (one
-// minibatch), else all T tokens.
-__global__ void __launch_bounds__(256) sum_slot_rows(const int32_t* __restrict__ hdr, const int32_t* __restrict__ slot_row,
+__global__ void __launch_bounds__(256) sum_slot_rows(const int32_t* __restrict__ hdr, int hash, int32_t* status,
+                                                     const int32_t* __restrict__ slot_row,
                                                      const uint16_t* __restrict__ rows,
                                                      const uint16_t* __restrict__ rows_shared, uint16_t* __restrict__ out,
-                                                     int H, int k, int mb_index, int mb) {
+                                                     int H, int k) {
   constexpr int kBatch = 8;
+  if (!sched_matches(hdr, hash, status)) return;
   const int T = hdr[HDR_T];
-  const int t0 = mb > 0 ? min(T, mb_index * mb) : 0;
-  const int t1 = mb > 0 ? min(T, t0 + mb) : T;
   const int nchunk = H / 8;
-  for (int t = t0 + (int)blockIdx.x; t < t1; t += gridDim.x) {
+  for (int t = (int)blockIdx.x; t < T; t += gridDim.x) {
     const int32_t* sl = slot_row + (int64_t)t * k;
     for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
       float acc[8];

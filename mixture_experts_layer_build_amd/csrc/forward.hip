@@ -41,23 +41,27 @@ static void fill_schedule(nt::Params& p, const mok_workspace* ws, const SchedVie
   p.Is = c.shared_intermediate;
   p.rows_cap_max = ws->layout.rows_cap_max;
   p.swiglu_lim = swiglu_lim(c);
+  p.cfg_hash = v.hash;
+  p.status = v.status;
 }
 
-// Compute units given to the combine in the minibatch pipeline (0 = no
-// pipeline): num_mover_wgs rounded down to a multiple of the XCD count, with
-// at least one XCD's worth left to the GEMMs; the pipeline needs the tile
+// Mover workgroups of the minibatch pipeline (0 = no pipeline):
+// num_mover_wgs rounded down to a multiple of the XCD count, leaving at
+// least four XCD rounds of compute workgroups; the pipeline needs the tile
 // tables in LDS and more than one minibatch.
 int mover_units(const mok_workspace* ws) {
   const mok_config& c = ws->cfg;
   if (c.minibatch_size <= 0 || c.num_mover_wgs <= 0 || c.num_experts > nt::kMaxLdsE) return 0;
-  if ((int64_t)c.minibatch_size >= c.max_tokens || ws->aux_stream == nullptr) return 0;
+  if ((int64_t)c.minibatch_size >= c.max_tokens || ws->pipe_cnt == nullptr) return 0;
   const int m = c.num_mover_wgs / nt::kNumXcd * nt::kNumXcd;
-  return std::min(m, ws->num_cus - nt::kNumXcd);
+  return std::min(m, ws->num_cus - 4 * nt::kNumXcd);
 }
 
 hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a, hipStream_t s) {
   const mok_config& c = ws->cfg;
-  const SchedView v = sched_view(const_cast<void*>(sched), ws->layout);
+  SchedView v = sched_view(const_cast<void*>(sched), ws->layout);
+  v.hash = (int)config_hash(c);
+  v.status = ws->status;
   const int grid = ws->num_cus;  // one 512-thread workgroup per compute unit
   const size_t ce = ctx_elems(c, ws->layout);
   nt::Params p{};
@@ -73,7 +77,7 @@ hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a
     hq = a.ctx_g ? (uint8_t*)a.h : ws->hq;
     hq_scale = a.ctx_g ? (uint8_t*)a.h + ce : ws->hq_scale;
     LaunchTimer tm(ws, MOK_K_QUANT_X, s);
-    MOK_HIP_TRY(launch_quantize_rows_dev(a.x, v.header, c.max_tokens, c.hidden, ws->xq, ws->xq_scale, s));
+    MOK_HIP_TRY(launch_quantize_rows_dev(a.x, v, c.max_tokens, c.hidden, ws->xq, ws->xq_scale, s));
   }
   // gate/up
   if (a.mxfp8) {
@@ -93,6 +97,10 @@ hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a
   p.b1 = a.w->routed_up;
   p.sb0 = a.w->shared_gate;
   p.sb1 = a.w->shared_up;
+  if (mover_units(ws) > 0) {  // the pipeline's tile counters start at zero in every forward
+    p.mb_done = ws->pipe_cnt;
+    p.n_done = (int)ws->layout.n_mb_max;
+  }
   {
     LaunchTimer tm(ws, MOK_K_GATE_UP, s);
     if (a.mxfp8)
@@ -126,44 +134,32 @@ hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a
       MOK_HIP_TRY(hipGetLastError());
     }
     LaunchTimer tm(ws, MOK_K_COMBINE, s);
-    sum_slot_rows<<<cgrid, 256, 0, s>>>(v.header, v.slot_row, y, ys, (uint16_t*)a.out, c.hidden, c.topk, 0, 0);
+    sum_slot_rows<<<cgrid, 256, 0, s>>>(v.header, v.hash, v.status, v.slot_row, y, ys, (uint16_t*)a.out, c.hidden,
+                                        c.topk);
     MOK_HIP_TRY(hipGetLastError());
     return hipSuccess;
   }
-  // Minibatch pipeline ("Tuning the five hyperparameters before production":
-  // minibatch_size sets the granularity of the overlap, a set of SMs is
-  // given to the exchange). The down GEMM of minibatch b runs on the other
-  // compute units on the caller's stream; when it is done, the combine of
-  // minibatch b runs on `movers` compute units on the workspace's auxiliary
-  // stream while the down GEMM of minibatch b+1 proceeds. The host does not
-  // know T, so it launches every minibatch T_max allows; launches past the
-  // schedule's minibatch count find no rows. Each output row is computed by
-  // the same code whatever the split, so the result bits do not depend on
-  // minibatch_size or num_mover_wgs.
-  const int mb = c.minibatch_size;
-  const int n_mbq = (int)((c.max_tokens + mb - 1) / mb);
-  const int dgrid = ws->num_cus - movers;
-  d.mb = mb;
-  hipStream_t aux = ws->aux_stream;
-  for (int b = 0; b < n_mbq; ++b) {
-    d.mb_index = b;
-    {
-      LaunchTimer tm(ws, MOK_K_DOWN, s);
-      if (a.mxfp8)
-        nt::grouped_gemm_nt<nt::DOWN, true><<<dgrid, nt::NTHR, 0, s>>>(d);
-      else
-        nt::grouped_gemm_nt<nt::DOWN, false><<<dgrid, nt::NTHR, 0, s>>>(d);
-      MOK_HIP_TRY(hipGetLastError());
-    }
-    MOK_HIP_TRY(hipEventRecord(ws->mb_events[b], s));
-    MOK_HIP_TRY(hipStreamWaitEvent(aux, ws->mb_events[b], 0));
-    LaunchTimer tm(ws, MOK_K_COMBINE, aux);
-    sum_slot_rows<<<movers * 4, 256, 0, aux>>>(v.header, v.slot_row, y, ys, (uint16_t*)a.out, c.hidden, c.topk, b, mb);
-    MOK_HIP_TRY(hipGetLastError());
-  }
-  MOK_HIP_TRY(hipEventRecord(ws->mb_events[n_mbq], aux));
-  MOK_HIP_TRY(hipStreamWaitEvent(s, ws->mb_events[n_mbq], 0));
-  return hipSuccess;
+  // Minibatch pipeline in one launch ("Tuning the five hyperparameters before
+  // production": minibatch_size sets the granularity of the overlap, a set of
+  // SMs serves the exchange): one workgroup per compute unit; the compute
+  // workgroups run the down tiles minibatch by minibatch and count each
+  // finished tile in mb_done[b] (zeroed by the gate/up launch above); the last
+  // `movers` workgroups combine minibatch b as soon as its count is complete,
+  // while the tiles of later minibatches run. Each output row is summed by
+  // the same arithmetic as the stand-alone combine, so the bits do not depend
+  // on minibatch_size or num_mover_wgs.
+  d.mb = c.minibatch_size;
+  d.mb_done = ws->pipe_cnt;
+
+  d.n_movers = movers;
+  d.slot_row = v.slot_row;
+  d.comb_out = (uint16_t*)a.out;
+  LaunchTimer tm(ws, MOK_K_DOWN, s);
+  if (a.mxfp8)
+    nt::grouped_gemm_nt<nt::DOWN, true, true><<<grid, nt::NTHR, 0, s>>>(d);
+  else
+    nt::grouped_gemm_nt<nt::DOWN, false, true><<<grid, nt::NTHR, 0, s>>>(d);
+  return hipGetLastError();
 }
 
 }  // namespace mok

@@ -73,8 +73,17 @@ struct Params {
   const int32_t* tiles;    // prefix sums of 256-row tiles per expert; [E] routed total, [E+1] with shared
   const int32_t* row_src;
   const int32_t* mb_offsets;    // per (minibatch, expert) first rows, [(n_mb + 1) * E]
-  int mb_index;                 // DOWN with mb > 0: only the rows of minibatch mb_index (minibatch pipeline)
-  int mb;                       // tokens per minibatch; 0 = every row
+  int mb;                       // DOWN: tokens per minibatch of the pipeline (0 = no pipeline: one pass over every row)
+  // DOWN minibatch pipeline (mb > 0): the last n_movers workgroups combine
+  // minibatch b once mb_done[b] counts all of its tiles, while the others
+  // run the tiles of later minibatches
+  int32_t* mb_done;             // per-minibatch finished-tile counters (zeroed by the gate/up launch)
+  int n_done;                   // GATE_UP: how many counters it zeroes
+  int32_t* status;              // [0]: a mover's wait that ran out of time adds 1; [1]: schedule mismatches
+  int cfg_hash;                 // the configuration hash the schedule's header must carry
+  int n_movers;
+  const int32_t* slot_row;      // [T*k] the row of each assignment (combine)
+  uint16_t* comb_out;           // the layer output [T, H] bf16 (combine)
   int E, k, H, I, Is;
   int64_t rows_cap_max;
   // SwiGLU input limit L: h = silu(min(g, L)) * clamp(u, -L, L); +inf = none
@@ -176,9 +185,120 @@ __device__ __forceinline__ int n_of(const Params& p, bool shared) {
   return (MODE == GATE_UP || MODE == BWD_DH) ? Iv : p.H;
 }
 
-template <int MODE, bool FP8>
+// Down tiles of minibatch b of the pipeline: per expert, its rows of
+// tokens in [b mb, (b + 1) mb) in 256-row tiles, times the N tiles; plus the
+// shared expert's rows of those tokens. Every thread of the workgroup gets
+// the total (a workgroup reduction through L.wsum).
+__device__ __forceinline__ int pipe_tiles_of(const Params& p, Lds& L, int b, int T) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = p.E, nt = (p.H + BN - 1) / BN;  // down's N tiles: the same for routed and shared rows
+  int cnt = 0;
+  for (int e = tid; e < E; e += NTHR)
+    cnt += (p.mb_offsets[(b + 1) * E + e] - p.mb_offsets[b * E + e] + BM - 1) / BM * nt;
+  if (tid == 0 && p.Is > 0) {
+    const int t0 = min(T, b * p.mb), t1 = min(T, t0 + p.mb);
+    cnt += (t1 - t0 + BM - 1) / BM * nt;
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) cnt += __shfl_xor(cnt, d);
+  __syncthreads();  // L.wsum is free (a previous read has completed)
+  if (lane == 0) L.wsum[0][wave] = cnt;
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < NTHR / 64; ++w) total += L.wsum[0][w];
+  return total;
+}
+
+// A mover workgroup of the down GEMM's minibatch pipeline. For each
+// minibatch b in order: wait (bounded) until the compute workgroups have
+// counted all of b's down tiles in mb_done[b], then combine b's tokens:
+// out[t] = bf16(sum over j in slot order of y[slot_row[t, j]], then + the
+// shared row), fp32 adds, as the stand-alone combine does, so the bits do
+// not depend on the split. The y rows come from other XCDs' L2s: they were
+// stored, and are loaded here, at agent scope (sc1), and a tile is counted
+// only after all of its stores completed. A wait that runs out of time adds
+// 1 to status[0] and gives up on the remaining waits (the kernel always
+// ends; the host reads the flag).
+__device__ __forceinline__ void pipe_mover(const Params& p, Lds& L, int T) {
+  constexpr int kSleepsPerWait = 1 << 20;   // s_sleep 64 (~2 us each): about 2 s in all
+  const int tid = threadIdx.x;
+  const int n_mb = p.hdr[HDR_NMB];
+  const int mover = (int)blockIdx.x - ((int)gridDim.x - p.n_movers);
+  const int H = p.H, k = p.k, nchunk = H / 8;
+  const uint16_t* y = (const uint16_t*)p.out;
+  const uint16_t* ys = p.Is > 0 ? y + p.rows_cap_max * (int64_t)H : nullptr;
+  int budget = kSleepsPerWait;  // shared by every wait of this workgroup (thread 0's copy counts)
+  for (int b = 0; b < n_mb; ++b) {
+    const int target = pipe_tiles_of(p, L, b, T);
+    if (tid == 0) {
+      int seen = __hip_atomic_load(p.mb_done + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      while (seen < target && budget > 0) {
+        __builtin_amdgcn_s_sleep(64);
+        --budget;
+        seen = __hip_atomic_load(p.mb_done + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (seen < target) {
+        budget = 0;
+        __hip_atomic_fetch_add(p.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();  // the wait is over for every thread; no load below moves above it
+    asm volatile("" ::: "memory");
+    const int t0 = min(T, b * p.mb), t1 = min(T, t0 + p.mb);
+    // two tokens at a time (one per half workgroup), 16 bytes of a row per thread
+    for (int t = t0 + 2 * mover + (tid >> 8); t < t1; t += 2 * p.n_movers) {
+      const int32_t* sl = p.slot_row + (int64_t)t * k;
+      for (int c = tid & 255; c < nchunk; c += 256) {
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+        auto add = [&](uint64_t lo, uint64_t hi) {
+          const uint32_t w[4] = {(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += u2f(w[q] << 16);
+            acc[2 * q + 1] += u2f(w[q] & 0xFFFF0000u);
+          }
+        };
+        for (int j0 = 0; j0 < k; j0 += 8) {
+          int row[8];
+          uint64_t lo[8], hi[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            row[u] = j0 + u < k ? sl[j0 + u] : -1;
+            lo[u] = hi[u] = 0;
+            if (row[u] >= 0) {
+              const uint64_t* src = reinterpret_cast<const uint64_t*>(y + (int64_t)row[u] * H + c * 8);
+              lo[u] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              hi[u] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (row[u] >= 0) add(lo[u], hi[u]);
+        }
+        if (ys) {
+          const uint64_t* src = reinterpret_cast<const uint64_t*>(ys + (int64_t)t * H + c * 8);
+          add(__hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+              __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
+        u32x4 o;
+        o[0] = pack_bf16x2(acc[0], acc[1]);
+        o[1] = pack_bf16x2(acc[2], acc[3]);
+        o[2] = pack_bf16x2(acc[4], acc[5]);
+        o[3] = pack_bf16x2(acc[6], acc[7]);
+        *reinterpret_cast<u32x4*>(p.comb_out + (int64_t)t * H + c * 8) = o;
+      }
+    }
+  }
+}
+
+// PIPE (MODE == DOWN only): the minibatch pipeline, movers included.
+template <int MODE, bool FP8, bool PIPE = false>
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
 grouped_gemm_nt(Params p) {
+  static_assert(!PIPE || MODE == DOWN, "the pipeline is the down GEMM's");
   __shared__ Lds L;
   constexpr int ES = FP8 ? 1 : 2;           // element size in bytes
   constexpr int KS = ROWB / ES;             // K elements per step
@@ -188,6 +308,7 @@ grouped_gemm_nt(Params p) {
   const int lr = lane & 31, lh = lane >> 5;
   const int E = p.E;
 
+  if (!sched_matches(p.hdr, p.cfg_hash, p.status)) return;  // before any barrier: the whole grid returns
   const bool lds_tiles = E <= kMaxLdsE;
   if (lds_tiles) {
     for (int i = tid; i < E + 2; i += NTHR) L.tiles[i] = p.tiles[i];
@@ -197,22 +318,32 @@ grouped_gemm_nt(Params p) {
     }
   }
   const int T = p.hdr[HDR_T];
+  if (MODE == GATE_UP && p.mb_done && blockIdx.x == 0)  // for the pipelined down launch that follows
+    for (int i = tid; i < p.n_done; i += NTHR) p.mb_done[i] = 0;
   __syncthreads();
-  // shared-expert rows of this launch: every token, or one minibatch's tokens
+  // the down GEMM's minibatch pipeline (one launch): movers combine, the
+  // other workgroups run the tiles minibatch by minibatch
+  constexpr bool pipe = PIPE;
+  if (pipe && (int)blockIdx.x >= (int)gridDim.x - p.n_movers) {
+    pipe_mover(p, L, T);
+    return;
+  }
+  const int n_pass = pipe ? p.hdr[HDR_NMB] : 1;  // (1 at compile time without the pipeline)
+  for (int pass = 0; pass < n_pass; ++pass) {
+  // shared-expert rows of this pass: every token, or one minibatch's tokens
   int sh0 = 0, sh1 = T;
-  if (MODE == DOWN && p.mb > 0) {
-    // minibatch pipeline: only minibatch b's rows, expert e's being rows
-    // [mb_offsets[b][e], mb_offsets[b+1][e]) of its segment (the schedule
-    // has n_mb minibatches; launches past them get no tiles). The tile table
+  if (pipe) {
+    // minibatch b = pass: only its rows, expert e's being rows
+    // [mb_offsets[b][e], mb_offsets[b+1][e]) of its segment. The tile table
     // of these row ranges is built here (the launcher keeps E <= kMaxLdsE).
-    const int b = p.mb_index;
-    const bool real = b < p.hdr[HDR_NMB];
-    sh0 = real ? min(T, b * p.mb) : T;
-    sh1 = real ? min(T, sh0 + p.mb) : T;
+    const int b = pass;
+    sh0 = min(T, b * p.mb);
+    sh1 = min(T, sh0 + p.mb);
     int cnt = 0;
+    __syncthreads();  // the previous pass's tables are no longer read
     if (tid < E) {
-      const int lo = real ? p.mb_offsets[b * E + tid] : 0;
-      const int hi = real ? p.mb_offsets[(b + 1) * E + tid] : 0;
+      const int lo = p.mb_offsets[b * E + tid];
+      const int hi = p.mb_offsets[(b + 1) * E + tid];
       L.offs[tid] = lo;
       L.keptl[tid] = hi - lo;
       cnt = (hi - lo + BM - 1) / BM;
@@ -258,9 +389,10 @@ grouped_gemm_nt(Params p) {
   // idle wave half skips), which then fill the last round. The other modes
   // keep the natural order (an expert's tiles together, its tail tile right
   // after its full ones), which reads each expert's weights once.
-  const int nq = (gridDim.x % kNumXcd) == 0 ? kNumXcd : 1;
+  const int ncomp = (int)gridDim.x - (pipe ? p.n_movers : 0);  // compute workgroups (the movers are the last)
+  const int nq = (ncomp % kNumXcd) == 0 ? kNumXcd : 1;
   const int xq = blockIdx.x % nq;
-  const int slot = blockIdx.x / nq, slots = gridDim.x / nq;
+  const int slot = blockIdx.x / nq, slots = ncomp / nq;
   // experts with at least kGroupM M tiles on average
   const bool deep = n_routed_mt >= kGroupM * E;
   // longest-first lists: always for gate/up and dh; for down (not in a
@@ -268,7 +400,7 @@ grouped_gemm_nt(Params p) {
   // experts are deep, where the ragged tail tiles otherwise end the kernel
   // unevenly (at shallow experts the natural order measured faster for them)
   const bool lpt = lds_tiles && (MODE == GATE_UP || MODE == BWD_DH ||
-                                 (deep && (MODE == BWD_DX || (MODE == DOWN && p.mb == 0))));
+                                 (deep && (MODE == BWD_DX || (MODE == DOWN && !pipe))));
   int TFr = 0, TF = 0, TTr = 0, TT = 0, f0 = 0, nf = 0, u0 = 0, qlen = 0, id0 = 0;
   if (lpt) {
     // counts of full and tail M tiles per expert (index E = shared expert),
@@ -492,7 +624,10 @@ grouped_gemm_nt(Params p) {
     // a tile without a valid row (the schedule counts tiles from kept rows,
     // so none is listed; kept as a guard) would turn the byte counts of its
     // buffer resources negative: skip it, the same decision in every wave
-    if (rows_here <= 0) continue;
+    if (rows_here <= 0) {
+      if (pipe && tid == 0) __hip_atomic_fetch_add(p.mb_done + pass, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      continue;
+    }
     // 32-row MFMA blocks of this wave's 128 rows that hold valid rows
     // (uniform across the wave): 4 except in a segment's last tile
     const int live_blocks = min(4, max(0, (rows_here - wm * 128 + 31) / 32));
@@ -996,7 +1131,17 @@ grouped_gemm_nt(Params p) {
           const int r = it * 8 + (lane >> 3);
           const int ml = wm * 128 + half * 64 + r;
           const u32x4 v = *reinterpret_cast<const u32x4*>(reg + r * SW + (lane & 7) * 8);
-          if (ml < rows_here && col < Nd) *reinterpret_cast<u32x4*>(ob + (int64_t)(t.m0 + ml) * ldo + col) = v;
+          if (ml < rows_here && col < Nd) {
+            if (pipe) {  // read by movers on other XCDs within this launch: stored at agent scope
+              uint64_t* d8 = reinterpret_cast<uint64_t*>(ob + (int64_t)(t.m0 + ml) * ldo + col);
+              __hip_atomic_store(d8, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(d8 + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+              *reinterpret_cast<u32x4*>(ob + (int64_t)(t.m0 + ml) * ldo + col) = v;
+            }
+          }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
@@ -1114,8 +1259,12 @@ grouped_gemm_nt(Params p) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
     }
+    if (pipe) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's y stores are complete
     __syncthreads();  // row metadata and LDS stages are reused by the next tile
+    if (pipe && tid == 0)  // every thread's stores of the tile completed: count it
+      __hip_atomic_fetch_add(p.mb_done + pass, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  }  // pass
 }
 
 }  // namespace nt

@@ -57,6 +57,10 @@ struct SchedView {
   int32_t* row_src;     // [rows_cap_max]
   int32_t* slot_row;    // [T_max*k]
   int32_t* tiles;       // [4][E+2]
+  // not part of the buffer: the hash of the configuration the reading
+  // launches expect in header[HDR_HASH], and where they count a mismatch
+  int hash = 0;
+  int32_t* status = nullptr;
 };
 SchedView sched_view(void* base, const Layout& L);
 
@@ -139,10 +143,11 @@ struct mok_workspace {
   uint8_t* hq_scale = nullptr;     // its E8M0 scales, one per 32 along I
   // backward scratch
   mok::BwdScratch bwd;
-  // minibatch pipeline: the combine runs on aux_stream (mover compute units)
-  // while the down GEMM of the next minibatch runs on the caller's stream
-  hipStream_t aux_stream = nullptr;
-  std::vector<hipEvent_t> mb_events;  // one per minibatch (down done), then the join
+  // minibatch pipeline of the down GEMM: per-minibatch finished-tile
+  // counters; status words: [0] mover waits that ran out of time, [1]
+  // launches that found a schedule of another configuration
+  int32_t* pipe_cnt = nullptr;     // [n_mb_max]
+  int32_t* status = nullptr;       // [2]
   // timing
   uint32_t timing_mask = 0;  // bit k: time launches of kernel id k
   std::vector<mok::TimedLaunch> launches;
@@ -200,7 +205,7 @@ hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* 
 
 // Axis-1 MXFP8 quantization of a bf16 [T, cols] tensor whose row count T is
 // read on the device from a schedule header; the grid covers max_rows.
-hipError_t launch_quantize_rows_dev(const void* src, const int32_t* hdr, int64_t max_rows, int64_t cols, uint8_t* dst,
+hipError_t launch_quantize_rows_dev(const void* src, const SchedView& v, int64_t max_rows, int64_t cols, uint8_t* dst,
                                     uint8_t* dst_scale, hipStream_t s);
 
 struct BwdArgs {
@@ -226,6 +231,16 @@ inline float swiglu_lim(const mok_config& c) {
 // Host-side checks shared by the entry points (api.hip).
 bool mxfp8_shapes_ok(const mok_config& c);
 mok_status check_weights(const mok_config& c, mok_mode mode, const mok_weights* w, bool need_scales);
+
+// Start of every launch that reads a schedule: false when the schedule's
+// header carries another configuration's hash (the launch then does
+// nothing; one thread of workgroup 0 counts it in status[1]).
+__device__ __forceinline__ bool sched_matches(const int32_t* hdr, int hash, int32_t* status) {
+  if (hdr[HDR_HASH] == hash) return true;
+  if (status && blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_fetch_add(status + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
+}
 
 // Columns of the per-row partial router-weight gradients.
 int dw_parts(const mok_config& c);

@@ -72,8 +72,9 @@ __global__ void __launch_bounds__(256) quant_axis1_bf16(const uint16_t* __restri
 // The same with the row count read on the device (the schedule header's
 // token count), over a grid sized for max_rows.
 __global__ void __launch_bounds__(256) quant_rows_dev_bf16(const uint16_t* __restrict__ src, const int32_t* __restrict__ hdr,
-                                                           int64_t cols, uint8_t* __restrict__ dst,
-                                                           uint8_t* __restrict__ scale) {
+                                                           int hash, int32_t* status, int64_t cols,
+                                                           uint8_t* __restrict__ dst, uint8_t* __restrict__ scale) {
+  if (!sched_matches(hdr, hash, status)) return;
   const int64_t row = blockIdx.x;
   if (row >= hdr[HDR_T]) return;
   quant_row_bf16(src + row * cols, dst + row * cols, scale + row * (cols >> 5), (int)(cols >> 3));
@@ -249,6 +250,8 @@ enum TqSrc : int {
 constexpr int kMaxT128 = 1024 + 2;  // experts + 2 entries of a workspace's largest tile table
 
 struct TqParams {
+  int hash;             // the configuration hash the schedule's header must carry
+  int32_t* status;      // where a mismatch is counted
   const int32_t* hdr;
   const int32_t* offsets;
   const int32_t* kept;
@@ -276,6 +279,7 @@ template <int SRC>
 __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
   __shared__ float tile[kTqRows][kTqLd];
   __shared__ int32_t t128[kMaxT128];  // the per-expert 128-row tile prefix sums, searched per unit
+  if (!sched_matches(p.hdr, p.hash, p.status)) return;  // before any barrier
   const int E = p.E;
   const int T = p.hdr[HDR_T];
   for (int i = threadIdx.x; i <= E + 1; i += blockDim.x) t128[i] = p.tiles128[i];
@@ -444,6 +448,7 @@ template <int SRC>
 __global__ void __launch_bounds__(256) transpose_rows_bf16(TqParams p) {
   __shared__ uint32_t tile[kTbCols][kTbLd];
   __shared__ int32_t t128[kMaxT128];  // the per-expert 128-row tile prefix sums, searched per unit
+  if (!sched_matches(p.hdr, p.hash, p.status)) return;  // before any barrier
   const int E = p.E;
   const int T = p.hdr[HDR_T];
   for (int i = threadIdx.x; i <= E + 1; i += blockDim.x) t128[i] = p.tiles128[i];
@@ -548,6 +553,8 @@ hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* 
   p.rowq = rowq;
   p.rowq_scale = rowq_scale;
   p.hdr = v.header;
+  p.hash = v.hash;
+  p.status = v.status;
   p.offsets = v.offsets;
   p.kept = v.kept;
   p.tiles128 = v.tiles + tile_bm_index(128) * (E + 2);
@@ -591,10 +598,10 @@ static int row_threads(int64_t cols) {
   return (int)std::min<int64_t>(256, std::max<int64_t>(64, (nchunk / 4 + 63) / 64 * 64));
 }
 
-hipError_t launch_quantize_rows_dev(const void* src, const int32_t* hdr, int64_t max_rows, int64_t cols, uint8_t* dst,
+hipError_t launch_quantize_rows_dev(const void* src, const SchedView& v, int64_t max_rows, int64_t cols, uint8_t* dst,
                                     uint8_t* dst_scale, hipStream_t s) {
   if (max_rows == 0 || cols == 0) return hipSuccess;
-  quant_rows_dev_bf16<<<dim3((unsigned)max_rows), dim3(row_threads(cols)), 0, s>>>((const uint16_t*)src, hdr, cols,
+  quant_rows_dev_bf16<<<dim3((unsigned)max_rows), dim3(row_threads(cols)), 0, s>>>((const uint16_t*)src, v.header, v.hash, v.status, cols,
                                                                                   dst, dst_scale);
   return hipGetLastError();
 }

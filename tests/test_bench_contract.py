@@ -41,6 +41,7 @@ def test_bench_json_line_contract():
     assert "traffic" in rf
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    assert cb["cpu_model"] and cb["blas"] and cb["host_cpus"] >= 1
 
 
 @pytest.mark.gpu

@@ -271,26 +271,35 @@ def test_autograd_mxfp8_requantizes_changed_weights():
     rt = MoKRuntime(cfg, mok.MOK_MODE_MXFP8)
     L = leaves(d)
     out1 = run_layer(rt, L)
-    codes1 = {n: rt._q[n][3] for n in rt._q}
+    out1.backward(d["grad_out"])  # also makes the backward's transposed codes
+    codes1 = {n: rt._q[n][3] for n in rt._q}  # keyed (name, transposed)
+    assert {n for n, _ in codes1} == set(NAMES) and {t for _, t in codes1} == {False, True}
     out1b = run_layer(rt, L)
+    out1b.backward(d["grad_out"])
     # unchanged weights: the cached codes are reused
     assert all(rt._q[n][3] is codes1[n] for n in codes1)
     same(out1b, out1, "repeat")
+    for t in [L["x"], L["rw"]] + [L["w"][n] for n in NAMES]:
+        t.grad = None
     # an optimizer-like in-place step on two weights: their codes are made again
     with torch.no_grad():
         L["w"]["routed_up"].mul_(0.5)
         L["w"]["shared_down"].add_(0.01)
     out2 = run_layer(rt, L)
-    assert rt._q["routed_up"][3] is not codes1["routed_up"]
-    assert rt._q["shared_down"][3] is not codes1["shared_down"]
-    assert rt._q["routed_gate"][3] is codes1["routed_gate"]
+    # the forward's codes are made again for the changed weights only
+    assert rt._q[("routed_up", False)][3] is not codes1[("routed_up", False)]
+    assert rt._q[("shared_down", False)][3] is not codes1[("shared_down", False)]
+    assert rt._q[("routed_gate", False)][3] is codes1[("routed_gate", False)]
     e = dict(d, weights={n: L["w"][n].detach() for n in NAMES})
     ref_out, ref_g = direct(cfg, e, mok.MOK_MODE_MXFP8)
     same(out2, ref_out, "after the step")
     out2.backward(d["grad_out"])
+    # the backward's transposed codes are made again for the changed weights only
+    assert rt._q[("routed_up", True)][3] is not codes1[("routed_up", True)]
+    assert rt._q[("shared_down", True)][3] is not codes1[("shared_down", True)]
+    assert rt._q[("routed_gate", True)][3] is codes1[("routed_gate", True)]
     g = grads_of(L)
-    # the gradients of this call only (the earlier outputs were never
-    # backpropagated)
+    # the gradients of this call only (the earlier ones were cleared)
     for n in ref_g:
         same(g[n], ref_g[n], "after the step " + n)
 

@@ -256,3 +256,27 @@ def test_swiglu_limit(mxfp8, limit):
                          ("d_shared_up", "d_s_up"), ("d_shared_down", "d_s_down")]:
         err, scale = assert_close_inf(np64(g[gname]), ref[rname], tol, f"limit {limit} {gname}")
         print(f"  {gname}: max err {err:.3g} of max {scale:.3g}", flush=True)
+
+
+def test_schedule_of_another_configuration_is_refused_on_the_device():
+    # Two configs with the same buffer sizes but different capacity
+    # multipliers: a schedule built by one and handed to the other's forward
+    # carries the other hash, so every launch of that forward does nothing
+    # (the output keeps its sentinel) and the workspace counts the mismatches.
+    c = MoEShape("hash", T=1000, H=256, I=128, E=4, k=2, I_s=128, seed=171, w_std=0.05)
+    d = to_dev(make_inputs(c))
+    base = dict(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=c.T, shared_intermediate=c.I_s)
+    ws_a = mok.Workspace(mok.MoKConfig(capacity_multiplier=1.0, **base))
+    ws_b = mok.Workspace(mok.MoKConfig(capacity_multiplier=0.9, **base))
+    assert ws_a.layout.total_bytes == ws_b.layout.total_bytes
+    sched = mok.build_schedule(ws_a, d["top_experts"])
+    out = torch.full_like(d["x"], 3.0)
+    mok.forward(ws_b, sched, d["x"], d["router_weights"], d["weights"], out=out)
+    timeouts, mismatches = ws_b.read_status()
+    assert timeouts == 0 and mismatches >= 3  # gate/up, down, combine
+    assert torch.all(out == 3.0)
+    assert ws_b.read_status() == (0, 0)  # the counts were reset
+    # the matching workspace runs it, and its status stays clean
+    mok.forward(ws_a, sched, d["x"], d["router_weights"], d["weights"], out=out)
+    assert ws_a.read_status() == (0, 0)
+    assert not torch.all(out == 3.0)

@@ -1,6 +1,6 @@
-"""The forward's minibatch pipeline (down GEMM of minibatch b on the compute
-units, combine of minibatch b on the mover compute units of a second stream)
-gives the same bits as the single-pass forward, for ragged minibatches,
+"""The forward's minibatch pipeline (one launch: compute workgroups run the
+down tiles minibatch by minibatch, mover workgroups combine minibatch b once
+all of its tiles are counted) gives the same bits as the single-pass forward, for ragged minibatches,
 minibatches past the batch (T below max_tokens), no shared expert, many
 experts, MXFP8 mode, and with a context kept for the backward; at 8192
 tokens the pipelined output is also compared with the oracle on every
@@ -36,6 +36,7 @@ def run_forward(c: MoEShape, d: dict, T_max: int, mode: int, minibatch: int, mov
     out = mok.forward(ws, sched, d["x"], d["router_weights"], w, mode=mode, context=ctx)
     out2 = mok.forward(ws, sched, d["x"], d["router_weights"], w, mode=mode, context=ctx)  # reuse the workspace
     torch.cuda.synchronize()
+    assert ws.read_status() == (0, 0)  # no mover wait ran out of time; the schedule matched
     return out, out2, ctx
 
 
@@ -81,9 +82,8 @@ def test_minibatch_pipeline_8192_tokens():
 
 
 def test_minibatch_pipeline_graph_replay():
-    # the fork to the workspace's second stream and the join back are captured
-    # with the forward; every replay (eager work and synchronisations between
-    # them) matches the single-pass result
+    # the pipelined forward captured in a graph: every replay (eager work and
+    # synchronisations between them) matches the single-pass result
     c = MoEShape("graph", T=900, H=256, I=256, E=6, k=3, I_s=128, seed=17, w_std=0.05)
     d = to_dev(make_inputs(c))
     ref, _, _ = run_forward(c, d, c.T, mok.MOK_MODE_BF16, 0, 0, False)
@@ -110,3 +110,4 @@ def test_minibatch_pipeline_graph_replay():
         # eager work between replays
         eager, _, _ = run_forward(c, d, c.T, mok.MOK_MODE_BF16, 256, 16, False)
         assert torch.equal(eager.view(torch.int16), ref.view(torch.int16))
+    assert ws.read_status() == (0, 0)
