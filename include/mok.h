@@ -63,7 +63,8 @@ typedef enum mok_mode {
  * ([R] "The two API layers and the schedule object", "Tuning the five
  * hyperparameters before production"). Set struct_size = sizeof(mok_config).
  *
- * Contract (MOK_ERR_UNSUPPORTED otherwise): hidden % 128 == 0;
+ * Contract (MOK_ERR_UNSUPPORTED otherwise, MOK_ERR_INVALID_ARGUMENT for
+ * negative sizes): hidden % 128 == 0;
  * intermediate % 64 == 0 and shared_intermediate % 64 == 0 (0 = no shared
  * expert); 1 <= num_experts <= 1024; 1 <= topk <= 64; expert_pad a positive
  * multiple of 32 (MXFP8 backward needs 32-row blocks inside one expert);
@@ -95,6 +96,17 @@ typedef struct mok_config {
                                    no formula): L > 0 computes h = silu(min(g, L)) * clamp(u, -L, L), and the
                                    backward passes no gradient where a clamp is active (g > L, |u| > L);
                                    0 or +inf = no limit. Negative or NaN: MOK_ERR_INVALID_ARGUMENT. */
+  int32_t macrobatch_size;      /* tokens per pass of the workspace's token ring ([R] "Tuning...": macrobatch_size, the
+                                   token ring buffer; a size at least max_tokens means the ring is used once).
+                                   0 or >= max_tokens: one pass. Otherwise mok_forward streams the batch through
+                                   scratch sized for macrobatch_size tokens, macrobatch by macrobatch, with the
+                                   whole batch's schedule (capacity and drops as in one pass): the output bits are
+                                   those of one pass. Requires forward_only = 1 (a backward contracts each expert's
+                                   weight gradient over the whole batch), num_experts >= topk and, when
+                                   minibatch_size > 0, a multiple of it (MOK_ERR_UNSUPPORTED otherwise). Each pass
+                                   adds one small kernel (its schedule) and runs without the minibatch pipeline. */
+  int32_t forward_only;         /* 1: an inference workspace, with no backward scratch (mok_backward returns
+                                   MOK_ERR_UNSUPPORTED, mok_forward takes no context); 0: training */
 } mok_config;
 
 /* Routed and shared expert weights, layouts of [A] _MoKRuntime.forward:
@@ -291,8 +303,8 @@ mok_status mok_backward(mok_workspace* ws, mok_mode mode, const void* schedule, 
  * in MXFP8 also x's codes and scales, m + m/32 with m = max_tokens * H. A
  * config that needs more returns MOK_ERR_UNSUPPORTED before anything is
  * enqueued. cfg is the config of the workspace whose
- * mok_build_schedule wrote `schedule` (minibatch pipeline fields are
- * ignored: no pipeline). Runs on the current device (`stream` must belong
+ * mok_build_schedule wrote `schedule` (minibatch pipeline and token ring
+ * fields are ignored: one pass, no pipeline; the bits are the same). Runs on the current device (`stream` must belong
  * to it). Arguments and results otherwise as mok_forward. Calls on one GPU
  * share the array: calls that overlap on one GPU race.
  */
@@ -358,6 +370,7 @@ typedef enum mok_kernel_id {
   MOK_K_BWD_DX_SUM,
   MOK_K_BWD_DW,
   MOK_K_BWD_QUANT,
+  MOK_K_SCHED_SLICE,     /* token ring: one pass's schedule */
   MOK_K_COUNT
 } mok_kernel_id;
 

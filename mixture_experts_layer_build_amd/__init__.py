@@ -26,7 +26,7 @@ from ._lib import (MOK_MODE_BF16, MOK_MODE_MXFP8, HDR_FIELDS, TILE_BMS, MokError
 __all__ = ["MoKConfig", "Workspace", "create_workspace", "get_workspace", "clear_workspace_cache",
            "build_schedule", "forward", "forward_static", "backward", "mxfp8_quantize",
            "mxfp8_quantize_transposed", "mxfp8_backward_weights", "schedule_fields",
-           "schedule_bytes", "context_bytes", "MokError", "MOK_MODE_BF16", "MOK_MODE_MXFP8", "lib"]
+           "schedule_bytes", "context_bytes", "workspace_bytes", "MokError", "MOK_MODE_BF16", "MOK_MODE_MXFP8", "lib"]
 
 
 def lib():
@@ -47,12 +47,15 @@ class MoKConfig:
     minibatch_size: int = 0
     num_mover_wgs: int = 0
     swiglu_limit: float = 0.0     # 0 = no limit (see include/mok.h)
+    macrobatch_size: int = 0      # tokens per pass of the forward's token ring; 0 = one pass
+    forward_only: int = 0         # 1 = inference workspace (no backward scratch)
 
     def c(self) -> _lib.MokConfig:
         return _lib.MokConfig(C.sizeof(_lib.MokConfig), self.hidden, self.intermediate, self.num_experts,
                               self.topk, self.shared_intermediate, self.max_tokens,
                               float(self.capacity_multiplier), self.expert_pad, self.minibatch_size,
-                              self.num_mover_wgs, float(self.swiglu_limit))
+                              self.num_mover_wgs, float(self.swiglu_limit), self.macrobatch_size,
+                              self.forward_only)
 
 
 def schedule_bytes(cfg: MoKConfig) -> int:
@@ -68,6 +71,15 @@ def context_bytes(cfg: MoKConfig, mode: int = MOK_MODE_BF16) -> int:
     n = lib().mok_context_bytes(C.byref(c), mode)
     if n == 0:
         _lib.check("mok_context_bytes", lib().mok_validate_config(C.byref(c)))
+    return n
+
+
+def workspace_bytes(cfg: MoKConfig) -> int:
+    """Device bytes a workspace of this configuration allocates."""
+    c = cfg.c()
+    n = lib().mok_workspace_bytes(C.byref(c))
+    if n == 0:
+        _lib.check("mok_workspace_bytes", lib().mok_validate_config(C.byref(c)))
     return n
 
 

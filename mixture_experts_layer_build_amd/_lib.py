@@ -30,7 +30,7 @@ EXPORTS = (
 
 HDR_FIELDS = ("T", "k", "E", "C", "P", "rows_cap", "n_mb", "minibatch", "dropped", "invalid",
               "rows_total", "hash")
-KERNEL_COUNT = 16
+KERNEL_COUNT = 17
 TILE_BMS = (32, 64, 128, 256)
 
 
@@ -48,6 +48,8 @@ class MokConfig(C.Structure):
         ("minibatch_size", C.c_int32),
         ("num_mover_wgs", C.c_int32),
         ("swiglu_limit", C.c_float),
+        ("macrobatch_size", C.c_int32),
+        ("forward_only", C.c_int32),
     ]
 
 

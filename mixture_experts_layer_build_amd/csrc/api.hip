@@ -27,9 +27,17 @@ int64_t rows_cap(const mok_config& c, int64_t T) {
   return std::min<int64_t>(T * c.topk, (int64_t)c.num_experts * C) + (int64_t)c.num_experts * (c.expert_pad - 1);
 }
 
+bool ring(const mok_config& c) { return c.macrobatch_size > 0 && (int64_t)c.macrobatch_size < c.max_tokens; }
+
+int64_t sub_offset_tokens(const mok_config& c) {
+  if (c.minibatch_size > 0) return c.minibatch_size;
+  return ring(c) ? c.macrobatch_size : 0;
+}
+
 int64_t n_minibatches(const mok_config& c, int64_t T) {
-  if (c.minibatch_size <= 0 || T <= 0) return 1;
-  return std::max<int64_t>(1, (T + c.minibatch_size - 1) / c.minibatch_size);
+  const int64_t g = sub_offset_tokens(c);
+  if (g <= 0 || T <= 0) return 1;
+  return std::max<int64_t>(1, (T + g - 1) / g);
 }
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -70,6 +78,7 @@ uint32_t config_hash(const mok_config& c) {
   mix(&c.capacity_multiplier, 4);
   mix(&c.expert_pad, 4);
   mix(&c.minibatch_size, 4);
+  mix(&c.macrobatch_size, 4);
   return h & 0x7FFFFFFFu;
 }
 
@@ -137,6 +146,7 @@ enum ScratchPart : int {
   SP_DWP,        // partial router-weight gradients
   SP_ROWS,       // transposed operands of the weight-gradient GEMMs
   SP_PIPE,       // the minibatch pipeline's counters and its status word
+  SP_PASS,       // the token ring: one macrobatch's schedule
   SP_COUNT
 };
 
@@ -194,23 +204,45 @@ Bf16DwPlan bf16_dw_plan(const mok_config& c, const Layout& L) {
   return f;
 }
 
+// One pass of the token ring: macrobatch_size tokens, every expert able to
+// take all of them (capacity 1: the whole batch's capacity decided which
+// assignments are kept), one minibatch, no pipeline.
+mok_config pass_config(const mok_config& c) {
+  mok_config q = c;
+  q.max_tokens = c.macrobatch_size;
+  q.capacity_multiplier = 1.0f;
+  q.minibatch_size = 0;
+  q.num_mover_wgs = 0;
+  q.macrobatch_size = 0;
+  q.forward_only = 1;
+  return q;
+}
+
 size_t workspace_bytes(const mok_config& c, const Layout& L, size_t* parts) {
   const int64_t Tm = c.max_tokens, H = c.hidden, E = c.num_experts, I = c.intermediate, Is = c.shared_intermediate;
   const int64_t rowsR = L.rows_cap_max;
   const int64_t n_chunks_max = std::max<int64_t>(1, 24 * 1024 / c.num_experts);
   const size_t ce = ctx_elems(c, L);
+  // the forward's token-sized scratch holds one macrobatch in ring mode
+  const bool rg = ring(c);
+  const mok_config fc = rg ? pass_config(c) : c;
+  const Layout FL = rg ? schedule_layout(fc) : L;
+  const size_t fce = ctx_elems(fc, FL);
+  const int64_t fT = fc.max_tokens;
   size_t p[SP_COUNT] = {
       (size_t)n_chunks_max * E * 4,
-      ce * 2,
-      (size_t)(rowsR + Tm) * H * 2,
-      (size_t)Tm * H + (size_t)Tm * (H / 32),
-      ce + ce / 32,
+      fce * 2,
+      (size_t)(FL.rows_cap_max + fT) * H * 2,
+      (size_t)fT * H + (size_t)fT * (H / 32),
+      fce + fce / 32,
       3 * align_up((size_t)E * I * H * 2, 256) + 3 * align_up((size_t)Is * H * 2, 256),
       3 * align_up(ce * 2, 256),
       (size_t)(rowsR + Tm) * dw_parts(c) * 4,
       bf16_dw_plan(c, L).rows,
-      (size_t)(L.n_mb_max + 64) * 4};
-  if (mxfp8_shapes_ok(c)) {
+      (size_t)(L.n_mb_max + 64) * 4,
+      rg ? FL.total : 0};
+  if (c.forward_only) p[SP_WT] = p[SP_DGUH] = p[SP_DWP] = p[SP_ROWS] = 0;  // no backward
+  if (mxfp8_shapes_ok(c) && !c.forward_only) {
     const Fp8BwdPlan f = fp8_bwd_plan(c, L);
     p[SP_WT] = std::max(p[SP_WT], f.wt);
     p[SP_DGUH] = std::max(p[SP_DGUH], f.dguh);
@@ -257,6 +289,13 @@ extern "C" mok_status mok_validate_config(const mok_config* c) {
     return MOK_ERR_INVALID_ARGUMENT;
   if (!(c->capacity_multiplier > 0.0f) || !std::isfinite(c->capacity_multiplier)) return MOK_ERR_INVALID_ARGUMENT;
   if (!(c->swiglu_limit >= 0.0f)) return MOK_ERR_INVALID_ARGUMENT;  // negative or NaN
+  if (c->macrobatch_size < 0 || (c->forward_only != 0 && c->forward_only != 1)) return MOK_ERR_INVALID_ARGUMENT;
+  // the ring: inference only; passes made of whole minibatches; E >= k, so
+  // that a pass's kept rows (at most M k, repeated ids included) fit the
+  // pass layout's min(M k, E M)
+  if (ring(*c) && (!c->forward_only || c->num_experts < c->topk ||
+                   (c->minibatch_size > 0 && c->macrobatch_size % c->minibatch_size != 0)))
+    return MOK_ERR_UNSUPPORTED;
   if (c->hidden % 128 != 0 || c->intermediate % 64 != 0 || c->shared_intermediate % 64 != 0)
     return MOK_ERR_UNSUPPORTED;
   if (c->num_experts > 1024 || c->topk > 64 || c->expert_pad % 32 != 0) return MOK_ERR_UNSUPPORTED;
@@ -343,34 +382,38 @@ extern "C" mok_status mok_workspace_create(const mok_config* c, int device, mok_
   p += parts[SP_H];
   ws->ybuf = p;
   p += parts[SP_Y];
+  // (in ring mode these four are sized for one macrobatch: pass_config)
+  const mok_config fc = ring(*c) ? pass_config(*c) : *c;
+  const size_t fce = ctx_elems(fc, ring(*c) ? schedule_layout(fc) : ws->layout);
   ws->xq = (uint8_t*)p;
-  ws->xq_scale = (uint8_t*)p + (size_t)c->max_tokens * c->hidden;
+  ws->xq_scale = (uint8_t*)p + (size_t)fc.max_tokens * c->hidden;
   p += parts[SP_XQ];
-  const size_t ce = ctx_elems(*c, ws->layout);
   ws->hq = (uint8_t*)p;
-  ws->hq_scale = (uint8_t*)p + ce;
+  ws->hq_scale = (uint8_t*)p + fce;
   p += parts[SP_HQ];
-  {
+  const size_t ce = ctx_elems(*c, ws->layout);
+  if (!c->forward_only) {
+    char* bp = p;  // the backward regions: WT, DGUH, DWP, ROWS
     const size_t wr = align_up((size_t)c->num_experts * c->intermediate * c->hidden * 2, 256);
     const size_t wsh = align_up((size_t)c->shared_intermediate * c->hidden * 2, 256);
     BwdScratch& b = ws->bwd;
-    b.wdT = (uint16_t*)p;
-    b.wgT = (uint16_t*)(p + wr);
-    b.wuT = (uint16_t*)(p + 2 * wr);
-    b.sdT = (uint16_t*)(p + 3 * wr);
-    b.sgT = (uint16_t*)(p + 3 * wr + wsh);
-    b.suT = (uint16_t*)(p + 3 * wr + 2 * wsh);
-    p += parts[SP_WT];
+    b.wdT = (uint16_t*)bp;
+    b.wgT = (uint16_t*)(bp + wr);
+    b.wuT = (uint16_t*)(bp + 2 * wr);
+    b.sdT = (uint16_t*)(bp + 3 * wr);
+    b.sgT = (uint16_t*)(bp + 3 * wr + wsh);
+    b.suT = (uint16_t*)(bp + 3 * wr + 2 * wsh);
+    bp += parts[SP_WT];
     const size_t cb = align_up(ce * 2, 256);
-    b.dg = (uint16_t*)p;
-    b.du = (uint16_t*)(p + cb);
-    b.hw = (uint16_t*)(p + 2 * cb);
-    p += parts[SP_DGUH];
-    b.dw_part = (float*)p;
-    p += parts[SP_DWP];
+    b.dg = (uint16_t*)bp;
+    b.du = (uint16_t*)(bp + cb);
+    b.hw = (uint16_t*)(bp + 2 * cb);
+    bp += parts[SP_DGUH];
+    b.dw_part = (float*)bp;
+    bp += parts[SP_DWP];
     {
       const Bf16DwPlan f = bf16_dw_plan(*c, ws->layout);
-      uint8_t* r = (uint8_t*)p;  // start of the ROWS region
+      uint8_t* r = (uint8_t*)bp;  // start of the ROWS region
       TqArrays& q = b.tq16;
       q.x = r;
       q.dy = r + f.xc;
@@ -379,7 +422,7 @@ extern "C" mok_status mok_workspace_create(const mok_config* c, int device, mok_
       q.du = r + 2 * f.xc + 2 * f.ic;
       q.kr_cap = f.kr_cap;
     }
-    if (mxfp8_shapes_ok(*c)) {
+    if (mxfp8_shapes_ok(*c) && !c->forward_only) {
       const Fp8BwdPlan f = fp8_bwd_plan(*c, ws->layout);
       uint8_t* w = (uint8_t*)b.wdT;  // start of the WT region
       uint8_t** wc[6] = {&b.wdTq, &b.wgTq, &b.wuTq, &b.sdTq, &b.sgTq, &b.suTq};
@@ -414,8 +457,9 @@ extern "C" mok_status mok_workspace_create(const mok_config* c, int device, mok_
       q.kr_cap = f.kr_cap;
       b.mxfp8_ready = true;
     }
-    p += parts[SP_ROWS];
   }
+  p += parts[SP_WT] + parts[SP_DGUH] + parts[SP_DWP] + parts[SP_ROWS];
+  ws->pass_sched = parts[SP_PASS] ? p + parts[SP_PIPE] : nullptr;
   ws->status = (int32_t*)p;  // status words first, then the counters
   ws->pipe_cnt = (int32_t*)p + 64;
   if (hipMemset(p, 0, parts[SP_PIPE]) != hipSuccess) {
@@ -482,6 +526,7 @@ extern "C" mok_status mok_forward(mok_workspace* ws, mok_mode mode, const void* 
   mok_status st = check_weights(ws->cfg, mode, weights, true);
   if (st != MOK_OK) return st;
   if (mode == MOK_MODE_MXFP8 && !mxfp8_shapes_ok(ws->cfg)) return MOK_ERR_UNSUPPORTED;
+  if (context && ws->cfg.forward_only) return MOK_ERR_UNSUPPORTED;
   if (context && context_bytes < mok_context_bytes(&ws->cfg, mode)) return MOK_ERR_BUFFER_TOO_SMALL;
   DeviceGuard g(ws->device);
   if (!g.ok) return MOK_ERR_HIP;
@@ -501,7 +546,31 @@ extern "C" mok_status mok_forward(mok_workspace* ws, mok_mode mode, const void* 
     a.h = ws->hbuf;
   }
   a.y = ws->ybuf;
-  return to_status(launch_forward(ws, schedule, a, (hipStream_t)stream));
+  const hipStream_t s = (hipStream_t)stream;
+  if (!ring(ws->cfg)) return to_status(launch_forward(ws, ws->cfg, ws->layout, schedule, a, s));
+  // Token ring: the batch goes through the scratch macrobatch by macrobatch.
+  // T is only known on the device, so every pass that max_tokens allows is
+  // enqueued; a pass past T has no tokens and its launches return at once.
+  // Pass p cuts its own schedule out of the whole batch's (capacity and drops
+  // stay the whole batch's) and runs the one-pass launches on tokens
+  // [p*M, p*M + M) through pointers offset by p*M tokens; the row sums of the
+  // combine do not depend on the pass, so the output bits are those of one
+  // pass.
+  const mok_config qc = pass_config(ws->cfg);
+  const Layout QL = schedule_layout(qc);
+  const int64_t M = ws->cfg.macrobatch_size, H = ws->cfg.hidden, k = ws->cfg.topk;
+  const int64_t passes = (ws->cfg.max_tokens + M - 1) / M;
+  for (int64_t pass = 0; pass < passes; ++pass) {
+    hipError_t e = launch_sched_slice(ws, schedule, (int)pass, ws->pass_sched, s);
+    if (e != hipSuccess) return to_status(e);
+    FwdArgs b = a;
+    b.x = (const uint16_t*)x + pass * M * H;
+    b.router_w = router_weights + pass * M * k;
+    b.out = (uint16_t*)out + pass * M * H;
+    e = launch_forward(ws, qc, QL, ws->pass_sched, b, s);
+    if (e != hipSuccess) return to_status(e);
+  }
+  return MOK_OK;
 }
 
 extern "C" mok_status mok_backward(mok_workspace* ws, mok_mode mode, const void* schedule, size_t schedule_bytes,
@@ -510,6 +579,7 @@ extern "C" mok_status mok_backward(mok_workspace* ws, mok_mode mode, const void*
                                    void* stream) {
   if (!ws || !schedule || !context || !grad_out || !x || !router_weights || !grads) return MOK_ERR_INVALID_ARGUMENT;
   if (mode != MOK_MODE_BF16 && mode != MOK_MODE_MXFP8) return MOK_ERR_INVALID_ARGUMENT;
+  if (ws->cfg.forward_only) return MOK_ERR_UNSUPPORTED;
   if (schedule_bytes < ws->layout.total) return MOK_ERR_BUFFER_TOO_SMALL;
   if (context_bytes < mok_context_bytes(&ws->cfg, mode)) return MOK_ERR_BUFFER_TOO_SMALL;
   mok_status st = check_weights(ws->cfg, mode, weights, false);
@@ -591,7 +661,7 @@ extern "C" const char* mok_kernel_name(int id) {
   static const char* names[MOK_K_COUNT] = {
       "sched_count", "sched_scan", "sched_scatter", "sched_minibatch", "quant_x",      "gate_up",
       "down",        "combine",    "bwd_transpose", "bwd_gather",      "bwd_dh",       "bwd_dw_reduce",
-      "bwd_dx_rows", "bwd_dx_sum", "bwd_dw",        "bwd_quant"};
+      "bwd_dx_rows", "bwd_dx_sum", "bwd_dw",        "bwd_quant",       "sched_slice"};
   if (id < 0 || id >= MOK_K_COUNT) return "unknown";
   return names[id];
 }

@@ -26,8 +26,7 @@
 
 namespace mok {
 
-static void fill_schedule(nt::Params& p, const mok_workspace* ws, const SchedView& v) {
-  const mok_config& c = ws->cfg;
+static void fill_schedule(nt::Params& p, const mok_config& c, const Layout& L, const SchedView& v) {
   p.hdr = v.header;
   p.offsets = v.offsets;
   p.kept = v.kept;
@@ -39,7 +38,7 @@ static void fill_schedule(nt::Params& p, const mok_workspace* ws, const SchedVie
   p.H = c.hidden;
   p.I = c.intermediate;
   p.Is = c.shared_intermediate;
-  p.rows_cap_max = ws->layout.rows_cap_max;
+  p.rows_cap_max = L.rows_cap_max;
   p.swiglu_lim = swiglu_lim(c);
   p.cfg_hash = v.hash;
   p.status = v.status;
@@ -49,23 +48,22 @@ static void fill_schedule(nt::Params& p, const mok_workspace* ws, const SchedVie
 // num_mover_wgs rounded down to a multiple of the XCD count, leaving at
 // least four XCD rounds of compute workgroups; the pipeline needs the tile
 // tables in LDS and more than one minibatch.
-int mover_units(const mok_workspace* ws) {
-  const mok_config& c = ws->cfg;
+int mover_units(const mok_workspace* ws, const mok_config& c) {
   if (c.minibatch_size <= 0 || c.num_mover_wgs <= 0 || c.num_experts > nt::kMaxLdsE) return 0;
   if ((int64_t)c.minibatch_size >= c.max_tokens || ws->pipe_cnt == nullptr) return 0;
   const int m = c.num_mover_wgs / nt::kNumXcd * nt::kNumXcd;
   return std::min(m, ws->num_cus - 4 * nt::kNumXcd);
 }
 
-hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a, hipStream_t s) {
-  const mok_config& c = ws->cfg;
-  SchedView v = sched_view(const_cast<void*>(sched), ws->layout);
+hipError_t launch_forward(mok_workspace* ws, const mok_config& c, const Layout& L, const void* sched,
+                          const FwdArgs& a, hipStream_t s) {
+  SchedView v = sched_view(const_cast<void*>(sched), L);
   v.hash = (int)config_hash(c);
   v.status = ws->status;
   const int grid = ws->num_cus;  // one 512-thread workgroup per compute unit
-  const size_t ce = ctx_elems(c, ws->layout);
+  const size_t ce = ctx_elems(c, L);
   nt::Params p{};
-  fill_schedule(p, ws, v);
+  fill_schedule(p, c, L, v);
   p.router_w = a.router_w;
   p.ctx_g = a.ctx_g;
   p.ctx_u = a.ctx_u;
@@ -97,9 +95,9 @@ hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a
   p.b1 = a.w->routed_up;
   p.sb0 = a.w->shared_gate;
   p.sb1 = a.w->shared_up;
-  if (mover_units(ws) > 0) {  // the pipeline's tile counters start at zero in every forward
+  if (mover_units(ws, c) > 0) {  // the pipeline's tile counters start at zero in every forward
     p.mb_done = ws->pipe_cnt;
-    p.n_done = (int)ws->layout.n_mb_max;
+    p.n_done = (int)L.n_mb_max;
   }
   {
     LaunchTimer tm(ws, MOK_K_GATE_UP, s);
@@ -111,7 +109,7 @@ hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a
   }
   // down
   nt::Params d{};
-  fill_schedule(d, ws, v);
+  fill_schedule(d, c, L, v);
   d.router_w = a.router_w;
   d.a_row = a.mxfp8 ? (const void*)hq : a.h;
   d.a_row_scale = hq_scale;
@@ -121,9 +119,9 @@ hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a
   d.sb0s = a.w->shared_down_scale;
   d.out = a.y;
   const uint16_t* y = (const uint16_t*)a.y;
-  const uint16_t* ys = c.shared_intermediate > 0 ? y + ws->layout.rows_cap_max * c.hidden : nullptr;
+  const uint16_t* ys = c.shared_intermediate > 0 ? y + L.rows_cap_max * c.hidden : nullptr;
   const int cgrid = (int)std::min<int64_t>(c.max_tokens, (int64_t)ws->num_cus * 8);
-  const int movers = mover_units(ws);
+  const int movers = mover_units(ws, c);
   if (movers == 0) {
     {
       LaunchTimer tm(ws, MOK_K_DOWN, s);

@@ -44,6 +44,10 @@ struct Layout {
 int64_t capacity(int64_t T, float mult);
 int64_t rows_cap(const mok_config& c, int64_t T);
 int64_t n_minibatches(const mok_config& c, int64_t T);
+// The forward streams the batch through a token ring (0 < macrobatch_size < max_tokens).
+bool ring(const mok_config& c);
+// Tokens per schedule sub-offset step: minibatch_size, else the macrobatch in ring mode (0 = none).
+int64_t sub_offset_tokens(const mok_config& c);
 Layout schedule_layout(const mok_config& c);
 uint32_t config_hash(const mok_config& c);
 
@@ -148,6 +152,8 @@ struct mok_workspace {
   // launches that found a schedule of another configuration
   int32_t* pipe_cnt = nullptr;     // [n_mb_max]
   int32_t* status = nullptr;       // [2]
+  // token ring (0 < macrobatch_size < max_tokens): one macrobatch's schedule
+  void* pass_sched = nullptr;
   // timing
   uint32_t timing_mask = 0;  // bit k: time launches of kernel id k
   std::vector<mok::TimedLaunch> launches;
@@ -170,6 +176,10 @@ struct LaunchTimer {
 // Launchers (each returns hipSuccess or the launch error)
 // ---------------------------------------------------------------------------
 hipError_t launch_schedule(mok_workspace* ws, const int64_t* top, int64_t T, void* sched, hipStream_t s);
+// One macrobatch of the token ring: its schedule, in the pass layout
+// (pass_config), cut out of the whole batch's.
+mok_config pass_config(const mok_config& c);
+hipError_t launch_sched_slice(mok_workspace* ws, const void* sched, int pass, void* pass_sched, hipStream_t s);
 
 hipError_t launch_quantize(const void* src, int src_is_fp32, int64_t rows, int64_t cols, int64_t ld_src, int axis,
                            uint8_t* dst, int64_t ld_dst, uint8_t* dst_scale, hipStream_t s);
@@ -185,7 +195,10 @@ struct FwdArgs {
   void* y;                    // bf16 [(rows_cap_max + T_max), H]
   int mxfp8;
 };
-hipError_t launch_forward(mok_workspace* ws, const void* sched, const FwdArgs& a, hipStream_t s);
+// One forward over the schedule `sched` (layout L) of configuration c: the
+// workspace's own, or one pass of its token ring.
+hipError_t launch_forward(mok_workspace* ws, const mok_config& c, const Layout& L, const void* sched,
+                          const FwdArgs& a, hipStream_t s);
 
 // Transposed MXFP8 quantization of bf16 matrices [B][R][C] -> [B][C][R]
 // codes with [B][C][R/32] scales (R % 128 == 0, C % 64 == 0).

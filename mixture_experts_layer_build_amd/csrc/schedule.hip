@@ -322,7 +322,170 @@ __global__ void __launch_bounds__(256) sched_minibatch(SchedParams p) {
   p.v.mb_offsets[idx] = lo;
 }
 
+// One pass of the token ring: the schedule of the tokens [t0, t0 + T_p),
+// t0 = pass * M, cut out of the whole batch's schedule, with its rows
+// packed. Expert e keeps the rows of those tokens that the whole batch kept,
+// rows [lo_e, hi_e) of its segment (the sub-offsets at the pass's
+// boundaries), in the same order; they become rows [offq_e, offq_e + n_e)
+// of the pass, segments padded to P. Assignment ids and slot indices are
+// made relative to t0, so that the pass runs with x, the router weights and
+// the output offset by t0 tokens. Every workgroup derives the per-expert
+// tables itself; workgroup 0 writes them; all share the rows and slots.
+struct SliceParams {
+  SchedView g;        // the whole batch's schedule
+  SchedView q;        // the pass's
+  int E, k, P, M;
+  int steps;          // sub-offset steps per pass
+  int pass;
+  int rows_cap_q;     // rows of the pass layout
+  int hash_q;         // the pass configuration's hash
+  int shared;         // 1 with a shared expert
+};
+
+__global__ void __launch_bounds__(kThreads) sched_slice(SliceParams p) {
+  __shared__ int32_t lo[kMaxE], kp[kMaxE], offq[kMaxE + 1], goff[kMaxE + 1];
+  __shared__ int32_t s_wtot[1 + kNumTileBMs][kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = p.E, k = p.k;
+  if (!sched_matches(p.g.header, p.g.hash, p.g.status)) {
+    // a foreign schedule: the pass's header gets a hash no launch expects,
+    // so that the pass's launches return too
+    if (blockIdx.x == 0 && tid == 0) p.q.header[HDR_HASH] = p.hash_q ^ 0x40000000;
+    return;
+  }
+  const int T = p.g.header[HDR_T], n_mb = p.g.header[HDR_NMB];
+  const int t0 = min(T, p.pass * p.M);
+  const int Tp = min(p.M, T - t0);
+  const int i0 = min(p.pass * p.steps, n_mb), i1 = min((p.pass + 1) * p.steps, n_mb);
+  int n = 0;
+  if (tid < E) {
+    const int l = p.g.mb_offsets[i0 * E + tid];
+    n = p.g.mb_offsets[i1 * E + tid] - l;
+    lo[tid] = l;
+    kp[tid] = n;
+  }
+  if (tid <= E) goff[tid] = p.g.offsets[tid];
+  // exclusive scans over experts: padded rows, and the 32/64/128/256-row tiles
+  const int padded = (n + p.P - 1) / p.P * p.P;
+  int val[1 + kNumTileBMs], incl[1 + kNumTileBMs];
+#pragma unroll
+  for (int t = 0; t < 1 + kNumTileBMs; ++t) {
+    val[t] = t == 0 ? padded : (n + kTileBM[t - 1] - 1) / kTileBM[t - 1];
+    incl[t] = wave_inclusive_scan(val[t], lane);
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int t = 0; t < 1 + kNumTileBMs; ++t) s_wtot[t][wave] = incl[t];
+  }
+  __syncthreads();
+  int tot[1 + kNumTileBMs];
+#pragma unroll
+  for (int t = 0; t < 1 + kNumTileBMs; ++t) {
+    int before = 0, all = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      before += w < wave ? s_wtot[t][w] : 0;
+      all += s_wtot[t][w];
+    }
+    tot[t] = all;
+    const int excl = before + incl[t] - val[t];
+    if (tid < E) {
+      if (t == 0) offq[tid] = excl;
+      else if (blockIdx.x == 0) p.q.tiles[(t - 1) * (E + 2) + tid] = excl;
+    }
+  }
+  if (tid == 0) offq[E] = tot[0];
+  __syncthreads();
+  const int rows_total = tot[0];
+  if (blockIdx.x == 0) {
+    if (tid < E) {
+      p.q.counts[tid] = kp[tid];
+      p.q.kept[tid] = kp[tid];
+      p.q.offsets[tid] = offq[tid];
+      p.q.mb_offsets[tid] = offq[tid];
+      p.q.mb_offsets[E + tid] = offq[tid] + kp[tid];
+    }
+    if (tid == 0) {
+      p.q.offsets[E] = rows_total;
+#pragma unroll
+      for (int t = 0; t < kNumTileBMs; ++t) {
+        const int bm = kTileBM[t];
+        p.q.tiles[t * (E + 2) + E] = tot[t + 1];
+        p.q.tiles[t * (E + 2) + E + 1] = tot[t + 1] + (p.shared ? (Tp + bm - 1) / bm : 0);
+      }
+      int32_t* hd = p.q.header;
+      hd[HDR_T] = Tp;
+      hd[HDR_K] = k;
+      hd[HDR_E] = E;
+      hd[HDR_C] = p.M;
+      hd[HDR_P] = p.P;
+      hd[HDR_ROWS_CAP] = min(Tp * k, E * Tp) + E * (p.P - 1);
+      hd[HDR_NMB] = 1;
+      hd[HDR_MB] = Tp;
+      hd[HDR_DROPPED] = 0;
+      hd[HDR_INVALID] = 0;
+      hd[HDR_ROWS_TOTAL] = rows_total;
+      hd[HDR_HASH] = p.hash_q;
+      for (int i = HDR_HASH + 1; i < HDR_INTS; ++i) hd[i] = 0;
+    }
+  }
+  // largest e with a[e] <= v (segments that start at the same row: the last,
+  // the only one that can hold it)
+  auto search = [&](const int32_t* a, int v) {
+    int l = 0, h = E;
+    while (h - l > 1) {
+      const int mid = (l + h) >> 1;
+      if (a[mid] <= v) l = mid; else h = mid;
+    }
+    return l;
+  };
+  const int stride = gridDim.x * kThreads;
+  for (int r = blockIdx.x * kThreads + tid; r < p.rows_cap_q; r += stride) {
+    int src = -1;
+    if (r < rows_total) {
+      const int e = search(offq, r);
+      const int i = r - offq[e];
+      if (i < kp[e]) src = p.g.row_src[lo[e] + i] - t0 * k;
+    }
+    p.q.row_src[r] = src;
+  }
+  for (int a = blockIdx.x * kThreads + tid; a < Tp * k; a += stride) {
+    const int r = p.g.slot_row[(int64_t)t0 * k + a];
+    int s = -1;
+    if (r >= 0) {
+      const int e = search(goff, r);
+      s = offq[e] + (r - lo[e]);
+    }
+    p.q.slot_row[a] = s;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_sched_slice(mok_workspace* ws, const void* sched, int pass, void* pass_sched, hipStream_t s) {
+  const mok_config& c = ws->cfg;
+  const mok_config qc = pass_config(c);
+  const Layout QL = schedule_layout(qc);
+  SliceParams p;
+  p.g = sched_view(const_cast<void*>(sched), ws->layout);
+  p.g.hash = (int)config_hash(c);
+  p.g.status = ws->status;
+  p.q = sched_view(pass_sched, QL);
+  p.E = c.num_experts;
+  p.k = c.topk;
+  p.P = c.expert_pad;
+  p.M = c.macrobatch_size;
+  p.steps = (int)(c.macrobatch_size / sub_offset_tokens(c));
+  p.pass = pass;
+  p.rows_cap_q = (int)QL.rows_cap_max;
+  p.hash_q = (int)config_hash(qc);
+  p.shared = c.shared_intermediate > 0;
+  if (p.E > kMaxE) return hipErrorInvalidValue;
+  const int64_t work = std::max<int64_t>(QL.rows_cap_max, (int64_t)c.macrobatch_size * c.topk);
+  const int grid = (int)std::min<int64_t>((work + kThreads - 1) / kThreads, 256);
+  LaunchTimer t(ws, MOK_K_SCHED_SLICE, s);
+  sched_slice<<<grid, kThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
 
 hipError_t launch_schedule(mok_workspace* ws, const int64_t* top, int64_t T, void* sched, hipStream_t s) {
   const mok_config& c = ws->cfg;
@@ -336,7 +499,7 @@ hipError_t launch_schedule(mok_workspace* ws, const int64_t* top, int64_t T, voi
   p.P = c.expert_pad;
   p.rows_cap = (int)rows_cap(c, T);
   p.n_mb = (int)n_minibatches(c, T);
-  p.mb = c.minibatch_size > 0 ? c.minibatch_size : (int)T;
+  p.mb = sub_offset_tokens(c) > 0 ? (int)sub_offset_tokens(c) : (int)T;
   p.hash = (int)config_hash(c);
   p.shared_rows = c.shared_intermediate > 0 ? (int)T : 0;
   p.v = sched_view(sched, ws->layout);

@@ -110,6 +110,6 @@ extern "C" mok_status mok_forward_static(const mok_config* cfg, mok_mode mode, c
   a.mxfp8 = mx;
   a.h = ws.hbuf;
   a.y = ws.ybuf;
-  const hipError_t e = launch_forward(&ws, schedule, a, (hipStream_t)stream);
+  const hipError_t e = launch_forward(&ws, ws.cfg, ws.layout, schedule, a, (hipStream_t)stream);
   return e == hipSuccess ? MOK_OK : MOK_ERR_HIP;
 }

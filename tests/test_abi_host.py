@@ -95,6 +95,34 @@ def test_minibatch_layout():
     assert L.row_src - L.mb_offsets >= 4 * 5 * 128
 
 
+def test_token_ring_contract_and_scratch():
+    # the ring is for inference workspaces, in whole minibatches, with E >= k
+    assert status(cfg(macrobatch_size=2048, forward_only=1)) == _lib.MOK_OK
+    assert status(cfg(macrobatch_size=2048)) == _lib.MOK_ERR_UNSUPPORTED
+    assert status(cfg(macrobatch_size=2048, forward_only=1, minibatch_size=1024)) == _lib.MOK_OK
+    assert status(cfg(macrobatch_size=2048, forward_only=1, minibatch_size=1536)) == _lib.MOK_ERR_UNSUPPORTED
+    assert status(cfg(macrobatch_size=64, forward_only=1, num_experts=4, topk=8)) == _lib.MOK_ERR_UNSUPPORTED
+    assert status(cfg(macrobatch_size=-1, forward_only=1)) == _lib.MOK_ERR_INVALID_ARGUMENT
+    assert status(cfg(forward_only=2)) == _lib.MOK_ERR_INVALID_ARGUMENT
+    # a size of at least max_tokens is one pass, also for training workspaces
+    assert status(cfg(macrobatch_size=8192)) == _lib.MOK_OK
+    assert status(cfg(macrobatch_size=100000)) == _lib.MOK_OK
+    # the schedule's sub-offsets fall on the macrobatch boundaries
+    assert mok.schedule_layout(cfg(macrobatch_size=3000, forward_only=1)).n_mb_max == 3
+    assert mok.schedule_layout(cfg(macrobatch_size=2048, forward_only=1, minibatch_size=512)).n_mb_max == 16
+    # scratch: an inference workspace drops the backward's regions, and the
+    # ring sizes the token-proportional forward scratch for one macrobatch
+    big = dict(hidden=7168, intermediate=2048, num_experts=32, topk=8, max_tokens=65536, shared_intermediate=2048)
+    train = mok.workspace_bytes(cfg(**big))
+    infer = mok.workspace_bytes(cfg(forward_only=1, **big))
+    ring = mok.workspace_bytes(cfg(forward_only=1, macrobatch_size=8192, **big))
+    ring_small = mok.workspace_bytes(cfg(forward_only=1, macrobatch_size=2048, **big))
+    assert ring_small < ring < infer / 4 < train / 4
+    # h + y + quantized x/h of one 8192-token pass, plus the whole batch's
+    # schedule-sized pieces: about an eighth of the one-pass inference scratch
+    assert ring < infer * 0.15
+
+
 def test_invalid_configs_report_zero_sizes_and_raise():
     with pytest.raises(mok.MokError):
         mok.schedule_bytes(cfg(hidden=100))
