@@ -104,11 +104,26 @@ def cpu_baseline(c: MoEShape, inp: dict, mult: float, chunk_tokens: int, min_sec
     schedule), taken in order until at least `min_seconds` of CPU work."""
     from oracle import moe as omoe
     from workloads import bf16_bits_to_f32
+    np.ones((64, 64)) @ np.ones((64, 64))  # loads the BLAS library, so that it is listed below
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        threads = max([p.get("num_threads", 1) for p in libs] or [os.cpu_count() or 1])
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')} ({libs[0].get('architecture')}, " \
+                   f"{libs[0].get('threading_layer')})"
     except Exception:
         threads = os.cpu_count() or 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     n = max(1, min(chunk_tokens, c.T))
     f = lambda a: None if a is None else bf16_bits_to_f32(a).astype(np.float64)  # noqa: E731
     w = [f(inp["w_gate"]), f(inp["w_up"]), f(inp["w_down"]), f(inp["s_gate"]), f(inp["s_up"]), f(inp["s_down"])]
@@ -138,6 +153,7 @@ def cpu_baseline(c: MoEShape, inp: dict, mult: float, chunk_tokens: int, min_sec
             break
     dt = time.perf_counter() - t0
     return {"value": round(done / dt, 1), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model, "host_cpus": os.cpu_count(), "blas": blas,
             "sample": f"{chunks} consecutive chunks of {n} tokens ({done} tokens) of the same seeded "
                       f"{c.T}-token batch, each chunk scheduled on its own, float64 NumPy oracle "
                       f"({'fwd' if c.passes == 'fwd' else 'fwd+bwd'}, {c.mode}), {dt:.1f} s"}
