@@ -46,7 +46,8 @@ GATE_UP_SOURCES = ("gemm_nt.h", "gemm_common.h", "device_common.h", "mok_interna
 # (workload, sha256 of GATE_UP_SOURCES): once the kernel changes, the figure
 # no longer applies and traffic is reported as null.
 MEASURED_TRAFFIC = {
-    ("t8192_bf16_fwd", "302bb85f0683ff6f"): 793606 * 1024 * 2.000 + 110592 * 1024 * 1.000,
+    ("t8192_bf16_fwd", "d4b32ae8774abfcd"): 794672 * 1024 * 2.000 + 110592 * 1024 * 1.000,
+    ("t8192_mxfp8_fwd", "d4b32ae8774abfcd"): 435854 * 1024 * 2.000 + 57302 * 1024 * 1.000,
 }
 
 
@@ -74,6 +75,12 @@ def parse():
     ap.add_argument("--autograd", action="store_true",
                     help="run the step through the torch.autograd layer (forward, then backward from "
                          "grad_out for the training workloads) instead of the direct library calls")
+    ap.add_argument("--macrobatch", type=int, default=0,
+                    help="macrobatch_size of the forward's token ring (inference workloads; 0 = one pass)")
+    ap.add_argument("--dense-calibration", action="store_true",
+                    help="instead of the layer: time torch.matmul (hipBLASLt) on the dense GEMMs of the "
+                         "workload's shape (all routed rows and the shared rows as one matrix), a "
+                         "library ceiling for the grouped GEMMs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run one plain device-to-device copy of MIB MiB (a "
                          "known-size reference for the HBM byte counters of a profiler run)")
@@ -171,8 +178,55 @@ def copy_calibration(mib: int) -> None:
     torch.cuda.synchronize()
 
 
+def dense_calibration(c: MoEShape, steps: int, warmup: int) -> dict:
+    """torch.matmul on the dense equivalents of the grouped GEMMs: the
+    T*k routed rows and the T shared rows stacked into one M dimension
+    (M = T*(k+1) when I_s == I). gate/up: [M, H] x [H, 2I]; down: [M, I] x
+    [I, H]. Operands are N(0,1) bf16 (the chip's clock depends on the
+    data); in FP8 the same shapes through torch._scaled_mm with E4M3
+    operands and per-tensor scales, when this torch supports it."""
+    import torch
+    if c.I_s not in (0, c.I):
+        raise SystemExit("dense calibration needs I_s == I or no shared expert")
+    M = c.T * c.k + (c.T if c.I_s else 0)
+    g = torch.Generator(device="cuda").manual_seed(7)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    res = {}
+    for name, (K, N) in {"gate_up": (c.H, 2 * c.I), "down": (c.I, c.H)}.items():
+        A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        B = torch.randn(K, N, device="cuda", generator=g).to(torch.bfloat16)
+        C_ = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+        ms = timed(lambda: torch.matmul(A, B, out=C_))
+        fl = 2.0 * M * K * N
+        res[name + "_bf16"] = {"M": M, "K": K, "N": N, "ms": round(ms, 5),
+                               "tflops": round(fl / ms / 1e9, 1), "frac": round(fl / ms / 1e9 / 2500.0, 4)}
+        try:
+            A8 = A.to(torch.float8_e4m3fn)
+            B8 = B.t().contiguous().to(torch.float8_e4m3fn).t()  # column-major, as _scaled_mm wants
+            one = torch.ones((), device="cuda")
+            ms8 = timed(lambda: torch._scaled_mm(A8, B8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16))
+            res[name + "_fp8"] = {"ms": round(ms8, 5), "tflops": round(fl / ms8 / 1e9, 1),
+                                  "frac": round(fl / ms8 / 1e9 / 5000.0, 4)}
+        except Exception as e:  # not every torch build has an FP8 GEMM for this GPU
+            res[name + "_fp8"] = {"error": f"{type(e).__name__}: {str(e)[:200]}"}
+        del A, B, C_
+    return {"dense_calibration": c.name, "steps": steps, "warmup": warmup, **res}
+
+
 def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sample_tokens: int,
-        minibatch: int = 0, movers: int = 0, use_autograd: bool = False) -> dict:
+        minibatch: int = 0, movers: int = 0, use_autograd: bool = False, macrobatch: int = 0) -> dict:
     import torch
     import mixture_experts_layer_build_amd as mok
 
@@ -180,7 +234,8 @@ def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sampl
     d = to_device(inp, torch)
     cfg = mok.MoKConfig(hidden=c.H, intermediate=c.I, num_experts=c.E, topk=c.k, max_tokens=c.T,
                         shared_intermediate=c.I_s, capacity_multiplier=mult, expert_pad=c.expert_pad,
-                        minibatch_size=minibatch, num_mover_wgs=movers)
+                        minibatch_size=minibatch, num_mover_wgs=movers, macrobatch_size=macrobatch,
+                        forward_only=1 if macrobatch else 0)
     # the autograd layer takes its workspace from the per-config cache; the
     # direct calls use one of their own
     ws = mok.get_workspace(cfg) if use_autograd else mok.Workspace(cfg)
@@ -279,7 +334,7 @@ def run(c: MoEShape, steps: int, warmup: int, mult: float, want_cpu: bool, sampl
         "config": {"workload": c.name, "tokens": c.T, "hidden": c.H, "intermediate": c.I, "experts": c.E,
                    "topk": c.k, "shared_intermediate": c.I_s, "capacity_multiplier": mult,
                    "expert_pad": c.expert_pad, "passes": c.passes, "kept_assignments": R_kept,
-                   "minibatch_size": minibatch, "num_mover_wgs": movers,
+                   "minibatch_size": minibatch, "num_mover_wgs": movers, "macrobatch_size": macrobatch,
                    "api": "torch.autograd layer" if use_autograd else "direct library calls",
                    "parallelism": "single GPU (one GPU's share; no all-to-all)"},
         "tflops": round(flops / (dt / steps) / 1e12, 2),
@@ -305,12 +360,15 @@ def main():
         print(json.dumps({"error": "this library runs on one GPU only: the all-to-all between GPUs is left out, "
                                    "so --gpus N with N > 1 is not supported"}))
         sys.exit(2)
+    if a.dense_calibration:
+        print(json.dumps(dense_calibration(CONFIGS[a.workload], a.steps, a.warmup)), flush=True)
+        return
     names = [n for n in CONFIGS] if a.all else [a.workload]
     for n in names:
         c = CONFIGS[n]
         mult = c.capacity_multiplier if a.mult is None else a.mult
         line = run(c, a.steps, a.warmup, mult, not a.no_cpu_baseline and not a.all, a.cpu_sample_tokens,
-                   a.minibatch, a.movers, a.autograd)
+                   a.minibatch, a.movers, a.autograd, a.macrobatch)
         print(json.dumps(line), flush=True)
     if a.copy_calibration:
         copy_calibration(a.copy_calibration)
