@@ -109,8 +109,9 @@ __global__ void __launch_bounds__(256) quant_axis1_f32(const float* __restrict__
 }
 
 // axis = 0: one lane owns 16 bytes of columns (8 bf16 or 4 fp32) of one
-// 32-row block; it reads the 32 rows, reduces each column's maximum and
-// writes the 32 code rows and the block's scale bytes.
+// 32-row block; it reads the 32 rows to reduce each column's maximum, then
+// reads them again (from cache) to write the 32 code rows, and writes the
+// block's scale bytes (two passes: holding all 32 rows spilled).
 template <typename T>
 __global__ void __launch_bounds__(256) quant_axis0(const T* __restrict__ src, int64_t rows, int64_t cols,
                                                    int64_t ld_src, uint8_t* __restrict__ dst, int64_t ld_dst,
@@ -121,36 +122,29 @@ __global__ void __launch_bounds__(256) quant_axis0(const T* __restrict__ src, in
   if (g >= (rows >> 5) * ngrp) return;
   const int64_t rb = g / ngrp;
   const int64_t col = (g - rb * ngrp) * CW;
-  uint4 raw[32];
   const T* p = src + rb * 32 * ld_src + col;
-#pragma unroll
-  for (int r = 0; r < 32; ++r) raw[r] = *reinterpret_cast<const uint4*>(p + r * ld_src);
-  float vals[CW];
+  auto bits_of = [](const uint4& v, int c) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    return sizeof(T) == 2 ? ((c & 1) ? (w[c >> 1] & 0xFFFF0000u) : (w[c >> 1] << 16)) : w[c];
+  };
   uint32_t amax[CW];
 #pragma unroll
   for (int c = 0; c < CW; ++c) amax[c] = 0;
-#pragma unroll
+#pragma unroll 8
   for (int r = 0; r < 32; ++r) {
-    const uint32_t w[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+    const uint4 v = *reinterpret_cast<const uint4*>(p + r * ld_src);
 #pragma unroll
-    for (int c = 0; c < CW; ++c) {
-      uint32_t bits = sizeof(T) == 2 ? ((c & 1) ? (w[c >> 1] & 0xFFFF0000u) : (w[c >> 1] << 16)) : w[c];
-      amax[c] = max(amax[c], bits & 0x7FFFFFFFu);
-    }
+    for (int c = 0; c < CW; ++c) amax[c] = max(amax[c], bits_of(v, c) & 0x7FFFFFFFu);
   }
   int X[CW];
 #pragma unroll
   for (int c = 0; c < CW; ++c) X[c] = mx_block_exponent(amax[c]);
-#pragma unroll
+#pragma unroll 8
   for (int r = 0; r < 32; ++r) {
-    const uint32_t w[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+    const uint4 v = *reinterpret_cast<const uint4*>(p + r * ld_src);
     uint32_t code[2] = {0, 0};
 #pragma unroll
-    for (int c = 0; c < CW; ++c) {
-      uint32_t bits = sizeof(T) == 2 ? ((c & 1) ? (w[c >> 1] & 0xFFFF0000u) : (w[c >> 1] << 16)) : w[c];
-      vals[c] = u2f(bits);
-      code[c >> 2] |= e4m3_encode_scaled(vals[c], X[c]) << ((c & 3) * 8);
-    }
+    for (int c = 0; c < CW; ++c) code[c >> 2] |= e4m3_encode_scaled(u2f(bits_of(v, c)), X[c]) << ((c & 3) * 8);
     uint8_t* q = dst + (rb * 32 + r) * ld_dst + col;
     if (CW == 8)
       *reinterpret_cast<uint2*>(q) = make_uint2(code[0], code[1]);
