@@ -181,7 +181,7 @@ Fp8BwdPlan fp8_bwd_plan(const mok_config& c, const Layout& L) {
   f.ic = align_up((size_t)I * f.kr_cap + (size_t)Is * f.ks_cap, 256);
   f.is = align_up(((size_t)I * f.kr_cap + (size_t)Is * f.ks_cap) / 32, 256);
   f.wt = 3 * (f.w_c + f.w_s) + 3 * (f.sw_c + f.sw_s);
-  f.dguh = 2 * align_up(ce * 4, 256) + align_up(ce, 256) + align_up(ce / 32, 256);
+  f.dguh = align_up(ce, 256) + align_up(ce / 32, 256);
   f.rows = 2 * (f.xc + f.xs) + 3 * (f.ic + f.is);
   return f;
 }
@@ -433,10 +433,8 @@ extern "C" mok_status mok_workspace_create(const mok_config* c, int device, mok_
         *wsc[i] = w;
         w += i < 3 ? f.w_s : f.sw_s;
       }
-      // DGUH region: fp32 dG, fp32 dU, then dU's MXFP8 codes and scales
-      b.dg32 = (float*)b.dg;
-      b.du32 = (float*)((char*)b.dg + align_up(ce * 4, 256));
-      b.duq = (uint8_t*)b.dg + 2 * align_up(ce * 4, 256);
+      // DGUH region: dU's MXFP8 codes and scales along I
+      b.duq = (uint8_t*)b.dg;
       b.duq_scale = b.duq + align_up(ce, 256);
       uint8_t* r = b.tq16.x;  // start of the ROWS region
       TqArrays& q = b.tq;

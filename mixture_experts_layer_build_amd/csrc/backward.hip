@@ -183,8 +183,14 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
     p.u_in = a.ctx_u;
     p.hq_in = (const uint8_t*)a.ctx_h;
     p.hq_scale_in = (const uint8_t*)a.ctx_h + ce;
-    p.dg_out32 = b.dg32;
-    p.du_out32 = b.du32;
+    // dG and dU quantized in the epilogue: along I for dA (dG into the
+    // workspace's hq buffer, dU into duq), along rows for the weight gradients
+    p.rq_g = ws->hq;
+    p.rq_gs = ws->hq_scale;
+    p.rq_u = b.duq;
+    p.rq_us = b.duq_scale;
+    p.tq = b.tq;
+    p.tiles128 = v.tiles + tile_bm_index(128) * (E + 2);
     p.dw_part = b.dw_part;
     p.dw_parts = dw_parts(c);
     LaunchTimer tm(ws, MOK_K_BWD_DH, s);
@@ -199,16 +205,6 @@ static hipError_t launch_backward_mxfp8(mok_workspace* ws, const void* sched, co
     reduce_dw<<<rgrid, 256, 0, s>>>(v.header, v.hash, v.status, v.slot_row, b.dw_part, dw_parts(c), n_used, k,
                                     g->d_router_weights);
     MOK_HIP_TRY(hipGetLastError());
-  }
-  {
-    // dG and dU (fp32) in 32-row blocks for the weight gradients, and in the
-    // same pass along I (their kept rows, row-major) for dA
-    LaunchTimer tm(ws, MOK_K_BWD_QUANT, s);
-    const TqArrays& q = b.tq;
-    MOK_HIP_TRY(launch_quantize_t_rows(4, v, b.dg32, nullptr, nullptr, nullptr, E, k, I, Is, rcm, q.kr_cap, q.dg,
-                                       q.dgs, qgrid, s, false, ws->hq, ws->hq_scale));
-    MOK_HIP_TRY(launch_quantize_t_rows(4, v, b.du32, nullptr, nullptr, nullptr, E, k, I, Is, rcm, q.kr_cap, q.du,
-                                       q.dus, qgrid, s, false, b.duq, b.duq_scale));
   }
   {
     nt::Params p{};

@@ -110,8 +110,15 @@ struct Params {
   const uint16_t* h_in;
   uint16_t* dg_out;
   uint16_t* du_out;
-  float* dg_out32;              // MXFP8: dG, dU in fp32 (quantized from these afterwards)
-  float* du_out32;
+  // MXFP8: dG and dU quantized in the epilogue, along I (row-major codes
+  // and scales, the layout of the forward's h codes: the dA GEMM's A
+  // operands) and along rows (p.tq.dg/dgs, p.tq.du/dus: the weight
+  // gradients' operands, [cols, K_e] per expert at 128 * tiles128[e] * I)
+  uint8_t* rq_g;
+  uint8_t* rq_gs;
+  uint8_t* rq_u;
+  uint8_t* rq_us;
+  const int32_t* tiles128;      // prefix sums of 128-row tiles per expert, [E] routed, [E+1] with shared
   uint16_t* hw_out;
   const uint8_t* hq_in;         // MXFP8: h codes and scales saved by the forward (instead of h_in)
   const uint8_t* hq_scale_in;
@@ -137,8 +144,13 @@ struct Tile {
   int kofs;   // BWD_DW: the expert's K offset in the transposed arrays
 };
 
+// LDS past the stages that the MXFP8 dh_hat epilogue stages through with
+// them (two padded 32 x 64 fp32 buffers per wave)
+constexpr int kEpiExtra = NTHR / 64 * 2 * 32 * (64 + 4) * 4 - NSTAGE * (A_BYTES + B_BYTES);
+
 struct alignas(16) Lds {
   uint8_t stage[NSTAGE][A_BYTES + B_BYTES];
+  uint8_t epi_extra[kEpiExtra];  // (contiguous with the stages)
   uint8_t scale[NSTAGE][SA_BYTES + SB_BYTES];  // used in MXFP8 mode
   int32_t tiles[kMaxLdsE + 2];
   int32_t fullp[kMaxLdsE + 2];  // exclusive prefix over experts (shared last) of full M tiles
@@ -1150,9 +1162,6 @@ grouped_gemm_nt(Params p) {
       //   dw partial += dh_hat * h,   dh = w * dh_hat,
       //   dG = dh * u * s * (1 + g * (1 - s)) (s = sigmoid(g)),  dU = dh * silu(g),
       //   hw = w * h (the down-weight gradient's right operand; BF16 only).
-      // MXFP8: h is the forward's E4M3 h (codes and block scales); dG and dU
-      // are stored in fp32, so their two quantizations (along I for dA, along
-      // rows for the weight gradients) start from the accumulator values.
       // The wave's 128 x 64 tile is staged through LDS one 32-row block at a
       // time (fp32), so that each lane then takes 8 consecutive columns of
       // one row: the saved G, U, h reads and the dG, dU, hw writes of a wave
@@ -1162,8 +1171,7 @@ grouped_gemm_nt(Params p) {
       const int64_t sh = shared ? p.rows_cap_max * p.I : 0;
       const int rr = lane >> 3, cc = (lane & 7) * 8;  // read-back: rows rr + 8 it, columns cc .. cc + 7
       const int n = t.nt * BN + wn * 64 + cc;        // Nd is a multiple of 64: all 8 columns valid or none
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      auto stage_block = [&](int i) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1171,92 +1179,214 @@ grouped_gemm_nt(Params p) {
             *reinterpret_cast<float4*>(reg + lr * SWF + j * 32 + 8 * q + 4 * lh) =
                 make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      };
+      auto store_part = [&](float part, bool row_live, int ml) {  // the row's 64 columns of this wave: 8 lanes
+        part += __shfl_xor(part, 1);
+        part += __shfl_xor(part, 2);
+        part += __shfl_xor(part, 4);
+        if (row_live && (lane & 7) == 0) {
+          const int64_t prow = shared ? p.rows_cap_max + t.m0 + ml : t.m0 + ml;
+          p.dw_part[prow * p.dw_parts + t.nt * kDwPartsPerNTile + wn] = part;
+        }
+      };
+      if constexpr (!FP8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          stage_block(i);
 #pragma unroll 2
-        for (int it = 0; it < 4; ++it) {
-          const int r = it * 8 + rr;
-          const int ml = wm * 128 + i * 32 + r;
-          const bool row_live = ml < rows_here;
-          float part = 0.f;
-          if (row_live && n < Nd) {
-            const float w = L.row_w[ml];
-            const int64_t rowo = sh + (int64_t)(t.m0 + ml) * Nd + n;
-            const float4 d0 = *reinterpret_cast<const float4*>(reg + r * SWF + cc);
-            const float4 d1 = *reinterpret_cast<const float4*>(reg + r * SWF + cc + 4);
-            const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-            // saved G and U: bf16 pairs (BF16), or fp32 (MXFP8, read per half below)
-            uint32_t gw[4] = {0, 0, 0, 0}, uw[4] = {0, 0, 0, 0};
-            if constexpr (!FP8) {
+          for (int it = 0; it < 4; ++it) {
+            const int r = it * 8 + rr;
+            const int ml = wm * 128 + i * 32 + r;
+            const bool row_live = ml < rows_here;
+            float part = 0.f;
+            if (row_live && n < Nd) {
+              const float w = L.row_w[ml];
+              const int64_t rowo = sh + (int64_t)(t.m0 + ml) * Nd + n;
+              const float4 d0 = *reinterpret_cast<const float4*>(reg + r * SWF + cc);
+              const float4 d1 = *reinterpret_cast<const float4*>(reg + r * SWF + cc + 4);
+              const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+              // saved G and U: bf16 pairs
               const uint4 gv = *reinterpret_cast<const uint4*>((const uint16_t*)p.g_in + rowo);
               const uint4 uv = *reinterpret_cast<const uint4*>((const uint16_t*)p.u_in + rowo);
-              gw[0] = gv.x; gw[1] = gv.y; gw[2] = gv.z; gw[3] = gv.w;
-              uw[0] = uv.x; uw[1] = uv.y; uw[2] = uv.z; uw[3] = uv.w;
-            }
-            float h[8];
-            if constexpr (FP8) {
-              // the forward's MXFP8 h: 8 codes, all in one block of 32
-              const uint2 hc = *reinterpret_cast<const uint2*>(p.hq_in + rowo);
-              const int64_t srow = (shared ? p.rows_cap_max * (p.I / 32) : 0) + (int64_t)(t.m0 + ml) * (Nd / 32);
-              const int hX = (int)p.hq_scale_in[srow + n / 32] - 127;
-#pragma unroll
-              for (int c = 0; c < 8; ++c) h[c] = e4m3_decode_scaled((c < 4 ? hc.x : hc.y) >> (8 * (c & 3)), hX);
-            } else {
+              const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
               const uint4 hv = *reinterpret_cast<const uint4*>(p.h_in + rowo);
               const uint32_t hw4[4] = {hv.x, hv.y, hv.z, hv.w};
+              float h[8];
 #pragma unroll
               for (int c = 0; c < 8; ++c) h[c] = (c & 1) ? u2f(hw4[c >> 1] & 0xFFFF0000u) : u2f(hw4[c >> 1] << 16);
-            }
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {  // two halves of 4 columns: fewer live registers
-              float dg[4], du[4], hwv[4];
-              float4 g4 = make_float4(0.f, 0.f, 0.f, 0.f), u4 = g4;
-              if constexpr (FP8) {
-                g4 = *reinterpret_cast<const float4*>((const float*)p.g_in + rowo + 4 * hh);
-                u4 = *reinterpret_cast<const float4*>((const float*)p.u_in + rowo + 4 * hh);
-              }
+              for (int hh = 0; hh < 2; ++hh) {  // two halves of 4 columns: fewer live registers
+                float dg[4], du[4], hwv[4];
 #pragma unroll
-              for (int c4 = 0; c4 < 4; ++c4) {
-                const int c = 4 * hh + c4;
-                float g, u;
-                if constexpr (FP8) {
-                  g = c4 == 0 ? g4.x : c4 == 1 ? g4.y : c4 == 2 ? g4.z : g4.w;
-                  u = c4 == 0 ? u4.x : c4 == 1 ? u4.y : c4 == 2 ? u4.z : u4.w;
-                } else {
-                  g = (c & 1) ? u2f(gw[c >> 1] & 0xFFFF0000u) : u2f(gw[c >> 1] << 16);
-                  u = (c & 1) ? u2f(uw[c >> 1] & 0xFFFF0000u) : u2f(uw[c >> 1] << 16);
+                for (int c4 = 0; c4 < 4; ++c4) {
+                  const int c = 4 * hh + c4;
+                  const float g = (c & 1) ? u2f(gw[c >> 1] & 0xFFFF0000u) : u2f(gw[c >> 1] << 16);
+                  const float u = (c & 1) ? u2f(uw[c >> 1] & 0xFFFF0000u) : u2f(uw[c >> 1] << 16);
+                  part += d[c] * h[c];
+                  const float dh = w * d[c];
+                  // through the limit: the clamped inputs, and no gradient where the
+                  // forward clamped (saved as +-inf)
+                  const float L = p.swiglu_lim;
+                  const float gc = __builtin_fminf(g, L), uc = __builtin_fminf(__builtin_fmaxf(u, -L), L);
+                  const float sg = sigmoid_f(gc);
+                  dg[c4] = g < __builtin_inff() ? dh * uc * sg * (1.0f + gc * (1.0f - sg)) : 0.0f;
+                  du[c4] = __builtin_fabsf(u) < __builtin_inff() ? dh * gc * sg : 0.0f;
+                  hwv[c4] = w * h[c];
                 }
-                part += d[c] * h[c];
-                const float dh = w * d[c];
-                // through the limit: the clamped inputs, and no gradient where the
-                // forward clamped (saved as +-inf)
-                const float L = p.swiglu_lim;
-                const float gc = __builtin_fminf(g, L), uc = __builtin_fminf(__builtin_fmaxf(u, -L), L);
-                const float sg = sigmoid_f(gc);
-                dg[c4] = g < __builtin_inff() ? dh * uc * sg * (1.0f + gc * (1.0f - sg)) : 0.0f;
-                du[c4] = __builtin_fabsf(u) < __builtin_inff() ? dh * gc * sg : 0.0f;
-                hwv[c4] = w * h[c];
-              }
-              if constexpr (FP8) {
-                *reinterpret_cast<float4*>(p.dg_out32 + rowo + 4 * hh) = make_float4(dg[0], dg[1], dg[2], dg[3]);
-                *reinterpret_cast<float4*>(p.du_out32 + rowo + 4 * hh) = make_float4(du[0], du[1], du[2], du[3]);
-              } else {
-                *reinterpret_cast<uint2*>(p.dg_out + rowo + 4 * hh) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-                *reinterpret_cast<uint2*>(p.du_out + rowo + 4 * hh) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+                *reinterpret_cast<uint2*>(p.dg_out + rowo + 4 * hh) =
+                    make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+                *reinterpret_cast<uint2*>(p.du_out + rowo + 4 * hh) =
+                    make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
                 if (p.hw_out)
                   *reinterpret_cast<uint2*>(p.hw_out + rowo + 4 * hh) =
                       make_uint2(pack_bf16x2(hwv[0], hwv[1]), pack_bf16x2(hwv[2], hwv[3]));
               }
             }
+            store_part(part, row_live, ml);
           }
-          // the row's 64 columns of this wave: 8 lanes of 8 columns
-          part += __shfl_xor(part, 1);
-          part += __shfl_xor(part, 2);
-          part += __shfl_xor(part, 4);
-          if (row_live && (lane & 7) == 0) {
-            const int64_t prow = shared ? p.rows_cap_max + t.m0 + ml : t.m0 + ml;
-            p.dw_part[prow * p.dw_parts + t.nt * kDwPartsPerNTile + wn] = part;
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+      } else {
+        // MXFP8: h is the forward's E4M3 h (codes and block scales). dG and
+        // dU (fp32) are quantized here, from the values as computed:
+        //  - along I for dA: a row's block of 32 columns is 4 lanes x 8;
+        //  - along rows for the weight gradients: a staged block holds 32
+        //    rows of the expert's segment (tiles start at segment offsets,
+        //    which are multiples of 32). dG replaces dh_hat in the wave's
+        //    first LDS buffer and dU goes to its second; then lane c reduces
+        //    column c's 32 rows of each and writes its 32 codes, one
+        //    contiguous run of the transposed operand [cols, K_e]. Rows past
+        //    the kept rows are zeros, up to K_e (the segment's rows rounded
+        //    up to 128), as the weight gradients' K loop reads them.
+        // The two buffers per wave (rows padded as above) take the stages
+        // and the LDS right after them.
+        static_assert(NTHR / 64 * 2 * 32 * SWF * 4 == NSTAGE * (A_BYTES + B_BYTES) + kEpiExtra, "staging size");
+        float* bufg = reinterpret_cast<float*>(&L.stage[0][0]) + wave * 2 * 32 * SWF;
+        float* bufu = bufg + 32 * SWF;
+        auto at = [](int r, int c) { return r * SWF + c; };
+        const int e_t = shared ? E : t.e;
+        const int k0 = p.tiles128[e_t];
+        const int Kseg = 128 * (p.tiles128[e_t + 1] - k0);  // the segment's K
+        const int seg0 = shared ? 0 : offset_at(t.e);        // its first row
+        const int64_t tb = shared ? p.tq.kr_cap * p.I : (int64_t)128 * k0 * p.I;      // the segment's codes
+        const int64_t tbs = shared ? p.tq.kr_cap / 32 * p.I : (int64_t)4 * k0 * p.I;  // and scales
+        const int64_t rqs = shared ? p.rows_cap_max * (p.I / 32) : 0;
+        const int nw = t.nt * BN + wn * 64;  // the wave's first column
+        const bool cols_live = nw < Nd;      // (the same for the whole wave)
+        auto col_pass = [&](const float* buf, uint8_t* tq, uint8_t* tqs, int kl) {
+          float v[32];
+          uint32_t amax = 0;
+#pragma unroll
+          for (int r2 = 0; r2 < 32; ++r2) {
+            v[r2] = buf[r2 * SWF + lane];
+            amax = max(amax, f2u(v[r2]) & 0x7FFFFFFFu);
+          }
+          const int X = mx_block_exponent(amax);
+          uint32_t w[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) w[q] = e4m3x4_encode_scaled(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], X);
+          uint8_t* o = tq + tb + (int64_t)(nw + lane) * Kseg + kl;
+          *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+          *reinterpret_cast<uint4*>(o + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+          tqs[tbs + (int64_t)(nw + lane) * (Kseg / 32) + kl / 32] = (uint8_t)(X + 127);
+        };
+        if (cols_live) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4*>(bufg + at(lr, j * 32 + 8 * q + 4 * lh)) =
+                    make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 2
+            for (int it = 0; it < 4; ++it) {
+              const int r = it * 8 + rr;
+              const int ml = wm * 128 + i * 32 + r;
+              const bool row_live = ml < rows_here;
+              const int rowi = t.m0 + ml;
+              float part = 0.f;
+              if (row_live) {
+                const float w = L.row_w[ml];
+                const int64_t rowo = sh + (int64_t)rowi * Nd + n;
+                const float4 d0 = *reinterpret_cast<const float4*>(bufg + at(r, cc));
+                const float4 d1 = *reinterpret_cast<const float4*>(bufg + at(r, cc + 4));
+                const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                // the forward's MXFP8 h: 8 codes, all in one block of 32
+                const uint2 hc = *reinterpret_cast<const uint2*>(p.hq_in + rowo);
+                const int hX = (int)p.hq_scale_in[rqs + (int64_t)rowi * (Nd / 32) + n / 32] - 127;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {  // two halves of 4 columns: fewer live registers
+                  // saved G and U: fp32, as accumulated
+                  const float4 g4 = *reinterpret_cast<const float4*>((const float*)p.g_in + rowo + 4 * hh);
+                  const float4 u4 = *reinterpret_cast<const float4*>((const float*)p.u_in + rowo + 4 * hh);
+                  const float gs[4] = {g4.x, g4.y, g4.z, g4.w}, us[4] = {u4.x, u4.y, u4.z, u4.w};
+                  float dg[4], du[4];
+#pragma unroll
+                  for (int c4 = 0; c4 < 4; ++c4) {
+                    const int c = 4 * hh + c4;
+                    const float g = gs[c4], u = us[c4];
+                    const float hval = e4m3_decode_scaled((hh ? hc.y : hc.x) >> (8 * c4), hX);
+                    part += d[c] * hval;
+                    const float dh = w * d[c];
+                    const float L = p.swiglu_lim;
+                    const float gc = __builtin_fminf(g, L), uc = __builtin_fminf(__builtin_fmaxf(u, -L), L);
+                    const float sg = sigmoid_f(gc);
+                    dg[c4] = g < __builtin_inff() ? dh * uc * sg * (1.0f + gc * (1.0f - sg)) : 0.0f;
+                    du[c4] = __builtin_fabsf(u) < __builtin_inff() ? dh * gc * sg : 0.0f;
+                  }
+                  // dG takes these dh_hat values' place; dU the same place in
+                  // the second buffer
+                  *reinterpret_cast<float4*>(bufg + at(r, cc + 4 * hh)) = make_float4(dg[0], dg[1], dg[2], dg[3]);
+                  *reinterpret_cast<float4*>(bufu + at(r, cc + 4 * hh)) = make_float4(du[0], du[1], du[2], du[3]);
+                }
+              } else {  // zeros on rows past the kept rows
+                const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+                *reinterpret_cast<float4*>(bufg + at(r, cc)) = z;
+                *reinterpret_cast<float4*>(bufg + at(r, cc + 4)) = z;
+                *reinterpret_cast<float4*>(bufu + at(r, cc)) = z;
+                *reinterpret_cast<float4*>(bufu + at(r, cc + 4)) = z;
+              }
+              store_part(part, row_live, ml);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // along I: the same lanes read their 8 values of dG, then of dU, back
+#pragma unroll 1
+            for (int it = 0; it < 4; ++it) {
+              const int r = it * 8 + rr;
+              const int ml = wm * 128 + i * 32 + r;
+              const int rowi = t.m0 + ml;
+#pragma unroll
+              for (int gu = 0; gu < 2; ++gu) {
+                const float* buf = gu ? bufu : bufg;
+                const float4 v0 = *reinterpret_cast<const float4*>(buf + at(r, cc));
+                const float4 v1 = *reinterpret_cast<const float4*>(buf + at(r, cc + 4));
+                uint32_t am = max(max(max(f2u(v0.x) & 0x7FFFFFFFu, f2u(v0.y) & 0x7FFFFFFFu),
+                                      max(f2u(v0.z) & 0x7FFFFFFFu, f2u(v0.w) & 0x7FFFFFFFu)),
+                                  max(max(f2u(v1.x) & 0x7FFFFFFFu, f2u(v1.y) & 0x7FFFFFFFu),
+                                      max(f2u(v1.z) & 0x7FFFFFFFu, f2u(v1.w) & 0x7FFFFFFFu)));
+                am = max(am, (uint32_t)__shfl_xor((int)am, 1));
+                am = max(am, (uint32_t)__shfl_xor((int)am, 2));
+                if (ml < rows_here) {
+                  const int X = mx_block_exponent(am);
+                  const int64_t qo = sh + (int64_t)rowi * Nd + n;
+                  *reinterpret_cast<uint2*>((gu ? p.rq_u : p.rq_g) + qo) =
+                      make_uint2(e4m3x4_encode_scaled(v0.x, v0.y, v0.z, v0.w, X),
+                                 e4m3x4_encode_scaled(v1.x, v1.y, v1.z, v1.w, X));
+                  if ((lane & 3) == 0) (gu ? p.rq_us : p.rq_gs)[rqs + (int64_t)rowi * (Nd / 32) + n / 32] = (uint8_t)(X + 127);
+                }
+              }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const int kl = (t.m0 - seg0) + wm * 128 + i * 32;  // the block's first row in the segment
+            if (kl < Kseg) {
+              col_pass(bufg, p.tq.dg, p.tq.dgs, kl);
+              col_pass(bufu, p.tq.du, p.tq.dus, kl);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           }
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
     }
     if (pipe) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's y stores are complete

@@ -109,14 +109,11 @@ struct BwdScratch {
   uint16_t* suT = nullptr;
   uint16_t* dg = nullptr;   // dG, dU: routed [rows_cap_max, I] then shared [T_max, I_s]
   uint16_t* du = nullptr;
-  uint16_t* hw = nullptr;   // (third slot of the region; the MXFP8 backward keeps dU's codes there)
+  uint16_t* hw = nullptr;   // (the MXFP8 backward keeps dU's codes at the start of the region)
   float* dw_part = nullptr;      // [rows_cap_max + T_max, dw_parts(cfg)]
   // MXFP8: transposed weights quantized along their new rows (codes, scales)
   uint8_t *wdTq = nullptr, *wgTq = nullptr, *wuTq = nullptr, *sdTq = nullptr, *sgTq = nullptr, *suTq = nullptr;
   uint8_t *wdTs = nullptr, *wgTs = nullptr, *wuTs = nullptr, *sdTs = nullptr, *sgTs = nullptr, *suTs = nullptr;
-  // MXFP8: dG, dU in fp32 (routed rows then shared rows, as dg / du)
-  float* dg32 = nullptr;
-  float* du32 = nullptr;
   // MXFP8: dU quantized along I (dG uses the workspace's hq buffer)
   uint8_t* duq = nullptr;
   uint8_t* duq_scale = nullptr;
@@ -207,14 +204,11 @@ hipError_t launch_quantize_t_matrix(const void* src, int64_t batches, int64_t R,
 // The weight-gradient GEMM operands (TqArrays layout; bf16 elements without
 // scales when out_bf16, kinds 0-2 only) from one source:
 // src_kind 0 = x token rows, 1 = router weight times grad_out token rows,
-// 2 = schedule-row bf16 rows, 3 = schedule-row MXFP8 rows (h), 4 =
-// schedule-row fp32 rows (dG, dU). Kind 4 with rowq also writes the kept
-// rows quantized along their columns (row-major, the h codes' layout).
+// 2 = schedule-row bf16 rows, 3 = schedule-row MXFP8 rows (h).
 hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* src, const uint8_t* src_codes,
                                   const uint8_t* src_scale, const float* router_w, int E, int k, int cols_r, int cols_s,
                                   int64_t rows_cap_max, int64_t kr_cap, uint8_t* dst, uint8_t* dst_scale, int grid,
-                                  hipStream_t s, bool out_bf16 = false, uint8_t* rowq = nullptr,
-                                  uint8_t* rowq_scale = nullptr);
+                                  hipStream_t s, bool out_bf16 = false);
 
 // Axis-1 MXFP8 quantization of a bf16 [T, cols] tensor whose row count T is
 // read on the device from a schedule header; the grid covers max_rows.

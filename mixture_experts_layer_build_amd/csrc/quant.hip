@@ -237,8 +237,7 @@ enum TqSrc : int {
   TQ_X = 0,     // x rows of the segment's tokens (bf16)
   TQ_DY = 1,    // router weight times grad_out rows (bf16 source, fp32 product)
   TQ_ROWS = 2,  // schedule-row-indexed bf16 rows (dG, dU)
-  TQ_MX = 3,    // schedule-row-indexed MXFP8 rows (the forward's h codes and scales)
-  TQ_ROWS32 = 4 // schedule-row-indexed fp32 rows (dG, dU of the MXFP8 backward)
+  TQ_MX = 3     // schedule-row-indexed MXFP8 rows (the forward's h codes and scales)
 };
 
 constexpr int kMaxT128 = 1024 + 2;  // experts + 2 entries of a workspace's largest tile table
@@ -255,13 +254,10 @@ struct TqParams {
   int E, k, cols_r, cols_s;
   int64_t rows_cap_max, kr_cap;
   const uint16_t* src;       // TQ_X / TQ_DY: token rows [T, cols]; TQ_ROWS: routed rows then shared rows
-  const float* src32;        // TQ_ROWS32: routed rows then shared rows
   const uint8_t* src_codes;  // TQ_MX
   const uint8_t* src_scale;
   uint8_t* dst;
   uint8_t* dst_scale;
-  uint8_t* rowq;        // TQ_ROWS32 (optional): the same rows quantized along their columns, row-major
-  uint8_t* rowq_scale;  // (the layout of the forward's h codes: routed rows, then shared rows)
 };
 
 // The weight-gradient GEMMs' operands: for expert e, rows of its segment in
@@ -311,12 +307,11 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
   // The thread's 32 source values of its row (row r of the block, columns
   // 32 * half ..), held as loaded so that the next unit's loads are in
   // flight while the current unit is quantized and stored.
-  constexpr int NV = SRC == TQ_ROWS32 ? 8 : SRC == TQ_MX ? 2 : 4;  // 16-byte loads
+  constexpr int NV = SRC == TQ_MX ? 2 : 4;  // 16-byte loads
   uint4 raw[NV];
   float mul = 1.0f;
   int X = 0;
   bool have = false;
-  int64_t qo = 0, qso = 0;  // TQ_ROWS32 with rowq: the block's code and scale offsets
   auto fetch = [&](const Unit& w) {
     have = false;
     mul = 1.0f;
@@ -327,13 +322,7 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
     const int nrows = shared ? T : p.kept[w.e];
     if (lr >= nrows) return;  // zero row past the segment's end
     const int64_t row = shared ? lr : p.offsets[w.e] + (int64_t)lr;
-    if constexpr (SRC == TQ_ROWS32) {
-      qo = (shared ? p.rows_cap_max * p.cols_r : 0) + row * w.cols + c0;
-      qso = (shared ? p.rows_cap_max * (p.cols_r / 32) : 0) + row * (w.cols / 32) + c0 / 32;
-      const float* s = p.src32 + qo;
-#pragma unroll
-      for (int q = 0; q < NV; ++q) raw[q] = *reinterpret_cast<const uint4*>(s + 4 * q);
-    } else if constexpr (SRC == TQ_MX) {
+    if constexpr (SRC == TQ_MX) {
       const int64_t code0 = shared ? p.rows_cap_max * p.cols_r + row * w.cols : row * w.cols;
       const int64_t sc0 = shared ? p.rows_cap_max * (p.cols_r / 32) + row * (w.cols / 32) : row * (w.cols / 32);
       X = (int)p.src_scale[sc0 + c0 / 32] - 127;
@@ -363,33 +352,12 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
       for (int i = 0; i < 32; ++i) trow[i] = 0.f;
       return;
     }
-    if constexpr (SRC == TQ_ROWS32) {
-      // the thread's 32 values are one block along the row: its codes for
-      // the GEMM that contracts over the columns (dA), from the same fp32
-      if (p.rowq) {
-        uint32_t amax = 0;
-#pragma unroll
-        for (int q = 0; q < NV; ++q)
-          amax = max(max(amax, max(raw[q].x & 0x7FFFFFFFu, raw[q].y & 0x7FFFFFFFu)),
-                     max(raw[q].z & 0x7FFFFFFFu, raw[q].w & 0x7FFFFFFFu));
-        const int Xr = mx_block_exponent(amax);
-        uint32_t cw[NV];
-#pragma unroll
-        for (int q = 0; q < NV; ++q)
-          cw[q] = e4m3x4_encode_scaled(u2f(raw[q].x), u2f(raw[q].y), u2f(raw[q].z), u2f(raw[q].w), Xr);
-        *reinterpret_cast<uint4*>(p.rowq + qo) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-        *reinterpret_cast<uint4*>(p.rowq + qo + 16) = make_uint4(cw[4], cw[5], cw[6], cw[7]);
-        p.rowq_scale[qso] = (uint8_t)(Xr + 127);
-      }
-    }
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
       const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if constexpr (SRC == TQ_ROWS32) {
-          trow[4 * q + j] = u2f(w[j]);
-        } else if constexpr (SRC == TQ_MX) {
+        if constexpr (SRC == TQ_MX) {
 #pragma unroll
           for (int b = 0; b < 4; ++b) trow[16 * q + 4 * j + b] = e4m3_decode_scaled(w[j] >> (8 * b), X);
         } else {
@@ -542,10 +510,8 @@ hipError_t launch_quantize_t_matrix(const void* src, int64_t batches, int64_t R,
 hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* src, const uint8_t* src_codes,
                                   const uint8_t* src_scale, const float* router_w, int E, int k, int cols_r, int cols_s,
                                   int64_t rows_cap_max, int64_t kr_cap, uint8_t* dst, uint8_t* dst_scale, int grid,
-                                  hipStream_t s, bool out_bf16, uint8_t* rowq, uint8_t* rowq_scale) {
+                                  hipStream_t s, bool out_bf16) {
   TqParams p{};
-  p.rowq = rowq;
-  p.rowq_scale = rowq_scale;
   p.hdr = v.header;
   p.hash = v.hash;
   p.status = v.status;
@@ -561,7 +527,6 @@ hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* 
   p.rows_cap_max = rows_cap_max;
   p.kr_cap = kr_cap;
   p.src = (const uint16_t*)src;
-  p.src32 = (const float*)src;
   p.src_codes = src_codes;
   p.src_scale = src_scale;
   p.dst = dst;
@@ -578,7 +543,6 @@ hipError_t launch_quantize_t_rows(int src_kind, const SchedView& v, const void* 
       case TQ_X: quant_t_rows<TQ_X><<<grid, 256, 0, s>>>(p); break;
       case TQ_DY: quant_t_rows<TQ_DY><<<grid, 256, 0, s>>>(p); break;
       case TQ_ROWS: quant_t_rows<TQ_ROWS><<<grid, 256, 0, s>>>(p); break;
-      case TQ_ROWS32: quant_t_rows<TQ_ROWS32><<<grid, 256, 0, s>>>(p); break;
       default: quant_t_rows<TQ_MX><<<grid, 256, 0, s>>>(p); break;
     }
   }
