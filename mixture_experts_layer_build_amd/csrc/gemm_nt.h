@@ -821,7 +821,8 @@ grouped_gemm_nt(Params p) {
     // runs only its valid blocks' LDS reads and MFMAs without a per-block
     // branch in the unrolled step)
     // As, Bs: the stage's A and B rows; Sa, Sb: their MXFP8 scale dwords
-    auto compute = [&](auto ni_c, const uint8_t* As, const uint8_t* Bs, const uint8_t* Sa, const uint8_t* Sb) {
+    // pre(ks): called in BF16 sub-step ks before its MFMAs (the staggered load issue below)
+    auto compute = [&](auto ni_c, const uint8_t* As, const uint8_t* Bs, const uint8_t* Sa, const uint8_t* Sb, auto&& pre) {
       constexpr int NI = decltype(ni_c)::value;
       if constexpr (!FP8 && MODE == BWD_DH) {
         // (the dh epilogue leaves no registers for a second fragment set)
@@ -834,6 +835,7 @@ grouped_gemm_nt(Params p) {
             fa[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + i * 32 + lr) * ROWB + pc);
 #pragma unroll
           for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(Bs + (b_row(j) + lr) * ROWB + pc);
+          pre(ks);
 #pragma unroll
           for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -858,6 +860,7 @@ grouped_gemm_nt(Params p) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           if (ks + 1 < 4) load_frags(ks + 1, (ks + 1) & 1);
+          pre(ks);
           __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this sub-step's MFMAs
 #pragma unroll
           for (int i = 0; i < NI; ++i)
@@ -934,11 +937,20 @@ grouped_gemm_nt(Params p) {
       for (int kt = 0; kt < nk; ++kt) {
         wait_vmcnt<0>();
         __syncthreads();  // every wave's loads of step kt landed; step kt-1's stage is free
-        if (kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
+        // BF16: the two waves of a SIMD issue the next step's loads at
+        // different times (waves 0-3 here, waves 4-7 after their first
+        // sub-step's MFMAs), so that while one waits to issue its loads at
+        // the CU's load unit the other's MFMAs keep the matrix pipe busy.
+        // (MXFP8: issued here by all; the later issue point spills its
+        // fragments.)
+        constexpr bool kStagger = !FP8 && decltype(ni_c)::value > 0;
+        if ((!kStagger || wave < 4) && kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
         if constexpr (decltype(ni_c)::value > 0) {
           const uint8_t* As = &L.stage[kt & 1][0];
           const uint8_t* Sa = &L.scale[kt & 1][0];
-          compute(ni_c, As, As + A_BYTES, Sa, Sa + SA_BYTES);
+          compute(ni_c, As, As + A_BYTES, Sa, Sa + SA_BYTES, [&](int i) {
+            if (kStagger && wave >= 4 && i == 1 && kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
+          });
         }
       }
     };
@@ -980,7 +992,7 @@ grouped_gemm_nt(Params p) {
         if constexpr (decltype(ni_c)::value > 0) {
           const uint8_t* As = &L.stage[0][0] + slot * SHORT_SLOT;
           const uint8_t* Sa = &L.scale[0][0] + slot * SHORT_SSLOT;
-          compute(ni_c, As, As + SHORT_ROWS * ROWB, Sa, Sa + SHORT_ROWS * 4);
+          compute(ni_c, As, As + SHORT_ROWS * ROWB, Sa, Sa + SHORT_ROWS * 4, [](int) {});
         }
         slot = slot == 2 ? 0 : slot + 1;
       }
