@@ -20,15 +20,31 @@ __host__ __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit
 
 __host__ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return u2f((uint32_t)b << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (inputs finite; NaN kept quiet).
+typedef __attribute__((ext_vector_type(2))) float f32x2v;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+
+// fp32 -> bf16 bits, round to nearest even. On the device this is gfx950's
+// packed conversion instruction (v_cvt_pk_bf16_f32): compared on the GPU
+// with the integer rounding of the host path over 1.4e8 bit patterns of
+// every exponent, it gave the same bits for every finite input, subnormals
+// included; only NaN payloads may differ (both stay NaN). The integer form
+// costs a divergent branch per value.
 __host__ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+#else
   uint32_t u = f2u(f);
   if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+#endif
 }
 
 __host__ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){lo, hi}, bf16x2v));
+#else
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+#endif
 }
 
 // floor(log2 |v|) of a non-zero fp32 magnitude given by its bits (sign clear),
