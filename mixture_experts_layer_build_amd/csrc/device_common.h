@@ -135,8 +135,12 @@ __device__ uint32_t e4m3x4_encode_scaled(float v0, float v1, float v2, float v3,
 // Value of E4M3 code `code` (low 8 bits) times 2^X: a 4-bit significand
 // scaled by a power of two, so the fp32 result is exact (subnormals too).
 __host__ __device__ __forceinline__ float e4m3_decode_scaled(uint32_t code, int X) {
+  // subnormal codes (e == 0) are m * 2^(1 - 10 + X), normal ones (8 + m) *
+  // 2^(e - 10 + X): integer selects and one ldexp, no branch
   const uint32_t e = (code >> 3) & 15u, m = code & 7u;
-  const float mag = e == 0 ? __builtin_ldexpf((float)m, X - 9) : __builtin_ldexpf((float)(8u + m), (int)e - 10 + X);
+  const uint32_t sig = m | (e != 0 ? 8u : 0u);
+  const int ex = (e != 0 ? (int)e : 1) - 10 + X;
+  const float mag = __builtin_ldexpf((float)sig, ex);
   return (code & 0x80u) ? -mag : mag;
 }
 

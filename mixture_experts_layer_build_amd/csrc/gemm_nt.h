@@ -1241,8 +1241,11 @@ grouped_gemm_nt(Params p) {
                   const float L = p.swiglu_lim;
                   const float gc = __builtin_fminf(g, L), uc = __builtin_fminf(__builtin_fmaxf(u, -L), L);
                   const float sg = sigmoid_f(gc);
-                  dg[c4] = g < __builtin_inff() ? dh * uc * sg * (1.0f + gc * (1.0f - sg)) : 0.0f;
-                  du[c4] = __builtin_fabsf(u) < __builtin_inff() ? dh * gc * sg : 0.0f;
+                  // (both products computed, then selected: as conditional
+                  // expressions the compiler branched around them per value)
+                  const float dgv = dh * uc * sg * (1.0f + gc * (1.0f - sg)), duv = dh * gc * sg;
+                  dg[c4] = g < __builtin_inff() ? dgv : 0.0f;
+                  du[c4] = __builtin_fabsf(u) < __builtin_inff() ? duv : 0.0f;
                   hwv[c4] = w * h[c];
                 }
                 *reinterpret_cast<uint2*>(p.dg_out + rowo + 4 * hh) =
@@ -1345,8 +1348,9 @@ grouped_gemm_nt(Params p) {
                     const float L = p.swiglu_lim;
                     const float gc = __builtin_fminf(g, L), uc = __builtin_fminf(__builtin_fmaxf(u, -L), L);
                     const float sg = sigmoid_f(gc);
-                    dg[c4] = g < __builtin_inff() ? dh * uc * sg * (1.0f + gc * (1.0f - sg)) : 0.0f;
-                    du[c4] = __builtin_fabsf(u) < __builtin_inff() ? dh * gc * sg : 0.0f;
+                    const float dgv = dh * uc * sg * (1.0f + gc * (1.0f - sg)), duv = dh * gc * sg;
+                    dg[c4] = g < __builtin_inff() ? dgv : 0.0f;
+                    du[c4] = __builtin_fabsf(u) < __builtin_inff() ? duv : 0.0f;
                   }
                   // dG takes these dh_hat values' place; dU the same place in
                   // the second buffer
