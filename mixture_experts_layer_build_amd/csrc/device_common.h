@@ -132,6 +132,24 @@ __device__ __forceinline__ uint32_t e4m3x4_encode_scaled(float v0, float v1, flo
 __device__ uint32_t e4m3x4_encode_scaled(float v0, float v1, float v2, float v3, int X);  // device only
 #endif
 
+#if defined(__HIP_DEVICE_COMPILE__)
+// Value of byte b (0-3, a constant after unrolling) of `word` as an E4M3
+// code, times `scale` = 2^X, on gfx950's scaled conversion instruction (one
+// value per instruction). Compared on the GPU with e4m3_decode_scaled below
+// for every code but the two NaN codes (which the encoder never writes),
+// every X in [-127, 127] and every byte position: identical bits.
+__device__ __forceinline__ float e4m3_decode_byte_scaled(uint32_t word, int b, float scale) {
+  switch (b) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_f32_fp8((int)word, scale, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_f32_fp8((int)word, scale, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_f32_fp8((int)word, scale, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_f32_fp8((int)word, scale, 3);
+  }
+}
+#else
+__device__ float e4m3_decode_byte_scaled(uint32_t word, int b, float scale);  // device only
+#endif
+
 // Value of E4M3 code `code` (low 8 bits) times 2^X: a 4-bit significand
 // scaled by a power of two, so the fp32 result is exact (subnormals too).
 __host__ __device__ __forceinline__ float e4m3_decode_scaled(uint32_t code, int X) {

@@ -1330,7 +1330,8 @@ grouped_gemm_nt(Params p) {
                 const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
                 // the forward's MXFP8 h: 8 codes, all in one block of 32
                 const uint2 hc = *reinterpret_cast<const uint2*>(p.hq_in + rowo);
-                const int hX = (int)p.hq_scale_in[rqs + (int64_t)rowi * (Nd / 32) + n / 32] - 127;
+                const float hs =
+                    __builtin_ldexpf(1.0f, (int)p.hq_scale_in[rqs + (int64_t)rowi * (Nd / 32) + n / 32] - 127);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {  // two halves of 4 columns: fewer live registers
                   // saved G and U: fp32, as accumulated
@@ -1342,7 +1343,7 @@ grouped_gemm_nt(Params p) {
                   for (int c4 = 0; c4 < 4; ++c4) {
                     const int c = 4 * hh + c4;
                     const float g = gs[c4], u = us[c4];
-                    const float hval = e4m3_decode_scaled((hh ? hc.y : hc.x) >> (8 * c4), hX);
+                    const float hval = e4m3_decode_byte_scaled(hh ? hc.y : hc.x, c4, hs);
                     part += d[c] * hval;
                     const float dh = w * d[c];
                     const float L = p.swiglu_lim;

@@ -352,6 +352,7 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
       for (int i = 0; i < 32; ++i) trow[i] = 0.f;
       return;
     }
+    const float xs = SRC == TQ_MX ? __builtin_ldexpf(1.0f, X) : 1.0f;  // the h block's scale 2^X
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
       const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
@@ -359,7 +360,7 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
       for (int j = 0; j < 4; ++j) {
         if constexpr (SRC == TQ_MX) {
 #pragma unroll
-          for (int b = 0; b < 4; ++b) trow[16 * q + 4 * j + b] = e4m3_decode_scaled(w[j] >> (8 * b), X);
+          for (int b = 0; b < 4; ++b) trow[16 * q + 4 * j + b] = e4m3_decode_byte_scaled(w[j], b, xs);
         } else {
           trow[8 * q + 2 * j] = mul * u2f(w[j] << 16);
           trow[8 * q + 2 * j + 1] = mul * u2f(w[j] & 0xFFFF0000u);
