@@ -1288,7 +1288,13 @@ grouped_gemm_nt(Params p) {
         const int64_t rqs = shared ? p.rows_cap_max * (p.I / 32) : 0;
         const int nw = t.nt * BN + wn * 64;  // the wave's first column
         const bool cols_live = nw < Nd;      // (the same for the whole wave)
-        auto col_pass = [&](const float* buf, uint8_t* tq, uint8_t* tqs, int kl) {
+        // the wave's 4 blocks are all below K_e or all past it (K_e and the
+        // wave's first row are multiples of 128): their 4 scale bytes per
+        // column are adjacent, and go out as one dword after the last block
+        const int kl0 = (t.m0 - seg0) + wm * 128;
+        const bool blocks_live = kl0 < Kseg;
+        uint32_t sc_g = 0, sc_u = 0;
+        auto col_pass = [&](const float* buf, uint8_t* tq, uint32_t& sc, int kl, int i) {
           float v[32];
           uint32_t amax = 0;
 #pragma unroll
@@ -1303,7 +1309,7 @@ grouped_gemm_nt(Params p) {
           uint8_t* o = tq + tb + (int64_t)(nw + lane) * Kseg + kl;
           *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
           *reinterpret_cast<uint4*>(o + 16) = make_uint4(w[4], w[5], w[6], w[7]);
-          tqs[tbs + (int64_t)(nw + lane) * (Kseg / 32) + kl / 32] = (uint8_t)(X + 127);
+          sc |= (uint32_t)(X + 127) << (8 * i);
         };
         if (cols_live) {
 #pragma unroll
@@ -1396,12 +1402,17 @@ grouped_gemm_nt(Params p) {
               }
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            const int kl = (t.m0 - seg0) + wm * 128 + i * 32;  // the block's first row in the segment
-            if (kl < Kseg) {
-              col_pass(bufg, p.tq.dg, p.tq.dgs, kl);
-              col_pass(bufu, p.tq.du, p.tq.dus, kl);
+            if (blocks_live) {
+              const int kl = kl0 + i * 32;  // the block's first row in the segment
+              col_pass(bufg, p.tq.dg, sc_g, kl, i);
+              col_pass(bufu, p.tq.du, sc_u, kl, i);
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          }
+          if (blocks_live) {
+            const int64_t so = tbs + (int64_t)(nw + lane) * (Kseg / 32) + kl0 / 32;
+            *reinterpret_cast<uint32_t*>(p.tq.dgs + so) = sc_g;
+            *reinterpret_cast<uint32_t*>(p.tq.dus + so) = sc_u;
           }
         }
       }
