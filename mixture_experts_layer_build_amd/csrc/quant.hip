@@ -171,13 +171,20 @@ __global__ void __launch_bounds__(256) quant_axis0(const T* __restrict__ src, in
 
 constexpr int kTqRows = 128, kTqCols = 64, kTqLd = kTqCols + 1;
 
+// LDS column of (row, col) in the quantizers' 128 x 64 fp32 tile: the
+// column is XORed with 16 times the row's 32-row block, so that the column
+// reads of tq_store (4 lanes of a column in 4 different blocks) fall in
+// distinct banks; the row-wise staging writes (one 32-row block per wave)
+// stay conflict-free.
+__device__ __forceinline__ int tq_col(int row, int col) { return col ^ ((row >> 5) << 4); }
+
 __device__ __forceinline__ void tq_store(const float (*tile)[kTqLd], uint8_t* out_row, uint8_t* scale_row) {
   const int c = threadIdx.x >> 2, b = threadIdx.x & 3;
   float v[32];
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    v[i] = tile[32 * b + i][c];
+    v[i] = tile[32 * b + i][c ^ (b << 4)];  // tq_col(32 b + i, c)
     amax = max(amax, f2u(v[i]) & 0x7FFFFFFFu);
   }
   const int X = mx_block_exponent(amax);
@@ -212,14 +219,14 @@ __global__ void __launch_bounds__(256) quant_t_matrix(const uint16_t* __restrict
   int64_t u = blockIdx.x;
   if (u < units) fetch(u, raw);
   for (; u < units; u += gridDim.x) {
-    float* trow = &tile[r][32 * half];
+    float* trow = &tile[r][0];  // column (32 half + k) at tq_col(r, 32 half + k)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        trow[8 * q + 2 * j] = u2f(w[j] << 16);
-        trow[8 * q + 2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
+        trow[tq_col(r, 32 * half + 8 * q + 2 * j)] = u2f(w[j] << 16);
+        trow[tq_col(r, 32 * half + 8 * q + 2 * j + 1)] = u2f(w[j] & 0xFFFF0000u);
       }
     }
     __syncthreads();
@@ -346,10 +353,10 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
   };
   // raw values -> fp32 in the LDS tile (zeros for a row past the segment)
   auto stage = [&]() {
-    float* trow = &tile[r][32 * half];
+    float* trow = &tile[r][0];  // column (32 half + k) at tq_col(r, 32 half + k)
     if (!have) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) trow[i] = 0.f;
+      for (int i = 0; i < 32; ++i) trow[tq_col(r, 32 * half + i)] = 0.f;
       return;
     }
     const float xs = SRC == TQ_MX ? __builtin_ldexpf(1.0f, X) : 1.0f;  // the h block's scale 2^X
@@ -360,10 +367,10 @@ __global__ void __launch_bounds__(256) quant_t_rows(TqParams p) {
       for (int j = 0; j < 4; ++j) {
         if constexpr (SRC == TQ_MX) {
 #pragma unroll
-          for (int b = 0; b < 4; ++b) trow[16 * q + 4 * j + b] = e4m3_decode_byte_scaled(w[j], b, xs);
+          for (int b = 0; b < 4; ++b) trow[tq_col(r, 32 * half + 16 * q + 4 * j + b)] = e4m3_decode_byte_scaled(w[j], b, xs);
         } else {
-          trow[8 * q + 2 * j] = mul * u2f(w[j] << 16);
-          trow[8 * q + 2 * j + 1] = mul * u2f(w[j] & 0xFFFF0000u);
+          trow[tq_col(r, 32 * half + 8 * q + 2 * j)] = mul * u2f(w[j] << 16);
+          trow[tq_col(r, 32 * half + 8 * q + 2 * j + 1)] = mul * u2f(w[j] & 0xFFFF0000u);
         }
       }
     }
