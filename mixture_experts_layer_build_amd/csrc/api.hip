@@ -302,9 +302,19 @@ extern "C" mok_status mok_validate_config(const mok_config* c) {
   if (c->max_tokens * (int64_t)c->topk >= (int64_t)1 << 31) return MOK_ERR_UNSUPPORTED;
   const Layout L = schedule_layout(*c);
   if (L.rows_cap_max + c->max_tokens >= (int64_t)1 << 31) return MOK_ERR_UNSUPPORTED;
-  // token-indexed operands are read through one buffer range each, offsets
-  // below 2 GiB (the kernels' out-of-range marker sits at 2 GiB)
-  if (c->max_tokens * (int64_t)c->hidden * 2 >= (int64_t)1 << 31) return MOK_ERR_UNSUPPORTED;
+  // Operands are read through one buffer range each, with offsets below
+  // 2 GiB (the kernels' out-of-range marker sits at 2 GiB):
+  //  - token-indexed operands: max_tokens rows of H, I or I_s bf16 elements
+  //    (an expert may receive every token, and the weight gradients read its
+  //    rows transposed, [I or H][rows]), and a weight-gradient tile's 256
+  //    rows of that expert's row count;
+  //  - one expert's weight matrix, I x H or I_s x H bf16 elements.
+  const int64_t widest = std::max({(int64_t)c->hidden, (int64_t)c->intermediate,
+                                   (int64_t)c->shared_intermediate, (int64_t)256});
+  if (c->max_tokens * widest * 2 >= (int64_t)1 << 31) return MOK_ERR_UNSUPPORTED;
+  if ((int64_t)c->intermediate * c->hidden * 2 >= (int64_t)1 << 31 ||
+      (int64_t)c->shared_intermediate * c->hidden * 2 >= (int64_t)1 << 31)
+    return MOK_ERR_UNSUPPORTED;
   return MOK_OK;
 }
 
