@@ -69,7 +69,7 @@ typedef enum mok_mode {
  * expert); 1 <= num_experts <= 1024; 1 <= topk <= 64; expert_pad a positive
  * multiple of 32 (MXFP8 backward needs 32-row blocks inside one expert);
  * max_tokens >= 1 with max_tokens * topk < 2^31. Every operand a kernel
- * reads stays below 2 GiB: max_tokens * max(hidden, intermediate,
+ * reads stays below 2 GiB: (max_tokens + 127) * max(hidden, intermediate,
  * shared_intermediate, 256) * 2 < 2^31, intermediate * hidden * 2 < 2^31 and
  * shared_intermediate * hidden * 2 < 2^31; and the schedule's row bound
  * rows_cap_max + max_tokens < 2^31.

@@ -306,12 +306,12 @@ extern "C" mok_status mok_validate_config(const mok_config* c) {
   // 2 GiB (the kernels' out-of-range marker sits at 2 GiB):
   //  - token-indexed operands: max_tokens rows of H, I or I_s bf16 elements
   //    (an expert may receive every token, and the weight gradients read its
-  //    rows transposed, [I or H][rows]), and a weight-gradient tile's 256
-  //    rows of that expert's row count;
+  //    rows transposed, [I or H][rows rounded up to 128]), and a
+  //    weight-gradient tile's 256 rows of that expert's rounded row count;
   //  - one expert's weight matrix, I x H or I_s x H bf16 elements.
   const int64_t widest = std::max({(int64_t)c->hidden, (int64_t)c->intermediate,
                                    (int64_t)c->shared_intermediate, (int64_t)256});
-  if (c->max_tokens * widest * 2 >= (int64_t)1 << 31) return MOK_ERR_UNSUPPORTED;
+  if ((c->max_tokens + 127) * widest * 2 >= (int64_t)1 << 31) return MOK_ERR_UNSUPPORTED;
   if ((int64_t)c->intermediate * c->hidden * 2 >= (int64_t)1 << 31 ||
       (int64_t)c->shared_intermediate * c->hidden * 2 >= (int64_t)1 << 31)
     return MOK_ERR_UNSUPPORTED;

@@ -59,15 +59,16 @@ def test_validate_config_contract():
     assert status(cfg(max_tokens=0)) == _lib.MOK_ERR_INVALID_ARGUMENT
     assert status(cfg(capacity_multiplier=0.0)) == _lib.MOK_ERR_INVALID_ARGUMENT
     assert status(cfg(capacity_multiplier=float("nan"))) == _lib.MOK_ERR_INVALID_ARGUMENT
-    # every operand a kernel reads stays below 2 GiB: token rows of the
-    # widest of H, I, I_s and 256 (an expert may receive every token), and one
-    # expert's weight matrix
-    assert status(cfg(max_tokens=(1 << 30) // 2048 - 1)) == _lib.MOK_OK
-    assert status(cfg(max_tokens=(1 << 30) // 2048)) == _lib.MOK_ERR_UNSUPPORTED
-    assert status(cfg(intermediate=65536, max_tokens=(1 << 30) // 65536 - 1)) == _lib.MOK_OK
-    assert status(cfg(intermediate=65536, max_tokens=(1 << 30) // 65536)) == _lib.MOK_ERR_UNSUPPORTED
-    assert status(cfg(hidden=128, intermediate=64, shared_intermediate=0, max_tokens=(1 << 22) - 1)) == _lib.MOK_OK
-    assert status(cfg(hidden=128, intermediate=64, shared_intermediate=0, max_tokens=1 << 22)) == \
+    # every operand a kernel reads stays below 2 GiB: token rows (up to 127
+    # more in the weight gradients' rounded row counts) of the widest of H, I,
+    # I_s and 256 (an expert may receive every token), and one expert's weight
+    # matrix
+    assert status(cfg(max_tokens=(1 << 30) // 2048 - 128)) == _lib.MOK_OK
+    assert status(cfg(max_tokens=(1 << 30) // 2048 - 127)) == _lib.MOK_ERR_UNSUPPORTED
+    assert status(cfg(intermediate=65536, max_tokens=(1 << 30) // 65536 - 128)) == _lib.MOK_OK
+    assert status(cfg(intermediate=65536, max_tokens=(1 << 30) // 65536 - 127)) == _lib.MOK_ERR_UNSUPPORTED
+    assert status(cfg(hidden=128, intermediate=64, shared_intermediate=0, max_tokens=(1 << 22) - 128)) == _lib.MOK_OK
+    assert status(cfg(hidden=128, intermediate=64, shared_intermediate=0, max_tokens=(1 << 22) - 127)) == \
         _lib.MOK_ERR_UNSUPPORTED
     assert status(cfg(hidden=65536, intermediate=16384 - 64, max_tokens=8)) == _lib.MOK_OK
     assert status(cfg(hidden=65536, intermediate=16384, max_tokens=8)) == _lib.MOK_ERR_UNSUPPORTED
