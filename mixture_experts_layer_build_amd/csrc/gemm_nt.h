@@ -1163,7 +1163,12 @@ grouped_gemm_nt(Params p) {
               __hip_atomic_store(d8 + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
             } else {
-              *reinterpret_cast<u32x4*>(ob + (int64_t)(t.m0 + ml) * ldo + col) = v;
+              // non-temporal: the rows are read back by a later launch (or
+              // the caller), so streaming them past L2 keeps the operands'
+              // lines there. Each instruction writes whole 128-byte lines (8
+              // lanes per row); partial-line stores marked this way were
+              // slower.
+              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(ob + (int64_t)(t.m0 + ml) * ldo + col));
             }
           }
         }
