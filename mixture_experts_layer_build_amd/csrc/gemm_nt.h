@@ -1096,25 +1096,46 @@ grouped_gemm_nt(Params p) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(reg + r * SW + (lane & 1) * 16);
           if (ml < rows_here && col < Nd) *reinterpret_cast<u32x4*>(hq + (int64_t)(t.m0 + ml) * Nd + col) = v;
         }
-        if (p.ctx_g) {  // G and U for the backward, fp32 as accumulated (direct 16-byte stores)
-          float* cg = (float*)p.ctx_g;
-          float* cu = (float*)p.ctx_u;
+        if (p.ctx_g) {
+          // G and U for the backward, fp32 as accumulated. Staged through
+          // LDS 64 rows at a time, so that each store instruction writes
+          // whole 128-byte lines (8 lanes per row: the wave's 32 columns),
+          // non-temporal: they are read only by the backward, and streaming
+          // them past L2 keeps the operands' lines there.
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          constexpr int SWC = 32 + 4;  // staged row stride (floats)
+          // (past the 8 waves' h staging areas, so no wave waits for another)
+          float* regc = reinterpret_cast<float*>(&L.stage[0][0] + NTHR / 64 * 128 * SW) + wave * 64 * SWC;
+          static_assert(NTHR / 64 * (128 * SW + 64 * SWC * 4) <= NSTAGE * (A_BYTES + B_BYTES), "ctx staging fits");
+          const float L = p.swiglu_lim;
+          const int col = col0 + (lane & 7) * 4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int ml = wm * 128 + i * 32 + lr;
-            if (ml >= rows_here) continue;
+          for (int gu = 0; gu < 2; ++gu) {
+            float* dst = gu ? (float*)p.ctx_u : (float*)p.ctx_g;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int n = col0 + 8 * q + 4 * lh;
-              if (n >= Nd) continue;
-              const int64_t o = sh + (int64_t)(t.m0 + ml) * Nd + n;
-              const float L = p.swiglu_lim;
-              *reinterpret_cast<float4*>(cg + o) =
-                  make_float4(saved_gate(acc[i][0][4 * q], L), saved_gate(acc[i][0][4 * q + 1], L),
-                              saved_gate(acc[i][0][4 * q + 2], L), saved_gate(acc[i][0][4 * q + 3], L));
-              *reinterpret_cast<float4*>(cu + o) =
-                  make_float4(saved_up(acc[i][1][4 * q], L), saved_up(acc[i][1][4 * q + 1], L),
-                              saved_up(acc[i][1][4 * q + 2], L), saved_up(acc[i][1][4 * q + 3], L));
+            for (int half = 0; half < 2; ++half) {
+#pragma unroll
+              for (int ii = 0; ii < 2; ++ii) {
+                const int i = 2 * half + ii;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const float a0 = acc[i][gu][4 * q], a1 = acc[i][gu][4 * q + 1], a2 = acc[i][gu][4 * q + 2],
+                              a3 = acc[i][gu][4 * q + 3];
+                  *reinterpret_cast<float4*>(regc + (ii * 32 + lr) * SWC + 8 * q + 4 * lh) =
+                      gu ? make_float4(saved_up(a0, L), saved_up(a1, L), saved_up(a2, L), saved_up(a3, L))
+                         : make_float4(saved_gate(a0, L), saved_gate(a1, L), saved_gate(a2, L), saved_gate(a3, L));
+                }
+              }
+              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+              for (int it = 0; it < 8; ++it) {  // 64 rows x 8 chunks of 16 bytes, 8 rows per instruction
+                const int r = it * 8 + (lane >> 3);
+                const int ml = wm * 128 + half * 64 + r;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(regc + r * SWC + (lane & 7) * 4);
+                if (ml < rows_here && col < Nd)
+                  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + sh + (int64_t)(t.m0 + ml) * Nd + col));
+              }
+              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             }
           }
         }
